@@ -1,0 +1,222 @@
+"""CPU oracle of Veda's distilled sparse attention hot path.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may import
+this module.  The HIP library never does, and the two share no code: no helpers, tables or
+constants.  Inputs come from ``workloads`` (seeded data only).
+
+Everything is plain float64 numpy, written to be read against the pages
+("Technical Summary: Veda - Scalable Video Diffusion via Distilled Sparse Attention",
+gist.science, and the arXiv abstract on fugumt.com).  No blocking, fusion or reordering
+beyond the definitions below; a library matmul, sort or erf serves as a step.
+
+Where the pages leave a step open, the plainest reading is taken:
+  * tiles and the tokens inside a tile are numbered row-major over (t, h, w);
+  * TripPool = [mean | max | min] over the tile's tokens, per channel;
+  * the estimator is one 2-layer MLP per head (no bias, exact-erf GELU) applied to the
+    Q-tile and K-tile descriptors; tile score = dot(y_q, y_k) * score_scale; the row
+    distribution is the softmax over key tiles;
+  * selection keeps the k largest scores per row, ties to the lower tile index, listed in
+    ascending tile index;
+  * sparse attention renormalises the softmax over the kept keys only (scale 1/sqrt(d));
+  * the oracle tile map is the max, over each (query tile x key tile) region, of the
+    full-attention probabilities normalised over all N keys.
+
+Parity pins (tests/test_oracle_pins.py): every function below is pinned by closed forms,
+hand-worked fixtures under tests/golden/, brute-force loops, or library routines of torch;
+see each docstring.  The estimator's *form* (widths 3d->256->64, GELU, 1/8) is not given by
+the pages, which print no estimator formula: parity against the paper's estimator is
+unpinned; the functions are pinned to the definition stated above.
+"""
+import numpy as np
+from scipy.special import erf
+
+
+# ---------------------------------------------------------------------------
+# Head-aware tiling  [Veda Technical Summary, §2.2 Head-Aware Tiling: each head gets a
+# tiling (p_t, p_h, p_w) that factorises the hardware tile size]
+# ---------------------------------------------------------------------------
+def tile_permutation(grid, shape):
+    """perm[r] = raster token index held by row r of the tile-major sequence.
+
+    Raster token n = (t*H + h)*W + w.  Tile (a, b, c) covers t in [a*p_t, (a+1)*p_t), etc.;
+    tiles are numbered row-major over (a, b, c), tokens inside a tile row-major over
+    (t mod p_t, h mod p_h, w mod p_w).  Pinned: hand-derived fixtures, an explicit-loop
+    construction, bijection.
+    """
+    T, H, W = grid
+    pt, ph, pw = shape
+    if T % pt or H % ph or W % pw:
+        raise ValueError(f"tile shape {shape} does not divide grid {grid}")
+    tok = np.arange(T * H * W).reshape(T // pt, pt, H // ph, ph, W // pw, pw)
+    return tok.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+
+
+def to_tiles(x, perm):
+    """Rows of the raster-ordered [N, d] array x, in tile-major order."""
+    return np.asarray(x, dtype=np.float64)[perm]
+
+
+def from_tiles(xt, perm):
+    """Inverse of to_tiles."""
+    xt = np.asarray(xt, dtype=np.float64)
+    out = np.empty_like(xt)
+    out[perm] = xt
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Distilled tile scoring  [Veda Technical Summary, §2.1 Distilled Tile Scoring]
+# ---------------------------------------------------------------------------
+def trippool(xt, P):
+    """TripPool descriptor of each tile: [mean | max | min] over the tile's P tokens, per
+    channel, concatenated (§2.1, "Statistic-Aware Estimator").  [n_t, 3d].
+    Pinned: brute-force loops, hand fixture, constant tile."""
+    xt = np.asarray(xt, dtype=np.float64)
+    n_t = xt.shape[0] // P
+    t = xt.reshape(n_t, P, xt.shape[1])
+    return np.concatenate([t.mean(axis=1), t.max(axis=1), t.min(axis=1)], axis=1)
+
+
+def gelu(x):
+    """x * Phi(x) with the exact normal CDF.  Pinned: tabulated Phi values, torch's gelu."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def mlp(desc, w1, w2):
+    """Per-head projection of tile descriptors (§2.1, "Head-Specific Projections"):
+    y = GELU(desc @ W1) @ W2, no bias.  Pinned: torch linear + gelu in float64."""
+    desc = np.asarray(desc, dtype=np.float64)
+    return gelu(desc @ np.asarray(w1, np.float64)) @ np.asarray(w2, np.float64)
+
+
+def tile_scores(yq, yk, scale):
+    """S[i, j] = scale * <y_q[i], y_k[j]>: score of key tile j for query tile i.
+    Pinned: hand fixture, symmetry."""
+    return (np.asarray(yq, np.float64) @ np.asarray(yk, np.float64).T) * float(scale)
+
+
+def row_softmax(s):
+    """Predicted tile-score distribution of each query-tile row (§2.1, "Optimization":
+    row-wise distributions).  Pinned: hand fixture, rows sum to 1, shift invariance."""
+    s = np.asarray(s, dtype=np.float64)
+    z = s - s.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_rows(scores, k):
+    """Kept key tiles of each row: the k largest scores, ties to the lower tile index,
+    returned in ascending tile index.  [rows, k] int64.
+    Pinned: brute-force full sort, crafted ties."""
+    s = np.asarray(scores, dtype=np.float64)
+    rows, n = s.shape
+    if not 1 <= k <= n:
+        raise ValueError("k out of range")
+    cols = np.arange(n)
+    out = np.empty((rows, k), dtype=np.int64)
+    for i in range(rows):
+        order = np.lexsort((cols, -s[i]))      # primary: larger score; then lower index
+        out[i] = np.sort(order[:k])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Attention  [Veda Technical Summary, §1 Problem Statement (full self-attention over the
+# spatiotemporal tokens) and §2.3 Hardware-Efficient Implementation (a kernel that skips
+# the key/value tiles not selected)]
+# ---------------------------------------------------------------------------
+def _softmax_rows_with_lse(s):
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return e / z, (m + np.log(z))[:, 0]
+
+
+def dense_attention(q, k, v, scale, return_lse=False):
+    """softmax(q k^T * scale) v over all keys.  Pinned: torch SDPA in float64."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    p, lse = _softmax_rows_with_lse((q @ k.T) * float(scale))
+    return (p @ v, lse) if return_lse else p @ v
+
+
+def sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
+    """Tile-skipping attention on tile-major rows: query tile i attends only to the keys of
+    the tiles idx[i, :], with the softmax renormalised over those keys.
+
+    qt, kt, vt: [N, d]; idx: [n_t, k] (row i = kept key tiles of query tile i).
+    Returns [len(q_tiles) * P, d] for the query tiles listed (default: all), and the
+    natural-log LSE per query row if asked.  Pinned: 100%-kept equals dense attention,
+    explicit -inf mask on the full matrix, constant V, Q = 0.
+    """
+    qt, kt, vt = (np.asarray(a, np.float64) for a in (qt, kt, vt))
+    n_t = qt.shape[0] // P
+    q_tiles = np.arange(n_t) if q_tiles is None else np.asarray(q_tiles)
+    out = np.empty((len(q_tiles) * P, qt.shape[1]))
+    lses = np.empty(len(q_tiles) * P)
+    off = np.arange(P)
+    for a, i in enumerate(q_tiles):
+        rows = (np.asarray(idx[i])[:, None] * P + off[None, :]).ravel()
+        p, lse = _softmax_rows_with_lse((qt[i * P:(i + 1) * P] @ kt[rows].T) * float(scale))
+        out[a * P:(a + 1) * P] = p @ vt[rows]
+        lses[a * P:(a + 1) * P] = lse
+    return (out, lses) if return_lse else out
+
+
+# ---------------------------------------------------------------------------
+# Oracle tile map  [Veda Technical Summary, §2.1 "Target Construction": max-pooling of the
+# full-attention matrix over query-key tile regions; §2.3: heatmaps built in two passes on
+# random subsets of query tiles]
+# ---------------------------------------------------------------------------
+def tilemap(qt, kt, P, scale, q_tiles=None):
+    """M[a, j] = max over q in query tile q_tiles[a], key in tile j, of the full-attention
+    probability softmax_row(q k^T * scale).  First the per-row log-sum-exp over all N keys,
+    then the max over each region of exp(s - lse).  [len(q_tiles), n_t].
+    Pinned: Q = 0 gives 1/N, explicit dense-P max-pool, 1/N <= row max <= 1."""
+    qt, kt = np.asarray(qt, np.float64), np.asarray(kt, np.float64)
+    n_t = kt.shape[0] // P
+    q_tiles = np.arange(qt.shape[0] // P) if q_tiles is None else np.asarray(q_tiles)
+    out = np.empty((len(q_tiles), n_t))
+    for a, i in enumerate(q_tiles):
+        s = (qt[i * P:(i + 1) * P] @ kt.T) * float(scale)          # [P, N]
+        m = s.max(axis=1, keepdims=True)
+        lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))  # pass 1
+        out[a] = np.exp(s - lse).reshape(P, n_t, P).max(axis=(0, 2))  # pass 2
+    return out
+
+
+def recall(idx_est, idx_ref):
+    """Mean over rows of |est ∩ ref| / k."""
+    idx_est, idx_ref = np.asarray(idx_est), np.asarray(idx_ref)
+    k = idx_ref.shape[1]
+    hits = [len(np.intersect1d(a, b)) for a, b in zip(idx_est, idx_ref)]
+    return float(np.mean(hits)) / k
+
+
+# ---------------------------------------------------------------------------
+# Index agreement under near-ties
+# ---------------------------------------------------------------------------
+def topk_agrees(score_row, idx_row, k, gap=1e-5):
+    """Does idx_row (ascending, k entries) select the k largest of score_row?
+
+    If the k-th and (k+1)-th largest differ by at least ``gap`` the set must equal the
+    oracle's exactly.  Otherwise any k distinct indices are accepted that include every
+    index scoring above (k-th + gap) and none scoring below ((k+1)-th - gap).
+    Returns (ok, exempt)."""
+    s = np.asarray(score_row, dtype=np.float64)
+    idx = np.asarray(idx_row)
+    n = s.shape[0]
+    if idx.shape != (k,) or np.any(np.diff(idx) <= 0) or idx.min() < 0 or idx.max() >= n:
+        return False, False
+    ref = topk_rows(s[None, :], k)[0]
+    if k == n:
+        return bool(np.array_equal(idx, ref)), False
+    srt = np.sort(s)[::-1]
+    kth, nxt = srt[k - 1], srt[k]
+    if kth - nxt >= gap:
+        return bool(np.array_equal(idx, ref)), False
+    sel = np.zeros(n, bool)
+    sel[idx] = True
+    must = s > kth + gap
+    never = s < nxt - gap
+    return bool(np.all(sel[must]) and not np.any(sel[never])), True

@@ -1,0 +1,33 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def read_golden(name):
+    """Parse a tests/golden fixture: '#' lines are comments, other lines are
+    'tag v1 v2 ...' or plain number rows.  Returns (tagged: dict[str, list[list[float]]],
+    rows: list[list[float]])."""
+    tagged, rows = {}, []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            try:
+                rows.append([float(x) for x in parts])
+            except ValueError:
+                tagged.setdefault(parts[0], []).append([float(x) for x in parts[1:]])
+    return tagged, rows

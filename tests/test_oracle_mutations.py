@@ -1,0 +1,181 @@
+"""Plant plausible mistakes in copies of oracle functions (on the CPU) and check that at
+least one pin catches each: a dropped term, a wrong sign or index, a transposed operand,
+a swapped axis, a wrong tie order."""
+import numpy as np
+import pytest
+from scipy.special import erf
+
+import oracle.veda_oracle as O
+import test_oracle_pins as pins
+
+
+def _fails(pin, *fns):
+    try:
+        pin(*fns)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def perm_swapped_inner(grid, shape):
+    T, H, W = grid
+    pt, ph, pw = shape
+    tok = np.arange(T * H * W).reshape(T // pt, pt, H // ph, ph, W // pw, pw)
+    return tok.transpose(0, 2, 4, 1, 5, 3).reshape(-1)        # (h, w) swapped inside tile
+
+
+def perm_tile_order_colmajor(grid, shape):
+    T, H, W = grid
+    pt, ph, pw = shape
+    tok = np.arange(T * H * W).reshape(T // pt, pt, H // ph, ph, W // pw, pw)
+    return tok.transpose(4, 2, 0, 1, 3, 5).reshape(-1)        # tiles numbered w-fastest... reversed
+
+
+def perm_no_tiling(grid, shape):
+    return np.arange(grid[0] * grid[1] * grid[2])
+
+
+def trippool_min_is_max(xt, P):
+    t = np.asarray(xt, np.float64).reshape(-1, P, xt.shape[1])
+    return np.concatenate([t.mean(1), t.max(1), t.max(1)], 1)
+
+
+def trippool_sum_not_mean(xt, P):
+    t = np.asarray(xt, np.float64).reshape(-1, P, xt.shape[1])
+    return np.concatenate([t.sum(1), t.max(1), t.min(1)], 1)
+
+
+def trippool_order_swapped(xt, P):
+    t = np.asarray(xt, np.float64).reshape(-1, P, xt.shape[1])
+    return np.concatenate([t.max(1), t.mean(1), t.min(1)], 1)
+
+
+def gelu_tanh(x):
+    x = np.asarray(x, np.float64)
+    return 0.5 * x * (1 + np.tanh(np.sqrt(2 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gelu_no_sqrt2(x):
+    x = np.asarray(x, np.float64)
+    return 0.5 * x * (1 + erf(x))
+
+
+def mlp_no_gelu(desc, w1, w2):
+    return (desc @ w1) @ w2
+
+
+def mlp_relu(desc, w1, w2):
+    return np.maximum(desc @ w1, 0) @ w2
+
+
+def scores_wrong_scale(yq, yk, scale):
+    return (yq @ yk.T) / np.sqrt(yq.shape[1])
+
+
+def softmax_cols(s):
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def topk_ties_high(scores, k):
+    s = np.asarray(scores, np.float64)
+    cols = np.arange(s.shape[1])
+    return np.stack([np.sort(np.lexsort((-cols, -row))[:k]) for row in s])
+
+
+def topk_smallest(scores, k):
+    s = np.asarray(scores, np.float64)
+    cols = np.arange(s.shape[1])
+    return np.stack([np.sort(np.lexsort((cols, row))[:k]) for row in s])
+
+
+def topk_unsorted(scores, k):
+    s = np.asarray(scores, np.float64)
+    cols = np.arange(s.shape[1])
+    return np.stack([np.lexsort((cols, -row))[:k] for row in s])
+
+
+def dense_no_scale(q, k, v, scale, return_lse=False):
+    return O.dense_attention(q, k, v, 1.0)
+
+
+def dense_transposed_p(q, k, v, scale, return_lse=False):
+    s = (q @ k.T) * scale
+    p = np.exp(s - s.max(axis=0, keepdims=True))
+    p /= p.sum(axis=0, keepdims=True)
+    return p @ v
+
+
+def sparse_no_renorm(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
+    """Softmax over all keys, then zero the dropped ones (no renormalisation)."""
+    n = qt.shape[0]
+    n_t = n // P
+    s = (qt @ kt.T) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    keep = np.zeros((n, n), bool)
+    for i in range(n_t):
+        for j in idx[i]:
+            keep[i * P:(i + 1) * P, j * P:(j + 1) * P] = True
+    out = np.where(keep, p, 0) @ vt
+    if q_tiles is not None:
+        out = np.concatenate([out[i * P:(i + 1) * P] for i in q_tiles])
+    return (out, np.zeros(len(out))) if return_lse else out
+
+
+def sparse_wrong_tile(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
+    """Off by one in the kept-tile rows."""
+    idx2 = (np.asarray(idx) + 1) % (qt.shape[0] // P)
+    return O.sparse_attention(qt, kt, vt, idx2, P, scale, q_tiles, return_lse)
+
+
+def tilemap_mean(qt, kt, P, scale, q_tiles=None):
+    n_t = kt.shape[0] // P
+    q_tiles = np.arange(qt.shape[0] // P) if q_tiles is None else q_tiles
+    out = []
+    for i in q_tiles:
+        s = (qt[i * P:(i + 1) * P] @ kt.T) * scale
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        out.append(p.reshape(P, n_t, P).mean(axis=(0, 2)))
+    return np.array(out)
+
+
+def tilemap_unnormalised(qt, kt, P, scale, q_tiles=None):
+    n_t = kt.shape[0] // P
+    q_tiles = np.arange(qt.shape[0] // P) if q_tiles is None else q_tiles
+    out = []
+    for i in q_tiles:
+        s = (qt[i * P:(i + 1) * P] @ kt.T) * scale
+        out.append(np.exp(s - s.max(1, keepdims=True)).reshape(P, n_t, P).max(axis=(0, 2)))
+    return np.array(out)
+
+
+MUTANTS = [
+    ("perm: in-tile axes swapped", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_swapped_inner]),
+    ("perm: tile order reversed", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_tile_order_colmajor]),
+    ("perm: identity", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_no_tiling]),
+    ("trippool: min dropped", [pins.pin_trippool_golden, pins.pin_trippool_loops], [trippool_min_is_max]),
+    ("trippool: sum for mean", [pins.pin_trippool_golden, pins.pin_trippool_loops], [trippool_sum_not_mean]),
+    ("trippool: block order", [pins.pin_trippool_golden, pins.pin_trippool_loops], [trippool_order_swapped]),
+    ("gelu: tanh form", [pins.pin_gelu_table], [gelu_tanh]),
+    ("gelu: missing sqrt2", [pins.pin_gelu_table], [gelu_no_sqrt2]),
+    ("mlp: activation dropped", [pins.pin_mlp_torch], [mlp_no_gelu]),
+    ("mlp: relu", [pins.pin_mlp_torch], [mlp_relu]),
+    ("scores: 1/sqrt(dim) scale", [lambda f: pins.pin_scores_hand(f, O.row_softmax)], [scores_wrong_scale]),
+    ("softmax: over columns", [lambda f: pins.pin_scores_hand(O.tile_scores, f)], [softmax_cols]),
+    ("topk: ties to higher index", [pins.pin_topk_bruteforce, pins.pin_topk_ties], [topk_ties_high]),
+    ("topk: smallest", [pins.pin_topk_bruteforce, pins.pin_topk_ties], [topk_smallest]),
+    ("topk: not ascending", [pins.pin_topk_bruteforce, pins.pin_topk_ties], [topk_unsorted]),
+    ("attention: no scale", [pins.pin_attention_sdpa], [dense_no_scale]),
+    ("attention: softmax over queries", [pins.pin_attention_hand, pins.pin_attention_sdpa], [dense_transposed_p]),
+    ("sparse: no renormalisation", [pins.pin_sparse_vs_masked_matrix], [sparse_no_renorm]),
+    ("sparse: wrong kept tile", [pins.pin_sparse_vs_masked_matrix], [sparse_wrong_tile]),
+    ("tilemap: mean pooling", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_mean]),
+    ("tilemap: not normalised", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_unnormalised]),
+]
+
+
+@pytest.mark.parametrize("name,pin_list,fns", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, pin_list, fns):
+    assert any(_fails(p, *fns) for p in pin_list), f"no pin caught: {name}"

@@ -1,0 +1,374 @@
+"""Pins of the CPU oracle to facts outside itself: hand-worked fixtures (tests/golden),
+closed forms, brute-force loops, and torch's own routines.  CPU only.
+
+Each pin is a plain function of the oracle function(s) it checks, so that
+test_oracle_mutations.py can plant a mistake in a copy of the oracle and show that some
+pin fails.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.veda_oracle as O
+from conftest import read_golden
+
+
+# ------------------------------------------------------------------ permutation
+def pin_perm_golden(tile_permutation):
+    for name in ("perm_tiny.txt", "perm_nonsquare.txt"):
+        tagged, rows = read_golden(name)
+        grid = tuple(int(x) for x in tagged["grid"][0])
+        shape = tuple(int(x) for x in tagged["shape"][0])
+        perm = tile_permutation(grid, shape)
+        for r, n in rows:
+            assert perm[int(r)] == int(n), (name, r, perm[int(r)], n)
+
+
+def perm_by_loops(grid, shape):
+    """Explicit construction: walk tiles row-major, then offsets inside the tile row-major."""
+    T, H, W = grid
+    pt, ph, pw = shape
+    out = []
+    for a in range(T // pt):
+        for b in range(H // ph):
+            for c in range(W // pw):
+                for i in range(pt):
+                    for j in range(ph):
+                        for l in range(pw):
+                            t, h, w = a * pt + i, b * ph + j, c * pw + l
+                            out.append((t * H + h) * W + w)
+    return np.array(out)
+
+
+def pin_perm_loops(tile_permutation):
+    cases = [((4, 8, 8), (4, 4, 4)), ((2, 4, 6), (1, 2, 3)), ((8, 16, 32), (2, 8, 8)),
+             ((8, 16, 32), (8, 4, 4)), ((8, 16, 32), (1, 8, 16)), ((6, 4, 10), (3, 2, 5))]
+    for grid, shape in cases:
+        assert np.array_equal(tile_permutation(grid, shape), perm_by_loops(grid, shape)), (grid, shape)
+
+
+def test_perm_golden():
+    pin_perm_golden(O.tile_permutation)
+
+
+def test_perm_loops():
+    pin_perm_loops(O.tile_permutation)
+
+
+def test_perm_bijection_and_roundtrip():
+    rng = np.random.default_rng(0)
+    for grid, shape in [((20, 32, 48), (2, 8, 8)), ((20, 32, 48), (1, 8, 16)), ((8, 16, 32), (8, 4, 4))]:
+        perm = O.tile_permutation(grid, shape)
+        n = grid[0] * grid[1] * grid[2]
+        assert np.array_equal(np.sort(perm), np.arange(n))
+        x = rng.standard_normal((n, 3))
+        assert np.array_equal(O.from_tiles(O.to_tiles(x, perm), perm), x)
+
+
+def test_perm_tile_is_a_box():
+    """Every tile's tokens form exactly one (p_t, p_h, p_w) box of the grid."""
+    grid, shape = (8, 16, 32), (4, 4, 8)
+    perm = O.tile_permutation(grid, shape)
+    P = 128
+    T, H, W = grid
+    for j in range(len(perm) // P):
+        n = perm[j * P:(j + 1) * P]
+        t, h, w = n // (H * W), (n // W) % H, n % W
+        assert t.max() - t.min() + 1 == shape[0] and h.max() - h.min() + 1 == shape[1]
+        assert w.max() - w.min() + 1 == shape[2] and len(set(n.tolist())) == P
+        assert t.min() % shape[0] == 0 and h.min() % shape[1] == 0 and w.min() % shape[2] == 0
+
+
+def test_perm_rejects_non_dividing():
+    with pytest.raises(ValueError):
+        O.tile_permutation((20, 48, 80), (8, 4, 4))
+
+
+# ------------------------------------------------------------------ TripPool
+def pin_trippool_golden(trippool):
+    tagged, _ = read_golden("trippool_hand.txt")
+    x = np.array(tagged["token"])
+    assert np.allclose(trippool(x, 2)[0], tagged["desc"][0], rtol=0, atol=1e-15)
+
+
+def pin_trippool_loops(trippool):
+    rng = np.random.default_rng(1)
+    P, n_t, d = 8, 5, 6
+    x = rng.standard_normal((P * n_t, d))
+    got = trippool(x, P)
+    for j in range(n_t):
+        for c in range(d):
+            vals = [x[j * P + r, c] for r in range(P)]
+            assert math.isclose(got[j, c], sum(vals) / P, rel_tol=1e-13, abs_tol=1e-13)
+            assert got[j, d + c] == max(vals)
+            assert got[j, 2 * d + c] == min(vals)
+
+
+def test_trippool_golden():
+    pin_trippool_golden(O.trippool)
+
+
+def test_trippool_loops():
+    pin_trippool_loops(O.trippool)
+
+
+def test_trippool_constant_tile():
+    x = np.full((128, 4), 2.5)
+    assert np.all(O.trippool(x, 128) == 2.5)
+
+
+# ------------------------------------------------------------------ MLP
+def pin_gelu_table(gelu):
+    _, rows = read_golden("gelu_phi.txt")
+    for x, y in rows:
+        assert math.isclose(float(gelu(np.array([x]))[0]), y, rel_tol=1e-14, abs_tol=1e-15), (x, y)
+
+
+def pin_mlp_torch(mlp):
+    rng = np.random.default_rng(2)
+    desc = rng.standard_normal((7, 12))
+    w1 = rng.standard_normal((12, 9)) / np.sqrt(12)
+    w2 = rng.standard_normal((9, 5)) / 3.0
+    t = torch.from_numpy
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.gelu(torch.nn.functional.linear(t(desc), t(w1).T), approximate="none"), t(w2).T)
+    assert np.allclose(mlp(desc, w1, w2), ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_gelu_table():
+    pin_gelu_table(O.gelu)
+
+
+def test_gelu_vs_torch_and_limits():
+    x = np.linspace(-8, 8, 1001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(O.gelu(x), ref, rtol=1e-14, atol=1e-15)
+    assert O.gelu(np.array([40.0]))[0] == 40.0 and O.gelu(np.array([-40.0]))[0] == 0.0
+
+
+def test_mlp_torch():
+    pin_mlp_torch(O.mlp)
+
+
+# ------------------------------------------------------------------ scores, softmax
+def pin_scores_hand(tile_scores, row_softmax):
+    tagged, _ = read_golden("scores_hand.txt")
+    yq = np.array(tagged["yq"])
+    yk = np.array(tagged["yk"][0]).reshape(2, 2)
+    assert np.allclose(tile_scores(yq, yk, 1 / 8), [tagged["s"][0]], rtol=0, atol=1e-15)
+    assert np.allclose(row_softmax(np.array([[0.0, math.log(3.0)]])), [[0.25, 0.75]], rtol=0, atol=1e-15)
+
+
+def test_scores_hand():
+    pin_scores_hand(O.tile_scores, O.row_softmax)
+
+
+def test_scores_symmetric_and_softmax_props():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((10, 64))
+    s = O.tile_scores(y, y, 1 / 8)
+    assert np.allclose(s, s.T, rtol=0, atol=1e-13)
+    p = O.row_softmax(s)
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(O.row_softmax(s + 7.5), p, rtol=0, atol=1e-15)
+    ref = torch.softmax(torch.from_numpy(s), dim=1).numpy()
+    assert np.allclose(p, ref, rtol=1e-13, atol=1e-16)
+
+
+# ------------------------------------------------------------------ top-k
+def pin_topk_bruteforce(topk_rows):
+    rng = np.random.default_rng(4)
+    s = np.round(rng.standard_normal((40, 23)) * 2) / 2        # many exact ties
+    for k in (1, 3, 7, 23):
+        got = topk_rows(s, k)
+        for i in range(s.shape[0]):
+            ranked = sorted(range(s.shape[1]), key=lambda j: (-s[i, j], j))
+            assert list(got[i]) == sorted(ranked[:k]), (i, k)
+
+
+def pin_topk_ties(topk_rows):
+    s = np.array([[1.0, 3.0, 3.0, 2.0, 3.0]])
+    assert list(topk_rows(s, 2)[0]) == [1, 2]
+    assert list(topk_rows(s, 3)[0]) == [1, 2, 4]
+    assert list(topk_rows(s, 4)[0]) == [1, 2, 3, 4]
+    assert list(topk_rows(np.zeros((1, 6)), 3)[0]) == [0, 1, 2]
+
+
+def test_topk_bruteforce():
+    pin_topk_bruteforce(O.topk_rows)
+
+
+def test_topk_ties():
+    pin_topk_ties(O.topk_rows)
+
+
+def test_topk_agrees_rule():
+    s = np.array([5.0, 1.0, 4.0, 4.0 + 5e-6, 0.0])
+    ok, ex = O.topk_agrees(s, np.array([0, 3]), 2)
+    assert ok and ex                                    # exact choice inside the near-tie band
+    ok, ex = O.topk_agrees(s, np.array([0, 2]), 2)
+    assert ok and ex                                    # the other member of the near-tie
+    ok, _ = O.topk_agrees(s, np.array([0, 1]), 2)
+    assert not ok
+    s2 = np.array([5.0, 1.0, 4.0, 3.0])
+    assert O.topk_agrees(s2, np.array([0, 2]), 2) == (True, False)
+    assert O.topk_agrees(s2, np.array([0, 3]), 2) == (False, False)
+    assert O.topk_agrees(s2, np.array([2, 0]), 2) == (False, False)   # must be ascending
+
+
+def test_recall():
+    assert O.recall(np.array([[0, 1, 2], [3, 4, 5]]), np.array([[0, 1, 5], [3, 4, 5]])) == pytest.approx(5 / 6)
+
+
+# ------------------------------------------------------------------ attention
+def pin_attention_hand(dense_attention):
+    tagged, _ = read_golden("attention_hand.txt")
+    q = np.array(tagged["q"][0])[:, None]
+    k = np.array(tagged["k"][0])[:, None]
+    v = np.array(tagged["v"][0])[:, None]
+    assert np.allclose(dense_attention(q, k, v, 1.0)[:, 0], tagged["o"][0], rtol=0, atol=1e-14)
+
+
+def pin_attention_sdpa(dense_attention):
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((37, 16)) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(a)[None, None] for a in (q, k, v)))[0, 0].numpy()
+    assert np.allclose(dense_attention(q, k, v, 1 / 4.0), ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_sparse_full_equals_dense(sparse_attention, dense_attention):
+    rng = np.random.default_rng(6)
+    P, n_t, d = 8, 6, 16
+    q, k, v = (rng.standard_normal((P * n_t, d)) for _ in range(3))
+    idx = np.tile(np.arange(n_t), (n_t, 1))
+    assert np.allclose(sparse_attention(q, k, v, idx, P, 0.25), dense_attention(q, k, v, 0.25),
+                       rtol=1e-12, atol=1e-13)
+
+
+def pin_sparse_vs_masked_matrix(sparse_attention):
+    """Kept-tile attention equals full attention with -inf on every dropped key tile."""
+    rng = np.random.default_rng(7)
+    P, n_t, d, kk = 8, 6, 16, 2
+    q, k, v = (rng.standard_normal((P * n_t, d)) for _ in range(3))
+    idx = np.stack([np.sort(rng.choice(n_t, kk, replace=False)) for _ in range(n_t)])
+    s = (q @ k.T) * 0.25
+    keep = np.zeros((P * n_t, P * n_t), bool)
+    for i in range(n_t):
+        for j in idx[i]:
+            keep[i * P:(i + 1) * P, j * P:(j + 1) * P] = True
+    s = np.where(keep, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.allclose(sparse_attention(q, k, v, idx, P, 0.25), p @ v, rtol=1e-12, atol=1e-13)
+    out, lse = sparse_attention(q, k, v, idx, P, 0.25, q_tiles=[4, 1], return_lse=True)
+    assert np.allclose(out[:P], (p @ v)[4 * P:5 * P], rtol=1e-12, atol=1e-13)
+    s4 = (q[4 * P:5 * P] @ k.T) * 0.25
+    s4 = np.where(keep[4 * P:5 * P], s4, -np.inf)
+    assert np.allclose(lse[:P], np.log(np.exp(s4).sum(axis=1)), rtol=1e-13)
+
+
+def test_attention_hand():
+    pin_attention_hand(O.dense_attention)
+
+
+def test_attention_sdpa():
+    pin_attention_sdpa(O.dense_attention)
+
+
+def test_sparse_full_equals_dense():
+    pin_sparse_full_equals_dense(O.sparse_attention, O.dense_attention)
+
+
+def test_sparse_vs_masked_matrix():
+    pin_sparse_vs_masked_matrix(O.sparse_attention)
+
+
+def test_sparse_constant_v_and_zero_q():
+    rng = np.random.default_rng(8)
+    P, n_t, d = 8, 5, 16
+    q, k = rng.standard_normal((P * n_t, d)), rng.standard_normal((P * n_t, d))
+    idx = np.stack([np.sort(rng.choice(n_t, 3, replace=False)) for _ in range(n_t)])
+    v = np.full((P * n_t, d), -1.75)
+    assert np.allclose(O.sparse_attention(q, k, v, idx, P, 0.3), -1.75, rtol=0, atol=1e-13)
+    v = rng.standard_normal((P * n_t, d))
+    out = O.sparse_attention(np.zeros_like(q), k, v, idx, P, 0.3)
+    for i in range(n_t):
+        rows = np.concatenate([np.arange(j * P, (j + 1) * P) for j in idx[i]])
+        assert np.allclose(out[i * P:(i + 1) * P], v[rows].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_dominant_key():
+    rng = np.random.default_rng(9)
+    n, d = 64, 8
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    k[17] = q[3] * 50.0
+    out = O.dense_attention(q, k, v, 1.0)
+    assert np.allclose(out[3], v[17], atol=1e-10)
+
+
+def test_unpermuted_dense_invariant_to_tile_shape():
+    """With every tile kept, attention after un-permuting does not depend on the tiling."""
+    rng = np.random.default_rng(10)
+    grid = (8, 16, 32)
+    n, d = 4096, 16
+    q, k, v = (rng.standard_normal((n, d)) * 0.5 for _ in range(3))
+    ref = O.dense_attention(q[:256], k, v, 0.25)
+    for shape in [(2, 8, 8), (8, 4, 4), (1, 8, 16), (4, 4, 8)]:
+        perm = O.tile_permutation(grid, shape)
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(n)
+        qt, kt, vt = (O.to_tiles(a, perm) for a in (q, k, v))
+        n_t = n // 128
+        rows_needed = np.unique(inv[:256] // 128)
+        idx = np.tile(np.arange(n_t), (n_t, 1))
+        out_t = np.zeros((n, d))
+        part = O.sparse_attention(qt, kt, vt, idx, 128, 0.25, q_tiles=rows_needed)
+        for a, i in enumerate(rows_needed):
+            out_t[i * 128:(i + 1) * 128] = part[a * 128:(a + 1) * 128]
+        out = O.from_tiles(out_t, perm)
+        assert np.allclose(out[:256], ref, rtol=1e-12, atol=1e-13), shape
+
+
+# ------------------------------------------------------------------ tile map
+def pin_tilemap_hand(tilemap):
+    tagged, _ = read_golden("attention_hand.txt")
+    q = np.array(tagged["q"][0])[:, None]
+    k = np.array(tagged["k"][0])[:, None]
+    assert np.allclose(tilemap(q, k, 1, 1.0).ravel(), tagged["p"][0], rtol=0, atol=1e-15)
+
+
+def pin_tilemap_bruteforce(tilemap):
+    rng = np.random.default_rng(11)
+    P, n_t, d = 4, 5, 8
+    q, k = rng.standard_normal((P * n_t, d)), rng.standard_normal((P * n_t, d))
+    s = (q @ k.T) * 0.5
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    got = tilemap(q, k, P, 0.5, q_tiles=[3, 0, 4])
+    for a, i in enumerate([3, 0, 4]):
+        for j in range(n_t):
+            best = max(p[r, c] for r in range(i * P, (i + 1) * P) for c in range(j * P, (j + 1) * P))
+            assert math.isclose(got[a, j], best, rel_tol=1e-12)
+
+
+def test_tilemap_hand():
+    pin_tilemap_hand(O.tilemap)
+
+
+def test_tilemap_bruteforce():
+    pin_tilemap_bruteforce(O.tilemap)
+
+
+def test_tilemap_zero_q_and_bounds():
+    rng = np.random.default_rng(12)
+    P, n_t, d = 8, 6, 16
+    k = rng.standard_normal((P * n_t, d))
+    m = O.tilemap(np.zeros((P * n_t, d)), k, P, 0.25)
+    assert np.allclose(m, 1.0 / (P * n_t), rtol=1e-14)
+    q = rng.standard_normal((P * n_t, d)) * 3
+    m = O.tilemap(q, k, P, 0.25)
+    assert np.all(m <= 1.0 + 1e-15) and np.all(m.max(axis=1) >= 1.0 / (P * n_t))
