@@ -1,0 +1,159 @@
+/*
+ * veda.h - C ABI of the MI355X (gfx950) hot path of Veda's distilled sparse attention.
+ *
+ * The method ("Technical Summary: Veda - Scalable Video Diffusion via Distilled Sparse
+ * Attention", gist.science; arXiv abstract on fugumt.com): each attention head tiles the
+ * T x H x W video latent with its own (p_t, p_h, p_w) factorisation of the hardware tile
+ * (§2.2 Head-Aware Tiling), scores every (query tile, key tile) pair with a per-head MLP
+ * on TripPool [mean|max|min] tile descriptors (§2.1 Distilled Tile Scoring), keeps the
+ * best key tiles of each query tile, and runs attention only over the kept tiles
+ * (§2.3 Hardware-Efficient Implementation).  The full-attention max-pooled tile map
+ * (§2.1 "Target Construction") is the reference the estimator is distilled toward.
+ *
+ * Conventions (all entry points):
+ *  - Every device buffer is owned by the caller; the library never allocates or frees
+ *    device memory.  Host arrays (veda_geom.tile_shapes) are read before the call returns.
+ *  - Calls are asynchronous on the given HIP stream and never synchronise it.
+ *  - All arguments are validated before anything is launched; on an error nothing is
+ *    launched and the status says why.  A failed HIP launch returns VEDA_ERR_HIP and
+ *    veda_last_hip_error() reports the hipError_t (per host thread).
+ *  - Device pointers must be 16-byte aligned (veda_topk_mask: 4-byte).  Outputs must not
+ *    alias inputs.
+ *  - Supported element types: VEDA_F32 with head_dim 64 and tile 64; VEDA_BF16 with
+ *    head_dim 128 and tile 128.  Scores, descriptors, weights, LSEs and maps are float32.
+ *  - Stateless and thread-safe (apart from the per-thread last-error slot).
+ *
+ * Tiled layouts (per batch b and head h, N = t*h*w tokens, P = tile, n_t = N / P):
+ *  - VEDA_TILE_ROWS: [B, H, N, d]; row r holds token perm_h[r] of the raster sequence,
+ *    where tile r / P is numbered row-major over the tile grid (t/p_t, h/p_h, w/p_w) and
+ *    r % P row-major over (p_t, p_h, p_w).  Q, K and the attention output use it.
+ *  - VEDA_TILE_COLS: [B, H, n_t, d, P]; the same tiles, each stored channel-major
+ *    (element (token o, channel c) of tile j at ((j*d + c)*P + o)).  V uses it, so the
+ *    P x V product reads keys contiguously.
+ * The raster layout is [B, N, H, d] with any element strides for b, n, h and d contiguous;
+ * raster token n = (t*H + h)*W + w.
+ */
+#ifndef VEDA_H
+#define VEDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t veda_status;
+enum {
+  VEDA_OK = 0,
+  VEDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  VEDA_ERR_SHAPE = -2,       /* sizes inconsistent: tile shape product != tile, shape not
+                                dividing the grid, k out of range, too many heads ... */
+  VEDA_ERR_DTYPE = -3,       /* unknown element type */
+  VEDA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim/tile for this dtype) */
+  VEDA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  VEDA_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
+  VEDA_ERR_HIP = -7          /* a HIP launch failed; see veda_last_hip_error() */
+};
+
+typedef enum { VEDA_F32 = 0, VEDA_BF16 = 1 } veda_dtype;
+typedef enum { VEDA_TILE_ROWS = 0, VEDA_TILE_COLS = 1 } veda_layout;
+
+#define VEDA_MAX_HEADS 128
+
+/* Problem geometry.  [Technical Summary §2.2: the per-(layer, head) tiling
+ * pi = (p_t, p_h, p_w) factorises the hardware tile.] */
+typedef struct {
+  int32_t batch, heads, head_dim;  /* B, H (<= VEDA_MAX_HEADS), d */
+  int32_t t, h, w;                 /* latent grid; N = t*h*w, a multiple of tile */
+  int32_t tile;                    /* P tokens per tile */
+  const int32_t *tile_shapes;      /* HOST int32[heads][3] (p_t, p_h, p_w); each product
+                                      == tile and each entry divides (t, h, w) */
+} veda_geom;
+
+/* Head-aware tiling (permutation of tokens into per-head tiles).
+ * [Technical Summary §2.2 Head-Aware Tiling]
+ * inverse = 0: raster -> tiled (gather); inverse = 1: tiled -> raster (scatter; only
+ * with layout VEDA_TILE_ROWS).  raster element (b, n, h, c) is at
+ * raster[b*rs_b + n*rs_n + h*rs_h + c] (strides in elements; each multiple of 8 for
+ * bf16 / 4 for f32, so rows stay 16-byte aligned).  tiled: contiguous, `layout`. */
+veda_status veda_tile_gather(const veda_geom *g, veda_dtype dtype,
+                             void *raster, int64_t rs_b, int64_t rs_n, int64_t rs_h,
+                             void *tiled, veda_layout layout, int32_t inverse,
+                             hipStream_t stream);
+
+/* Workspace (bytes) that veda_trippool_score needs for the given geometry. */
+size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int32_t mlp_out);
+
+/* Distilled tile scoring.  [Technical Summary §2.1 Distilled Tile Scoring]
+ * For every tile of q_tiled and k_tiled (VEDA_TILE_ROWS): TripPool descriptor
+ * [mean | max | min] over the tile's P tokens per channel (3d floats); per-head MLP
+ * y = GELU(desc @ W1[h]) @ W2[h] (exact-erf GELU, no bias); logits
+ * S[b,h,i,j] = score_scale * <y_q[i], y_k[j]>; optional row softmax over j; optional
+ * top-k of each row (the k largest S, ties to the lower j, ascending j) - the same
+ * selection as veda_topk_mask applied to S.
+ *   w1_q, w1_k: [H, 3d, mlp_hidden] f32; w2_q, w2_k: [H, mlp_hidden, mlp_out] f32
+ *               (the K pointers may alias the Q pointers: one MLP per head)
+ *   scores:     out [B, H, n_t, n_t] f32, nullable
+ *   probs:      out [B, H, n_t, n_t] f32 row softmax, nullable
+ *   q_desc, k_desc: out [B, H, n_t, 3d] f32, nullable
+ *   topk, idx:  topk in [1, n_t] with idx out [B, H, n_t, topk] int32; or topk = 0, idx NULL
+ * At least one of scores / probs / idx must be requested.  mlp_out <= 64,
+ * mlp_hidden <= 256 (multiples of 4).  workspace >= veda_trippool_workspace_bytes. */
+veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype,
+                                const void *q_tiled, const void *k_tiled,
+                                const float *w1_q, const float *w2_q,
+                                const float *w1_k, const float *w2_k,
+                                int32_t mlp_hidden, int32_t mlp_out, float score_scale,
+                                float *scores, float *probs, float *q_desc, float *k_desc,
+                                int32_t topk, int32_t *idx,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Tile selection at a sparsity level.  [Technical Summary §4: 90% / 95% of key tiles
+ * skipped]  For each of `rows` rows of scores [rows, n_cols] (f32), write the indices of
+ * the k largest values (ties to the lower index) in ascending order to idx [rows, k]
+ * int32, and optionally a 0/1 mask [rows, n_cols] uint8.  1 <= k <= n_cols <= 4096. */
+veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k,
+                           int32_t *idx, uint8_t *mask, hipStream_t stream);
+
+/* Tile-skipping attention forward.  [Technical Summary §2.3: the kernel fetches only the
+ * selected, non-contiguous key/value tiles]  For every query tile i of every (b, h):
+ * O = softmax(Q_i K_sel^T * softmax_scale) V_sel over the keys of the tiles
+ * kv_idx[b, h, i, 0..k-1], the softmax renormalised over those keys.
+ *   q_tiled, k_tiled: VEDA_TILE_ROWS; v_tiled: VEDA_TILE_COLS
+ *   kv_idx: [B, H, n_t, k] int32, each entry in [0, n_t), no repeats within a row
+ *           (k == n_t with every tile listed is dense attention).  Entries outside
+ *           [0, n_t) are clamped into it (no out-of-bounds access; the result is then
+ *           not meaningful).
+ *   o_tiled: out VEDA_TILE_ROWS, same dtype
+ *   lse:     out [B, H, N] f32 natural-log log-sum-exp of each query row, nullable */
+veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype,
+                                 const void *q_tiled, const void *k_tiled, const void *v_tiled,
+                                 const int32_t *kv_idx, int32_t k, float softmax_scale,
+                                 void *o_tiled, float *lse, hipStream_t stream);
+
+/* Oracle tile map.  [Technical Summary §2.1 "Target Construction": max-pooling of the
+ * full-attention matrix over query-key tile regions; §2.3: built in two passes on random
+ * subsets of query tiles]  For each selected query tile a (q_tiles[b, h, a], or a itself
+ * if q_tiles is NULL) and each key tile j:
+ *   tilemap[b, h, a, j] = max over queries q of tile, keys x of tile j, of
+ *                         exp(s(q, x) - lse(q)),  s = q.x * softmax_scale,
+ *   lse(q) = log sum over all N keys of exp(s(q, x))  (pass 1; written to lse if non-NULL,
+ *   [B, H, n_sel * P] f32).  q_tiled, k_tiled: VEDA_TILE_ROWS.
+ *   q_tiles: DEVICE int32 [B, H, n_sel] in [0, n_t) (entries outside are clamped), or
+ *            NULL (then n_sel must be n_t). */
+veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
+                                const void *q_tiled, const void *k_tiled, float softmax_scale,
+                                const int32_t *q_tiles, int32_t n_sel,
+                                float *tilemap, float *lse, hipStream_t stream);
+
+const char *veda_status_str(veda_status s);
+int veda_last_hip_error(void);
+/* Library version string. */
+const char *veda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VEDA_H */

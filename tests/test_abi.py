@@ -1,0 +1,131 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/veda.h
+declares, and rejects bad arguments with the documented status before touching the GPU.
+
+No call here has arguments that pass validation, so nothing is ever launched (the fake
+device addresses below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_dit_block_head_amd as V
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "veda.h")
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN = 0, -1, -2, -3, -4, -5, -6
+A = ctypes.c_void_p(0x10000)       # aligned fake device address (never dereferenced)
+B_ = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)     # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(veda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(V.LIB_PATH):
+        pytest.skip("libveda.so not built")
+    return V.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) == 9, syms
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings(L):
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN, -7):
+        assert len(L.veda_status_str(code)) > 0
+    assert b"gfx950" in L.veda_version()
+    assert L.veda_last_hip_error() == 0
+
+
+def geom(d=128, tile=128, grid=(8, 16, 32), shapes=((2, 8, 8),) * 2, heads=None, batch=1):
+    heads = len(shapes) if heads is None else heads
+    return V.Geom(batch, heads, d, grid, tile, shapes)
+
+
+def gather(L, g, dt=V.BF16, raster=A, tiled=B_, strides=(4096 * 2 * 128, 2 * 128, 128), layout=0, inverse=0):
+    return L.veda_tile_gather(g.ref if g is not None else None, dt, raster, *strides, tiled, layout, inverse, None)
+
+
+def test_gather_validation(L):
+    assert gather(L, None) == NULL
+    assert gather(L, geom(), raster=None) == NULL
+    assert gather(L, geom(), dt=7) == DTYPE
+    assert gather(L, geom(d=64)) == UNSUP                      # bf16 needs d = 128
+    assert gather(L, geom(d=128, tile=64, shapes=((1, 8, 8),) * 2), dt=V.F32) == UNSUP
+    assert gather(L, geom(shapes=((2, 8, 4), (2, 8, 8)))) == SHAPE    # product != tile
+    assert gather(L, geom(grid=(20, 48, 80), shapes=((8, 4, 4),))) == SHAPE   # 8 does not divide 20
+    assert gather(L, geom(grid=(8, 16, 31), shapes=((1, 8, 16),))) == SHAPE  # N not a multiple of 128
+    assert gather(L, geom(), raster=MIS) == ALIGN
+    assert gather(L, geom(), strides=(4096 * 256, 260, 128)) == ALIGN
+    assert gather(L, geom(), layout=1, inverse=1) == UNSUP
+    assert gather(L, geom(), layout=5) == SHAPE
+    assert gather(L, geom(heads=200, shapes=((2, 8, 8),) * 200)) == SHAPE
+
+
+def score(L, g, topk=6, idx=B_, scores=None, ws=A, ws_bytes=1 << 30, hidden=256, out=64):
+    return L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, hidden, out, 0.125, scores, None, None, None,
+                                 topk, idx, ws, ws_bytes, None)
+
+
+def test_score_validation(L):
+    g = geom()
+    assert score(L, g, topk=0, idx=None) == NULL               # nothing requested
+    assert score(L, g, topk=0, idx=B_) == SHAPE
+    assert score(L, g, topk=6, idx=None) == NULL
+    assert score(L, g, topk=33) == SHAPE                       # n_t = 32
+    assert score(L, g, hidden=512) == UNSUP
+    assert score(L, g, out=128) == UNSUP
+    assert score(L, g, ws=None) == WS
+    need = L.veda_trippool_workspace_bytes(g.ref, 256, 64)
+    assert need > 0
+    assert score(L, g, ws_bytes=need - 1) == WS
+    assert score(L, g, idx=MIS) == ALIGN
+    big = geom(grid=(40, 48, 160), shapes=((2, 8, 8),))      # n_t = 2400 > fused-score limit
+    assert score(L, big, topk=10) == UNSUP
+
+
+def test_topk_validation(L):
+    assert L.veda_topk_mask(4, 10, A, 0, B_, None, None) == SHAPE
+    assert L.veda_topk_mask(4, 10, A, 11, B_, None, None) == SHAPE
+    assert L.veda_topk_mask(4, 5000, A, 3, B_, None, None) == SHAPE
+    assert L.veda_topk_mask(-1, 10, A, 3, B_, None, None) == SHAPE
+    assert L.veda_topk_mask(4, 10, None, 3, B_, None, None) == NULL
+    assert L.veda_topk_mask(4, 10, A, 3, None, None, None) == NULL
+    assert L.veda_topk_mask(4, 10, ctypes.c_void_p(0x10002), 3, B_, None, None) == ALIGN
+    assert L.veda_topk_mask(0, 10, A, 3, B_, None, None) == OK   # nothing to do: nothing launched
+
+
+def test_attn_validation(L):
+    g = geom()
+    f = L.veda_sparse_attn_fwd
+    assert f(g.ref, V.BF16, A, A, None, A, 4, 0.088, A, None, None) == NULL
+    assert f(g.ref, V.BF16, A, A, A, A, 0, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, A, 33, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, A, 4, 0.088, MIS, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, A, A, 4, 0.088, A, MIS, None) == ALIGN
+    assert f(geom(d=64).ref, V.BF16, A, A, A, A, 4, 0.088, A, None, None) == UNSUP
+
+
+def test_tilemap_validation(L):
+    g = geom()
+    f = L.veda_oracle_tilemap
+    assert f(g.ref, V.BF16, A, A, 0.088, None, 5, A, None, None) == SHAPE     # NULL list needs n_sel = n_t
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 0, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 33, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, None, 0.088, A, 4, A, None, None) == NULL
+    assert f(g.ref, V.BF16, A, A, 0.088, MIS, 4, A, None, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    g = geom()
+    with pytest.raises(V.VedaError):
+        V.veda_topk_mask(torch.zeros(4, 10), 3, torch.zeros(4, 3, dtype=torch.int32))

@@ -1,0 +1,370 @@
+"""GPU parity: every call of the C ABI against the CPU oracle on the seeded workloads.
+
+Tolerances: indices exact unless the k-th/(k+1)-th fp32 oracle scores differ by < 1e-5
+(then any near-tie choice is accepted); attention max-abs <= 2e-2 and relative Frobenius
+<= 1e-2 for bf16 (1e-4 for fp32); gather and TripPool max/min bit-exact; tile map within
+1e-3 in log space (1e-5 for fp32).  Large workloads compare 64 sampled query tiles per head.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.veda_oracle as O
+from workloads import get, make
+
+pytestmark = pytest.mark.gpu
+
+V = pytest.importorskip("video_dit_block_head_amd")
+from video_dit_block_head_amd.pipeline import SparseAttention, dense_index  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_raster(arr_hm, bf16):
+    """Head-major host array [B,H,N,d] -> contiguous GPU raster [B,N,H,d]."""
+    t = torch.from_numpy(arr_hm.view(np.int16) if bf16 else arr_hm).cuda()
+    if bf16:
+        t = t.view(torch.bfloat16)
+    return t.permute(0, 2, 1, 3).contiguous()
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+class Run:
+    """One workload on the GPU through the full path (headline k)."""
+
+    def __init__(self, ci):
+        cfg = self.cfg = get(ci)
+        say(f"[gpu-parity] config {cfg.name}: generating")
+        wl = self.wl = make(cfg)
+        self.bf16 = wl.is_bf16
+        B, H, N, d, P, nt = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim, cfg.tile, cfg.n_tiles
+        self.geom = V.Geom(B, H, d, cfg.grid, P, wl.shapes)
+        dt = torch.bfloat16 if self.bf16 else torch.float32
+        say(f"[gpu-parity] config {cfg.name}: upload + full path, k={cfg.topk[0]}")
+        self.sa = SparseAttention(self.geom, dt, torch.from_numpy(wl.w1), torch.from_numpy(wl.w2),
+                                  score_scale=cfg.score_scale)
+        self.q, self.k, self.v = (to_dev_raster(a, self.bf16) for a in (wl.q, wl.k, wl.v))
+        self.sa.gather(self.q, self.k, self.v)
+        self.scores = torch.empty((B, H, nt, nt), dtype=torch.float32, device="cuda")
+        self.probs = torch.empty_like(self.scores)
+        self.qd = torch.empty((B, H, nt, 3 * d), dtype=torch.float32, device="cuda")
+        self.kd = torch.empty_like(self.qd)
+        self.kk = cfg.topk[0]
+        self.idx = self.sa.score(self.kk, scores=self.scores, probs=self.probs, q_desc=self.qd, k_desc=self.kd)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        self.sa.attend(self.idx, self.lse)
+        self.out = torch.empty_like(self.q)
+        self.sa.scatter(self.out)
+        torch.cuda.synchronize()
+        say(f"[gpu-parity] config {cfg.name}: GPU path done")
+        self._oh = {}
+
+    def heads(self, limit=None):
+        H = self.cfg.heads
+        return list(range(H)) if limit is None or limit >= H else list(np.linspace(0, H - 1, limit).astype(int))
+
+    def oracle_head(self, b, h):
+        """Tile-major float64 Q, K, V of (b, h) and the permutation (oracle's own)."""
+        key = (b, h)
+        if key not in self._oh:
+            self._oh.clear()
+            perm = O.tile_permutation(self.cfg.grid, self.wl.shapes[h])
+            self._oh[key] = tuple(O.to_tiles(self.wl.head(w, b, h), perm) for w in ("q", "k", "v")) + (perm,)
+        return self._oh[key]
+
+    def q_tiles(self, h):
+        return self.wl.sample_tiles(h)
+
+
+CFGS = [0, 1, 2, 3, 4]
+
+
+@pytest.fixture(scope="module", params=CFGS, ids=[get(i).name for i in CFGS])
+def r(request):
+    """One workload at a time (pytest groups the tests by workload)."""
+    run = Run(request.param)
+    yield run
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+HEAD_LIMIT = {0: None, 1: None, 2: None, 3: 6, 4: 4}        # heads for bit-exact layout checks
+SCORE_HEADS = {0: None, 1: None, 2: None, 3: None, 4: 16}   # heads for index parity
+
+
+def bitwise_equal(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- gather
+def test_gather_bitexact(r):
+    cfg, ci = r.cfg, r.cfg.index
+    P, d, nt = cfg.tile, cfg.head_dim, cfg.n_tiles
+    for b in range(cfg.batch):
+        for h in r.heads(HEAD_LIMIT[ci]):
+            qt, kt, vt, perm = r.oracle_head(b, h)
+            assert bitwise_equal(host(r.sa.q_t[b, h]), qt), (cfg.name, h, "q")
+            assert bitwise_equal(host(r.sa.k_t[b, h]), kt), (cfg.name, h, "k")
+            vcols = host(r.sa.v_t[b, h]).reshape(nt, d, P).transpose(0, 2, 1).reshape(nt * P, d)
+            assert bitwise_equal(vcols, vt), (cfg.name, h, "v")
+    # scatter(gather(q)) is the identity
+    back = torch.empty_like(r.q)
+    V.veda_tile_gather(r.geom, back, r.sa.q_t, V.ROWS, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16) if r.bf16 else back, r.q.view(torch.int16) if r.bf16 else r.q)
+
+
+# ----------------------------------------------------------------------------- scoring
+def test_trippool_descriptors(r):
+    cfg, ci = r.cfg, r.cfg.index
+    d = cfg.head_dim
+    for b in range(cfg.batch):
+        for h in r.heads(HEAD_LIMIT[ci]):
+            qt, kt, _, _ = r.oracle_head(b, h)
+            for x, gd in ((qt, r.qd), (kt, r.kd)):
+                ref = O.trippool(x, cfg.tile)
+                got = host(gd[b, h])
+                assert bitwise_equal(got[:, d:], ref[:, d:]), (cfg.name, h)      # max, min exact
+                err = np.abs(got[:, :d] - ref[:, :d]) / np.maximum(np.abs(ref[:, :d]), 1.0)
+                assert err.max() <= 1e-6, (cfg.name, h, err.max())
+
+
+def test_scores_and_topk(r):
+    cfg, ci = r.cfg, r.cfg.index
+    kk = r.kk
+    worst, exempt, rows = 0.0, 0, 0
+    for b in range(cfg.batch):
+        for h in r.heads(SCORE_HEADS[ci]):
+            qt, kt, _, _ = r.oracle_head(b, h)
+            yq = O.mlp(O.trippool(qt, cfg.tile), r.wl.w1[h], r.wl.w2[h])
+            yk = O.mlp(O.trippool(kt, cfg.tile), r.wl.w1[h], r.wl.w2[h])
+            s = O.tile_scores(yq, yk, cfg.score_scale)
+            s32 = s.astype(np.float32)
+            got_s = host(r.scores[b, h])
+            worst = max(worst, float(np.abs(got_s - s).max()))
+            got_p = host(r.probs[b, h])
+            assert np.abs(got_p - O.row_softmax(s)).max() <= 2e-6, (cfg.name, h)
+            idx = host(r.idx[b, h]).astype(np.int64)
+            for i in range(cfg.n_tiles):
+                ok, ex = O.topk_agrees(s32[i], idx[i], kk)
+                assert ok, (cfg.name, h, i, idx[i], np.sort(s32[i])[::-1][kk - 2:kk + 2])
+                exempt += ex
+                rows += 1
+    say(f"[gpu-parity] {cfg.name}: score max|err| {worst:.3g}, {exempt}/{rows} rows in the near-tie band")
+    assert worst <= 2e-5
+
+
+# ----------------------------------------------------------------------------- attention
+def attention_errors(r, idx_dev, kk, heads, tiles_per_head=None, o_t=None, lse=None):
+    cfg = r.cfg
+    P = cfg.tile
+    o_t = r.sa.o_t if o_t is None else o_t
+    num = den = 0.0
+    mx = lse_err = 0.0
+    for b in range(cfg.batch):
+        for h in heads:
+            qt, kt, vt, _ = r.oracle_head(b, h)
+            tiles = r.q_tiles(h)
+            if tiles_per_head is not None:
+                tiles = tiles[np.linspace(0, len(tiles) - 1, tiles_per_head).astype(int)]
+            idx = host(idx_dev[b, h]).astype(np.int64)
+            ref, ref_lse = O.sparse_attention(qt, kt, vt, idx, P, 1 / math.sqrt(cfg.head_dim), q_tiles=tiles,
+                                              return_lse=True)
+            rows = (tiles[:, None] * P + np.arange(P)[None]).ravel()
+            got = host(o_t[b, h])[rows]
+            num += float(((got - ref) ** 2).sum())
+            den += float((ref ** 2).sum())
+            mx = max(mx, float(np.abs(got - ref).max()))
+            if lse is not None:
+                lse_err = max(lse_err, float(np.abs(host(lse[b, h])[rows] - ref_lse).max()))
+    return mx, math.sqrt(num / den), lse_err
+
+
+def tol(r):
+    return (2e-2, 1e-2) if r.bf16 else (1e-4, 1e-4)
+
+
+def test_sparse_attention(r):
+    ci = r.cfg.index
+    heads = r.heads(None if ci < 4 else 24)
+    mx, rel, lse_err = attention_errors(r, r.idx, r.kk, heads, lse=r.lse)
+    say(f"[gpu-parity] {r.cfg.name} k={r.kk}: max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
+    amax, arel = tol(r)
+    assert mx <= amax and rel <= arel
+    assert lse_err <= (2e-3 if r.bf16 else 1e-5)
+
+
+def test_output_unpermuted(r):
+    """The raster output is the tiled output scattered back through the permutation."""
+    cfg, ci = r.cfg, r.cfg.index
+    for b in range(cfg.batch):
+        for h in r.heads(HEAD_LIMIT[ci]):
+            _, _, _, perm = r.oracle_head(b, h)
+            assert bitwise_equal(host(r.out[b, :, h])[perm], host(r.sa.o_t[b, h])), (cfg.name, h)
+
+
+def test_dense_path(r):
+    """k = n_t with every tile listed: equals full attention."""
+    cfg, ci = r.cfg, r.cfg.index
+    idx = dense_index(r.geom)
+    o_t = torch.empty_like(r.sa.o_t)
+    say(f"[gpu-parity] {cfg.name}: dense path k={cfg.n_tiles}")
+    V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, cfg.n_tiles, 1 / math.sqrt(cfg.head_dim), o_t)
+    torch.cuda.synchronize()
+    heads = r.heads({0: None, 1: None, 2: 3, 3: 2, 4: 1}[ci])
+    tph = {0: None, 1: None, 2: 8, 3: 4, 4: 2}[ci]
+    mx, rel, _ = attention_errors(r, idx, cfg.n_tiles, heads, tiles_per_head=tph, o_t=o_t)
+    say(f"[gpu-parity] {cfg.name} dense: max|dO| {mx:.3g}  relFro {rel:.3g}")
+    amax, arel = tol(r)
+    assert mx <= amax and rel <= arel
+
+
+def test_sparsity_sweep(r):
+    cfg = r.cfg
+    if len(cfg.topk) < 3:
+        pytest.skip("no sparsity sweep for this workload")
+    for kk in cfg.topk[1:-1]:
+        idx = r.sa.score(kk)
+        o_t = torch.empty_like(r.sa.o_t)
+        say(f"[gpu-parity] {cfg.name}: k={kk}")
+        V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, kk, 1 / math.sqrt(cfg.head_dim), o_t)
+        torch.cuda.synchronize()
+        mx, rel, _ = attention_errors(r, idx, kk, r.heads(4), tiles_per_head=16, o_t=o_t)
+        say(f"[gpu-parity] {cfg.name} k={kk}: max|dO| {mx:.3g}  relFro {rel:.3g}")
+        assert mx <= 2e-2 and rel <= 1e-2
+
+
+# ----------------------------------------------------------------------------- tile map
+def test_tilemap_and_recall(r):
+    cfg, ci = r.cfg, r.cfg.index
+    B, H, nt, P = cfg.batch, cfg.heads, cfg.n_tiles, cfg.tile
+    n_sel = cfg.sampled_q_tiles or nt
+    qtl = torch.from_numpy(np.stack([r.q_tiles(h) for h in range(H)]).astype(np.int32)[None].repeat(B, 0)).cuda()
+    tm = torch.empty((B, H, n_sel, nt), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, n_sel * P), dtype=torch.float32, device="cuda")
+    say(f"[gpu-parity] {cfg.name}: tile map, {n_sel} query tiles per head")
+    r.sa.tilemap(qtl, n_sel, tm, lse)
+    torch.cuda.synchronize()
+    # oracle mask = top-k of the map (GPU top-k vs oracle top-k on the same map)
+    omask = torch.empty((B, H, n_sel, r.kk), dtype=torch.int32, device="cuda")
+    V.veda_topk_mask(tm, r.kk, omask)
+    torch.cuda.synchronize()
+    tmh, omh = host(tm), host(omask).astype(np.int64)
+    check_heads = r.heads({0: None, 1: 4, 2: 2, 3: 2, 4: 1}[ci])
+    n_check = {0: None, 1: 8, 2: 4, 3: 4, 4: 2}[ci]
+    worst = 0.0
+    for b in range(B):
+        for h in check_heads:
+            qt, kt, _, _ = r.oracle_head(b, h)
+            sel = np.arange(n_sel) if n_check is None else np.linspace(0, n_sel - 1, n_check).astype(int)
+            ref = O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=r.q_tiles(h)[sel])
+            got = tmh[b, h, sel]
+            keep = ref >= 1e-30
+            assert np.all(got[~keep] < 1e-25)
+            worst = max(worst, float(np.abs(np.log(got[keep]) - np.log(ref[keep])).max()))
+            assert np.all(got <= 1.0 + 1e-6)
+        for h in range(H):
+            for a in range(n_sel):
+                ok, _ = O.topk_agrees(tmh[b, h, a].astype(np.float64), omh[b, h, a], r.kk, gap=1e-12)
+                assert ok
+    est = host(r.idx).astype(np.int64)
+    recall = np.mean([O.recall(est[b, h][r.q_tiles(h)], omh[b, h]) for b in range(B) for h in range(H)])
+    say(f"[gpu-parity] {cfg.name}: tile map max|dlog M| {worst:.3g}; estimator recall vs oracle mask {recall:.3f}")
+    assert worst <= (1e-3 if r.bf16 else 1e-5)
+
+
+# ----------------------------------------------------------------------------- determinism, edges
+def test_determinism(r):
+    if r.cfg.index not in (1, 2):
+        pytest.skip("checked on the small and mid workloads")
+    o1 = r.sa.o_t.clone()
+    i1 = r.idx.clone()
+    idx = r.sa.score(r.kk)
+    r.sa.attend(idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, i1)
+    assert torch.equal(r.sa.o_t.view(torch.int16), o1.view(torch.int16))
+
+
+def small_geom_case(batch, grid, shapes, seed=7):
+    rng = np.random.default_rng(seed)
+    H = len(shapes)
+    N = grid[0] * grid[1] * grid[2]
+    geom = V.Geom(batch, H, 128, grid, 128, shapes)
+    x = [torch.from_numpy(rng.standard_normal((batch, N, H, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
+         for _ in range(3)]
+    return geom, x
+
+
+def test_batch_and_edge_k():
+    """batch > 1, k = 1 and k = n_t, on a 4x8x16 grid with three tile shapes."""
+    shapes = [(1, 8, 16), (2, 8, 8), (4, 4, 8)]
+    geom, (q, k, v) = small_geom_case(2, (4, 8, 16), shapes)
+    rng = np.random.default_rng(3)
+    w1 = torch.from_numpy((rng.standard_normal((3, 384, 256)) / math.sqrt(384)).astype(np.float32))
+    w2 = torch.from_numpy((rng.standard_normal((3, 256, 64)) / 16).astype(np.float32))
+    sa = SparseAttention(geom, torch.bfloat16, w1, w2)
+    say("[gpu-parity] batch-2 edge case")
+    sa.gather(q, k, v)
+    nt = geom.n_tiles
+    for kk in (1, 2, nt):
+        idx = sa.score(kk)
+        sa.attend(idx)
+        torch.cuda.synchronize()
+        idx_h = host(idx).astype(np.int64)
+        for b in range(2):
+            for h in range(3):
+                perm = O.tile_permutation(geom.grid, shapes[h])
+                qt, kt, vt = (O.to_tiles(host(x[b, :, h]), perm) for x in (q, k, v))
+                yq = O.mlp(O.trippool(qt, 128), w1[h].numpy(), w2[h].numpy())
+                yk = O.mlp(O.trippool(kt, 128), w1[h].numpy(), w2[h].numpy())
+                s32 = O.tile_scores(yq, yk, 0.125).astype(np.float32)
+                for i in range(nt):
+                    assert O.topk_agrees(s32[i], idx_h[b, h, i], kk)[0]
+                ref = O.sparse_attention(qt, kt, vt, idx_h[b, h], 128, 1 / math.sqrt(128))
+                got = host(sa.o_t[b, h])
+                assert np.abs(got - ref).max() <= 2e-2
+                assert math.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 1e-2
+
+
+def test_strided_raster_gather():
+    """A non-contiguous [B,N,H,d] view (head-major storage) gathers like a contiguous one."""
+    shapes = [(2, 8, 8), (1, 8, 16)]
+    geom, (q, _, _) = small_geom_case(1, (4, 8, 16), shapes)
+    hm = q.permute(0, 2, 1, 3).contiguous()        # [B,H,N,d] storage
+    view = hm.permute(0, 2, 1, 3)                  # [B,N,H,d] view with strides (HNd, d, Nd, 1)
+    a = torch.empty((1, 2, 512, 128), dtype=torch.bfloat16, device="cuda")
+    bb = torch.empty_like(a)
+    V.veda_tile_gather(geom, q, a, V.ROWS)
+    V.veda_tile_gather(geom, view, bb, V.ROWS)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), bb.view(torch.int16))
+
+
+@pytest.mark.parametrize("n_cols,k", [(1, 1), (7, 3), (64, 64), (600, 60), (1200, 120), (1300, 5), (4096, 409)])
+def test_topk_mask_standalone(n_cols, k):
+    rng = np.random.default_rng(n_cols)
+    rows = 37
+    s = (np.round(rng.standard_normal((rows, n_cols)) * 4) / 4).astype(np.float32)   # many exact ties
+    s[0] = 1.5                                                                       # an all-equal row
+    sd = torch.from_numpy(s).cuda()
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    mask = torch.empty((rows, n_cols), dtype=torch.uint8, device="cuda")
+    say(f"[gpu-parity] topk n_cols={n_cols} k={k}")
+    V.veda_topk_mask(sd, k, idx, mask)
+    torch.cuda.synchronize()
+    ref = O.topk_rows(s.astype(np.float64), k)
+    assert np.array_equal(host(idx).astype(np.int64), ref)
+    m = np.zeros((rows, n_cols), np.uint8)
+    np.put_along_axis(m, ref, 1, axis=1)
+    assert np.array_equal(host(mask), m)

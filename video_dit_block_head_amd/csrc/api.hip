@@ -1,0 +1,174 @@
+// C ABI of the library: argument validation (before anything is launched), status codes,
+// and dispatch to the kernel launchers.  No exception crosses this boundary.
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace veda;
+
+static thread_local int g_last_hip_error = 0;
+
+namespace {
+
+constexpr int SCORE_MAX_NT = 1280;  // fused score kernel holds a row of <= 1280 scores in registers
+constexpr int TILEMAP_MAX_NT = 1280;
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+veda_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return VEDA_OK;
+  g_last_hip_error = (int)e;
+  return VEDA_ERR_HIP;
+}
+
+// Validates the geometry and dtype; fills Geo and per-head shapes.
+veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *hs) {
+  if (g == nullptr || g->tile_shapes == nullptr) return VEDA_ERR_NULL;
+  if (dt != VEDA_F32 && dt != VEDA_BF16) return VEDA_ERR_DTYPE;
+  if (g->batch < 1 || g->heads < 1 || g->heads > VEDA_MAX_HEADS || g->t < 1 || g->h < 1 || g->w < 1 ||
+      g->tile < 1 || g->head_dim < 1)
+    return VEDA_ERR_SHAPE;
+  const int64_t n = (int64_t)g->t * g->h * g->w;
+  if (n > (int64_t)1 << 30 || n % g->tile != 0) return VEDA_ERR_SHAPE;
+  if (dt == VEDA_BF16 && !(g->head_dim == 128 && g->tile == 128)) return VEDA_ERR_UNSUPPORTED;
+  if (dt == VEDA_F32 && !(g->head_dim == 64 && g->tile == 64)) return VEDA_ERR_UNSUPPORTED;
+  memset(hs, 0, sizeof(*hs));
+  for (int h = 0; h < g->heads; ++h) {
+    const int32_t pt = g->tile_shapes[3 * h], ph = g->tile_shapes[3 * h + 1], pw = g->tile_shapes[3 * h + 2];
+    if (pt < 1 || ph < 1 || pw < 1) return VEDA_ERR_SHAPE;
+    if ((int64_t)pt * ph * pw != g->tile) return VEDA_ERR_SHAPE;
+    if (g->t % pt || g->h % ph || g->w % pw) return VEDA_ERR_SHAPE;
+    hs->s[h][0] = pt;
+    hs->s[h][1] = ph;
+    hs->s[h][2] = pw;
+  }
+  out->B = g->batch;
+  out->H = g->heads;
+  out->d = g->head_dim;
+  out->T = g->t;
+  out->Hs = g->h;
+  out->Ws = g->w;
+  out->P = g->tile;
+  out->N = (int32_t)n;
+  out->nt = (int32_t)(n / g->tile);
+  return VEDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+veda_status veda_tile_gather(const veda_geom *g, veda_dtype dtype, void *raster, int64_t rs_b, int64_t rs_n,
+                             int64_t rs_h, void *tiled, veda_layout layout, int32_t inverse, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (raster == nullptr || tiled == nullptr) return VEDA_ERR_NULL;
+  if (!aligned16(raster) || !aligned16(tiled)) return VEDA_ERR_ALIGN;
+  if (layout != VEDA_TILE_ROWS && layout != VEDA_TILE_COLS) return VEDA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return VEDA_ERR_SHAPE;
+  if (inverse && layout != VEDA_TILE_ROWS) return VEDA_ERR_UNSUPPORTED;
+  if (rs_b < 0 || rs_n < 0 || rs_h < 0) return VEDA_ERR_SHAPE;
+  const int64_t epc = dtype == VEDA_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (rs_b % epc || rs_n % epc || rs_h % epc) return VEDA_ERR_ALIGN;
+  return hip_status(launch_gather(geo, hs, dtype, raster, rs_b, rs_n, rs_h, tiled, layout, inverse, stream));
+}
+
+size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int32_t mlp_out) {
+  if (g == nullptr || g->batch < 1 || g->heads < 1 || g->tile < 1 || mlp_out < 1) return 0;
+  const int64_t n = (int64_t)g->t * g->h * g->w;
+  Geo geo{};
+  geo.B = g->batch;
+  geo.H = g->heads;
+  geo.d = g->head_dim;
+  geo.nt = (int32_t)(n / g->tile);
+  return score_workspace_bytes(geo, mlp_hidden, mlp_out);
+}
+
+veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
+                                const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
+                                int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores, float *probs,
+                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_tiled || !k_tiled || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
+  if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
+  if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
+  if (topk < 0 || topk > geo.nt) return VEDA_ERR_SHAPE;
+  if (mlp_hidden < 1 || mlp_hidden > 256 || mlp_out < 1 || mlp_out > 64) return VEDA_ERR_UNSUPPORTED;
+  if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
+    return VEDA_ERR_WORKSPACE;
+  return hip_status(launch_score(geo, dtype, q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
+                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream));
+}
+
+veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k, int32_t *idx,
+                           uint8_t *mask, hipStream_t stream) {
+  if (rows < 0 || n_cols < 1 || n_cols > 4096 || k < 1 || k > n_cols) return VEDA_ERR_SHAPE;
+  if (rows > ((int64_t)1 << 31) * 4 - 4) return VEDA_ERR_SHAPE;
+  if (scores == nullptr || idx == nullptr) return VEDA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u)) return VEDA_ERR_ALIGN;
+  if (rows == 0) return VEDA_OK;
+  return hip_status(launch_topk(rows, n_cols, scores, k, idx, mask, stream));
+}
+
+veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
+                                 const void *v_tiled, const int32_t *kv_idx, int32_t k, float softmax_scale,
+                                 void *o_tiled, float *lse, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_tiled || !k_tiled || !v_tiled || !kv_idx || !o_tiled) return VEDA_ERR_NULL;
+  if (k < 1 || k > geo.nt) return VEDA_ERR_SHAPE;
+  const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, o_tiled, lse};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  return hip_status(launch_sparse_attn(geo, dtype, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse,
+                                       stream));
+}
+
+veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
+                                float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
+                                float *lse, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_tiled || !k_tiled || !tilemap) return VEDA_ERR_NULL;
+  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
+  if (geo.nt > TILEMAP_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_tiled, k_tiled, q_tiles, tilemap, lse};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  return hip_status(launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, stream));
+}
+
+const char *veda_status_str(veda_status s) {
+  switch (s) {
+    case VEDA_OK: return "ok";
+    case VEDA_ERR_NULL: return "required pointer is NULL";
+    case VEDA_ERR_SHAPE: return "inconsistent sizes or tile shapes";
+    case VEDA_ERR_DTYPE: return "unknown element type";
+    case VEDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VEDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VEDA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case VEDA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int veda_last_hip_error(void) { return g_last_hip_error; }
+
+const char *veda_version(void) { return "veda-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

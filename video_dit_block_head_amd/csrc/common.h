@@ -1,0 +1,93 @@
+// Shared device-side definitions of the gfx950 kernels (internal; not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "veda.h"
+
+namespace veda {
+
+// Per-head tile shapes, passed to kernels by value (1.5 KB of kernel arguments).
+struct HeadShapes {
+  int32_t s[VEDA_MAX_HEADS][3];
+};
+
+// Geometry as the kernels see it.
+struct Geo {
+  int32_t B, H, d, T, Hs, Ws, P, N, nt;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Raster token index of row `o` of tile `j` for tile shape (pt, ph, pw): tiles row-major
+// over the tile grid, tokens row-major inside the tile.
+__device__ __forceinline__ int64_t tile_row_token(int j, int o, int pt, int ph, int pw, int Hs, int Ws) {
+  const int ntw = Ws / pw, nth = Hs / ph;
+  const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
+  const int ow = o % pw, oh = (o / pw) % ph, ot = o / (pw * ph);
+  return ((int64_t)(jt * pt + ot) * Hs + (jh * ph + oh)) * Ws + (jw * pw + ow);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key); -0 maps like +0.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane)); }
+
+// Top-k of one row held by a wave: lane `lane` holds columns j = 64*m + lane, m < MAXM,
+// as order-preserving keys (0 for columns >= n_cols).  Writes the indices of the k largest
+// keys, ties to the lower index, ascending, to idx[0..k); optional 0/1 mask[0..n_cols).
+// The k-th largest key is found bit by bit (largest T with count(key >= T) >= k).
+template <int MAXM>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_cols, int k, int lane,
+                                          int32_t *__restrict__ idx, uint8_t *__restrict__ mask) {
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
+    if (cnt >= k) T = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) n_gt += __popcll(__ballot(key[m] > T));
+  const int need = k - n_gt;
+  const uint64_t lt = lanemask_lt(lane);
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const int j = 64 * m + lane;
+    const bool gt = key[m] > T;
+    const bool eq = key[m] == T;
+    const uint64_t eqm = __ballot(eq);
+    const int tie_rank = ties + __popcll(eqm & lt);
+    const bool sel = gt || (eq && tie_rank < need);
+    const uint64_t selm = __ballot(sel);
+    if (sel) idx[base + __popcll(selm & lt)] = j;
+    if (mask != nullptr && j < n_cols) mask[j] = sel ? 1 : 0;
+    base += __popcll(selm);
+    ties += __popcll(eqm);
+  }
+}
+
+}  // namespace veda

@@ -1,0 +1,27 @@
+// Host-side launchers of the gfx950 kernels (internal).  Each enqueues its kernels on
+// `st` and returns hipGetLastError(); arguments are validated by the C ABI layer first.
+#pragma once
+#include "common.h"
+
+namespace veda {
+
+hipError_t launch_gather(const Geo &g, const HeadShapes &hs, veda_dtype dt, void *raster, int64_t rs_b,
+                         int64_t rs_n, int64_t rs_h, void *tiled, veda_layout layout, int inverse, hipStream_t st);
+
+// Scoring: pool -> MLP -> scores / softmax / top-k.  ws layout: see score.hip.
+size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out);
+hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
+                        const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
+                        float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
+                        void *ws, hipStream_t st);
+
+hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
+                       hipStream_t st);
+
+hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
+                              const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st);
+
+hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
+                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, hipStream_t st);
+
+}  // namespace veda

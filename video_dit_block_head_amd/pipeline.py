@@ -1,0 +1,81 @@
+"""One DiT self-attention layer through the library: head-aware tiling of Q, K, V ->
+distilled tile scoring with top-k -> tile-skipping attention -> un-tiling of the output.
+
+PyTorch only allocates device buffers (reused across calls) and supplies the stream; every
+step is a call into libveda.
+"""
+import math
+
+import torch
+
+from . import (BF16, COLS, ROWS, Geom, veda_oracle_tilemap, veda_sparse_attn_fwd, veda_tile_gather,
+               veda_trippool_score, veda_trippool_workspace_bytes)
+
+
+class SparseAttention:
+    """Holds the geometry, the per-head estimator weights and reusable device buffers."""
+
+    def __init__(self, geom: Geom, dtype: torch.dtype, w1, w2, w1_k=None, w2_k=None, score_scale=0.125,
+                 softmax_scale=None, device="cuda"):
+        self.geom, self.dtype, self.device = geom, dtype, device
+        self.w1 = w1.to(device=device, dtype=torch.float32).contiguous()
+        self.w2 = w2.to(device=device, dtype=torch.float32).contiguous()
+        self.w1_k = self.w1 if w1_k is None else w1_k.to(device=device, dtype=torch.float32).contiguous()
+        self.w2_k = self.w2 if w2_k is None else w2_k.to(device=device, dtype=torch.float32).contiguous()
+        self.score_scale = float(score_scale)
+        self.softmax_scale = 1.0 / math.sqrt(geom.head_dim) if softmax_scale is None else float(softmax_scale)
+        g = geom
+        shape = (g.batch, g.heads, g.n_tokens, g.head_dim)
+        self.q_t = torch.empty(shape, dtype=dtype, device=device)
+        self.k_t = torch.empty(shape, dtype=dtype, device=device)
+        self.v_t = torch.empty(shape, dtype=dtype, device=device)   # COLS layout, same size
+        self.o_t = torch.empty(shape, dtype=dtype, device=device)
+        nbytes = veda_trippool_workspace_bytes(g, self.w1.shape[-1], self.w2.shape[-1])
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._idx = {}
+
+    def idx_buffer(self, k):
+        if k not in self._idx:
+            g = self.geom
+            self._idx[k] = torch.empty((g.batch, g.heads, g.n_tiles, k), dtype=torch.int32, device=self.device)
+        return self._idx[k]
+
+    def gather(self, q, k, v):
+        """q, k, v: [B, N, H, d] (last dim contiguous)."""
+        veda_tile_gather(self.geom, q, self.q_t, ROWS)
+        veda_tile_gather(self.geom, k, self.k_t, ROWS)
+        veda_tile_gather(self.geom, v, self.v_t, COLS)
+
+    def score(self, topk, scores=None, probs=None, q_desc=None, k_desc=None):
+        idx = self.idx_buffer(topk) if topk > 0 else None
+        veda_trippool_score(self.geom, self.q_t, self.k_t, self.w1, self.w2, self.w1_k, self.w2_k,
+                            self.score_scale, scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc,
+                            topk=topk, idx=idx, workspace=self.ws)
+        return idx
+
+    def attend(self, idx, lse=None):
+        veda_sparse_attn_fwd(self.geom, self.q_t, self.k_t, self.v_t, idx, int(idx.shape[-1]),
+                             self.softmax_scale, self.o_t, lse)
+        return self.o_t
+
+    def scatter(self, out):
+        """Write the tiled output back to raster order: out [B, N, H, d]."""
+        veda_tile_gather(self.geom, out, self.o_t, ROWS, inverse=True)
+        return out
+
+    def tilemap(self, q_tiles, n_sel, out, lse=None):
+        veda_oracle_tilemap(self.geom, self.q_t, self.k_t, self.softmax_scale, q_tiles, n_sel, out, lse)
+        return out
+
+    def forward(self, q, k, v, topk, out):
+        self.gather(q, k, v)
+        idx = self.score(topk)
+        self.attend(idx)
+        return self.scatter(out)
+
+
+def dense_index(geom: Geom, device="cuda"):
+    """Kept-tile list with every key tile (0 % skipping): the dense path."""
+    g = geom
+    return (torch.arange(g.n_tiles, dtype=torch.int32, device=device)
+            .expand(g.batch, g.heads, g.n_tiles, g.n_tiles).contiguous())
