@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the distilled sparse attention hot path on one MI355X.
+
+One step = every stage of the path over one batch of the seeded synthetic workload
+(default: the 14B-DiT-scale "large" workload, B=1, H=40, d=128, latent 20x48x80 so
+N = 76 800 tokens, 128-token tiles with per-head shapes, 60 of 600 key tiles kept = 90 %
+skipped):
+  1. head-aware tile gather of Q, K (rows) and V (channel-major)
+  2. TripPool -> per-head MLP -> tile scores -> top-k (one call, fused top-k)
+  3. tile-skipping attention (bf16 MFMA)
+  4. inverse gather of the output to raster order
+  5. max-pooled full-attention tile map on the 64 sampled query tiles per head
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+
+value = kept attention FLOPs per step (4 N^2 d (k/n_t) H B) / step time, in TFLOP/s.
+Per-stage times come from HIP events recorded on the launch stream inside the timed
+steps; `roofline` is the attention kernel (the dominant one) against bf16 MFMA peak.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn ms/call + effective TFLOPS (kept FLOPs) at 90% sparsity, N≈77k"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+COUNTERS = os.path.join(ROOT, "profiles", "counters_attn_bf16_large.json")
+ATTN_SRC = os.path.join(ROOT, "video_dit_block_head_amd", "csrc", "attn.hip")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_from_counters(launch_bytes_unit="GB"):
+    """HBM bytes per attention launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts, scaled by the same counters' reading of a plain copy of known size.  None if
+    the attention source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    rec = json.load(open(COUNTERS))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("attn_source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, wl, kk, n_sel):
+    """Time the CPU oracle (as it stands) on a bounded sample of one step and scale each
+    stage to the full step: 2 heads; all tiles for gather / scoring / scatter; 32 query
+    tiles per head for attention; 4 query tiles per head for the tile map."""
+    import numpy as np
+    import oracle.veda_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    heads = [0, cfg.heads // 2]
+    P, nt, H = cfg.tile, cfg.n_tiles, cfg.heads
+    n_att, n_map = 32, 4
+    T = time.perf_counter
+    acc = dict(gather=0.0, score=0.0, attn=0.0, scatter=0.0, tilemap=0.0)
+    t_all = T()
+    for h in heads:
+        t = T()
+        perm = O.tile_permutation(cfg.grid, wl.shapes[h])
+        qt, kt, vt = (O.to_tiles(wl.head(w, 0, h), perm) for w in ("q", "k", "v"))
+        acc["gather"] += T() - t
+        t = T()
+        yq = O.mlp(O.trippool(qt, P), wl.w1[h], wl.w2[h])
+        yk = O.mlp(O.trippool(kt, P), wl.w1[h], wl.w2[h])
+        idx = O.topk_rows(O.tile_scores(yq, yk, cfg.score_scale).astype(np.float32), kk)
+        acc["score"] += T() - t
+        t = T()
+        out = O.sparse_attention(qt, kt, vt, idx, P, 1 / math.sqrt(cfg.head_dim), q_tiles=np.arange(n_att))
+        acc["attn"] += T() - t
+        t = T()
+        O.from_tiles(qt, perm)
+        acc["scatter"] += T() - t
+        t = T()
+        O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=wl.sample_tiles(h)[:n_map])
+        acc["tilemap"] += T() - t
+        del out
+    wall = T() - t_all
+    nh = len(heads)
+    scale = dict(gather=H / nh, score=H / nh, attn=H * nt / (nh * n_att), scatter=H / nh,
+                 tilemap=H * n_sel / (nh * n_map))
+    step_s = sum(acc[s] * scale[s] for s in acc)
+    return {
+        "value": cfg.kept_flops(kk) / step_s / 1e12, "unit": "TFLOP/s",
+        "cores": threads if threads else len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": (f"float64 numpy oracle on {nh} of {H} heads: gather/scoring/scatter of all {nt} tiles, "
+                   f"attention for {n_att} query tiles per head, tile map for {n_map} query tiles per head; "
+                   f"{wall:.1f} s measured, each stage scaled to the full step"),
+        "sample_seconds": round(wall, 2), "extrapolated_step_s": round(step_s, 1),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large", help="tiny|small|mid|large|long")
+    ap.add_argument("--topk", type=int, default=None, help="kept key tiles (default: the workload's headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the 0%%-skipping attention comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}); the path is "
+              "per-head independent and a multi-GPU run is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import video_dit_block_head_amd as V
+    from video_dit_block_head_amd.pipeline import SparseAttention, dense_index
+    from workloads import get, make
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    V.lib()  # fail loudly if the HIP library is missing
+    cfg = get(args.workload)
+    kk = args.topk or cfg.topk[0]
+    if cfg.dtype != "bf16":
+        raise SystemExit("the benchmark runs the bf16 workloads")
+    say(f"[bench] generating workload {cfg.name} (N={cfg.n_tokens}, H={cfg.heads}, k={kk}/{cfg.n_tiles})")
+    t0 = time.time()
+    wl = make(cfg)
+    say(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+    B, H, N, d, P, nt = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim, cfg.tile, cfg.n_tiles
+    geom = V.Geom(B, H, d, cfg.grid, P, wl.shapes)
+
+    def upload(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+
+    q, k, v = upload(wl.q), upload(wl.k), upload(wl.v)
+    sa = SparseAttention(geom, torch.bfloat16, torch.from_numpy(wl.w1), torch.from_numpy(wl.w2),
+                         score_scale=cfg.score_scale)
+    out = torch.empty_like(q)
+    n_sel = cfg.sampled_q_tiles or nt
+    qtl = torch.from_numpy(np.stack([wl.sample_tiles(h) for h in range(H)]).astype(np.int32)[None]
+                           .repeat(B, 0)).cuda()
+    tmap = torch.empty((B, H, n_sel, nt), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    stages = ["gather", "score_topk", "sparse_attn", "scatter", "tilemap"]
+
+    def step(ev):
+        ev[0].record()
+        sa.gather(q, k, v)
+        ev[1].record()
+        idx = sa.score(kk)
+        ev[2].record()
+        sa.attend(idx)
+        ev[3].record()
+        sa.scatter(out)
+        ev[4].record()
+        sa.tilemap(qtl, n_sel, tmap)
+        ev[5].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+
+    say(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+
+    evs = [events() for _ in range(args.steps)]
+    say(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    per_stage = {s: [] for s in stages}
+    for ev in evs:
+        for j, s in enumerate(stages):
+            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
+    med = {s: float(np.median(v)) for s, v in per_stage.items()}
+    attn_ms = float(np.mean(per_stage["sparse_attn"]))
+    kept = cfg.kept_flops(kk)
+    attn_tflops = kept / (attn_ms * 1e-3) / 1e12
+    score_bytes = 2 * B * H * N * d * 2 + B * H * nt * kk * 4
+    score_ms = float(np.mean(per_stage["score_topk"]))
+    say(f"[bench] step {ms_step:.2f} ms; stages (median ms) {json.dumps({s: round(x, 3) for s, x in med.items()})}")
+
+    # this library's own dense path (k = n_t, 0 % skipping), for the speedup
+    dense = None
+    if not args.no_dense:
+        didx = dense_index(geom)
+        say("[bench] dense path (k = n_t)")
+        sa.attend(didx)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            sa.attend(didx)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        dense = {"ms": round(dense_ms, 3),
+                 "tflops": round(cfg.kept_flops(nt) / (dense_ms * 1e-3) / 1e12, 1),
+                 "speedup_sparse_vs_dense": round(dense_ms / attn_ms, 2),
+                 "ideal_speedup": round(nt / kk, 2)}
+        del didx
+
+    if args.copy_calibration:
+        n = 1 << 29  # 1 GiB of bf16
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        say("[bench] copy calibration: 3 x 1 GiB device copies")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        say("[bench] CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(cfg, wl, kk, n_sel)
+
+    traffic = traffic_from_counters()
+    roof = {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": round(attn_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "flops_per_launch": kept, "avg_launch_ms": round(attn_ms, 4)}
+    result = {
+        "metric": METRIC,
+        "value": round(kept / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} H={H} d={d} latent {'x'.join(map(str, cfg.grid))} "
+                               f"(N={N}), tile {P}, k={kk}/{nt} kept ({100 * (1 - kk / nt):.0f}% skipped)",
+                   "batch": B, "heads": H, "seq_len": N, "head_dim": d, "tile": P, "topk": kk, "n_tiles": nt,
+                   "tile_shapes": sorted(set(wl.shapes)), "tilemap_query_tiles_per_head": n_sel},
+        "sparse_attn_ms_per_call": round(attn_ms, 4),
+        "sparse_attn_tflops": round(attn_tflops, 1),
+        "sparse_attn_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "scoring_ms": round(score_ms, 4),
+        "scoring_gbps": round(score_bytes / (score_ms * 1e-3) / 1e9, 1),
+        "scoring_frac_hbm_peak": round(score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "stages_median_ms": {s: round(x, 4) for s, x in med.items()},
+        "dense": dense,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
