@@ -27,9 +27,12 @@
  *  - VEDA_TILE_ROWS: [B, H, N, d]; row r holds token perm_h[r] of the raster sequence,
  *    where tile r / P is numbered row-major over the tile grid (t/p_t, h/p_h, w/p_w) and
  *    r % P row-major over (p_t, p_h, p_w).  Q, K and the attention output use it.
- *  - VEDA_TILE_COLS: [B, H, n_t, d, P]; the same tiles, each stored channel-major
- *    (element (token o, channel c) of tile j at ((j*d + c)*P + o)).  V uses it, so the
- *    P x V product reads keys contiguously.
+ *  - VEDA_TILE_COLS: [B, H, n_t, d, P]; the same tiles, each stored channel-major:
+ *    element (position p, channel c) of tile j at ((j*d + c)*P + p) holds token
+ *    key(p) of the tile, where within every group of 16 positions the tokens are ordered
+ *    0-3, 8-11, 4-7, 12-15 (key(p) = 16*(p/16) + {0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15}
+ *    [p%16]).  V uses it: that is the order in which the attention kernel's probability
+ *    fragments meet V in the MFMA, so every V operand is one contiguous 16-byte read.
  * The raster layout is [B, N, H, d] with any element strides for b, n, h and d contiguous;
  * raster token n = (t*H + h)*W + w.
  */

@@ -2,14 +2,22 @@
 // Implementation: only the selected, non-contiguous key/value tiles are fetched]
 //
 // bf16 path (d = 128, P = 128), gfx950 MFMA v_mfma_f32_32x32x16_bf16:
-//  - one workgroup (4 waves) per query tile; wave w owns queries 32w .. 32w+31;
-//  - the kept K tile ([key][d]) and V tile ([d][key], channel-major in HBM) are staged in
-//    LDS with XOR swizzles that make the MFMA operand reads bank-conflict free;
+//  - one workgroup (4 waves) per query tile, two workgroups per CU; wave w owns queries
+//    32w .. 32w+31;
+//  - the kept K tile ([key][d]) and V tile ([d][key], channel-major in HBM) are copied
+//    straight into LDS (global_load_lds, no register staging) with the XOR swizzle
+//    "16-byte chunk c of row r at slot c ^ (r & 15)", which makes every MFMA operand read
+//    a conflict-free 16-byte LDS read.  K and V have their own buffers: the next K tile
+//    streams in during softmax + P V, the next V tile during the next Q K^T;
 //  - S^T = K Q^T (32 keys x 32 queries per MFMA block) puts one query per lane column, so
-//    the row max / sum need one exchange between lane halves; O^T = V^T P^T keeps every
-//    lane's accumulators on its own query, so the online-softmax rescale is lane-local;
-//  - softmax in fp32 in the log2 domain (scale * log2 e folded into one multiply), P
-//    rounded to bf16 (nearest-even) for the P V product, 1/l applied in fp32 at the end.
+//    the row max needs one exchange between lane halves; O^T = V^T P^T keeps each lane's
+//    accumulators on its own query, so the online-softmax rescale is lane-local;
+//  - softmax in fp32 in the log2 domain (scale * log2 e folded into one FMA); the running
+//    max only moves when a row max exceeds it by more than 2^8 (the rescale of O is then
+//    rare; p <= 256 stays exact in fp32 and bf16 range); P rounded to bf16 (nearest even)
+//    for P V; 1/l applied in fp32 at the end;
+//  - workgroups are mapped so that each XCD walks consecutive query tiles of one head,
+//    sharing that head's K/V tiles in its L2.
 //
 // MFMA 32x32x16 operand layout (lane l, 0..63): A[m = l%32][k = 8*(l/32) + 0..7],
 // B[k = 8*(l/32) + 0..7][n = l%32], D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15.
@@ -20,60 +28,89 @@ namespace veda {
 
 static constexpr float LOG2E = 1.4426950408889634f;
 static constexpr float LN2 = 0.6931471805599453f;
+static constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8_t pack_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5, float x6,
-                                                float x7) {
-  bf16x8_t r;
-  r[0] = (__bf16)x0;
-  r[1] = (__bf16)x1;
-  r[2] = (__bf16)x2;
-  r[3] = (__bf16)x3;
-  r[4] = (__bf16)x4;
-  r[5] = (__bf16)x5;
-  r[6] = (__bf16)x6;
-  r[7] = (__bf16)x7;
-  return r;
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// Stage one 128x128 bf16 K tile (row-major) and V tile (channel-major) into LDS.
-//  K: 16-byte chunk c of row r at chunk slot c ^ (r & 15).
-//  V: 8-byte granule g of row r at granule slot g ^ (r & 31).
-__device__ __forceinline__ void stage_kv(const uint4 *__restrict__ ksrc, const uint4 *__restrict__ vsrc, uint4 *Ks,
-                                         uint4 *Vs, int t) {
+// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes at base + off land at LDS byte
+// m0_addr + 16 * i.  Issued as inline asm so that the compiler does not treat the pending
+// LDS write as aliasing every LDS read (it would wait for all copies before each read);
+// completion is tracked by the explicit vmcnt waits below.  No output registers; M0 is
+// set by the compiler through the "{m0}" operand.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t m0_addr) {
+  // s_nop: one wait state between the SALU write of M0 and an LDS-DMA load that reads it.
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0_addr) : "memory");
+}
+
+// The calling wave copies rows [32w, 32w+32) of a 128 x 256-byte tile into LDS, 4 rows per
+// instruction; LDS slot (r, s) receives global chunk (r, s ^ (r & 15)).  off[e] is the
+// lane's byte offset in the tile for instruction e.
+__device__ __forceinline__ void tile_to_lds(const char *src, uint32_t lds_base, int w, const uint32_t (&off)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ci = t + 256 * e;
-    const int r = ci >> 4, c = ci & 15;
-    const uint4 kv = ksrc[ci];
-    uint4 vv = vsrc[ci];
-    Ks[r * 16 + (c ^ (r & 15))] = kv;
-    if (r & 1) vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
-    Vs[r * 16 + (c ^ ((r & 31) >> 1))] = vv;
-  }
+  for (int e = 0; e < 8; ++e) dma16(src, off[e], lds_base + (uint32_t)((32 * w + 4 * e) * 256));
 }
 
-__global__ void __launch_bounds__(256) attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-                                                        const __bf16 *__restrict__ vt,
-                                                        const int32_t *__restrict__ kv_idx, int kk, float c2,
-                                                        __bf16 *__restrict__ o, float *__restrict__ lse, Geo g) {
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, hi = lane >> 5;
-  const int64_t head = ((int64_t)b * g.H + h) * (int64_t)g.N * 128;
-  const __bf16 *qh = q + head, *kh = k + head, *vh = vt + head;
-  const int32_t *list = kv_idx + (((int64_t)b * g.H + h) * g.nt + i) * kk;
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// blockIdx.x -> logical tile: XCD x (= blockIdx.x % 8) takes a contiguous range.
+__device__ __forceinline__ int xcd_tile(int bid, int nb) {
+  const int per = nb >> 3;
+  return bid < (per << 3) ? (bid & 7) * per + (bid >> 3) : bid;
+}
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
+                 const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
+                 float *__restrict__ lse, Geo g) {
+  const int L = xcd_tile(blockIdx.x, gridDim.x);
+  const int i = L % g.nt;
+  const int64_t bh = L / g.nt;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
+  const int64_t head = bh * (int64_t)g.N * 128;
+  const __bf16 *qh = q + head;
+  const char *kh = reinterpret_cast<const char *>(k + head), *vh = reinterpret_cast<const char *>(vt + head);
+  const int32_t *list = kv_idx + (bh * g.nt + i) * kk;
+  const int last = g.nt - 1;
 
   __shared__ uint4 Ks[128 * 16];
   __shared__ uint4 Vs[128 * 16];
-  const char *Vb = reinterpret_cast<const char *>(Vs);
 
+  // Q fragments first, consumed by an empty asm so that they have arrived before the first
+  // copy is issued (otherwise the compiler sinks the loads and waits for them in the loop).
   const int qrow = i * 128 + 32 * w + lr;
   bf16x8_t qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qh + (int64_t)qrow * 128 + 16 * s + 8 * hi);
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+
+  uint32_t off[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 32 * w + 4 * e + (lane >> 4);
+    off[e] = (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+  }
+  const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
+  int jn = min(max(list[0], 0), last);  // out-of-range entries are clamped
+  tile_to_lds(kh + (int64_t)jn * 32768, ks_lds, w, off);
+  tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
 
   f32x16_t acc_o[4];
 #pragma unroll
@@ -83,12 +120,10 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(const __bf16 *__restrict
   float m_run = -1e30f, l_run = 0.f;
 
   for (int tt = 0; tt < kk; ++tt) {
-    const int j = min(max(list[tt], 0), g.nt - 1);  // out-of-range entries are clamped
-    __syncthreads();
-    stage_kv(reinterpret_cast<const uint4 *>(kh + (int64_t)j * 128 * 128),
-             reinterpret_cast<const uint4 *>(vh + (int64_t)j * 128 * 128), Ks, Vs, t);
-    __syncthreads();
-
+    const bool more = tt + 1 < kk;
+    // ---- S^T = K Q^T on the K tile in LDS (its loads were issued before the V loads)
+    wait_vmem<8>();
+    barrier();
     f32x16_t acc_s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -97,52 +132,71 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(const __bf16 *__restrict
       const int row = 32 * kb + lr;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int c = 2 * s + hi;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + (c ^ (row & 15))]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (row & 15))]);
         acc_s[kb] = mfma32(a, qf[s], acc_s[kb]);
       }
     }
+    wait_lds();
+    barrier();  // every wave has its K operands: the buffer may be refilled
+    if (more) {
+      jn = min(max(list[tt + 1], 0), last);
+      tile_to_lds(kh + (int64_t)jn * 32768, ks_lds, w, off);
+    }
 
+    // ---- online softmax (log2 domain)
     float mx = -1e30f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = exp2f(m_run - m_new);
-    float lsum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    if (__ballot(mx > m_run + RESCALE_SLACK)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(acc_s[kb][r], c2, -m_new));
-        acc_s[kb][r] = p;
-        lsum += p;
-      }
-    l_run = fmaf(l_run, alpha, lsum);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+    }
+    // P = exp2(s * c - m) rounded to bf16; l sums the rounded values, so that the weights
+    // that multiply V are exactly the ones normalised (matters for near one-hot rows).
+    bf16x8_t pb[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const f32x16_t &ps = acc_s[s >> 1];
-      const int r0 = 8 * (s & 1);
-      const bf16x8_t pb = pack_bf16x8(ps[r0], ps[r0 + 1], ps[r0 + 2], ps[r0 + 3], ps[r0 + 4], ps[r0 + 5], ps[r0 + 6],
-                                      ps[r0 + 7]);
-      const int g0 = 4 * s + hi, g1 = 4 * s + 2 + hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[s][e] = (__bf16)fast_exp2(fmaf(acc_s[s >> 1][8 * (s & 1) + e], c2, -m_run));
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      ls[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[s], pb[s], 0, 1), ones, ls[0], false);
+      ls[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[s], pb[s], 2, 3), ones, ls[1], false);
+      ls[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[s], pb[s], 4, 5), ones, ls[2], false);
+      ls[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[s], pb[s], 6, 7), ones, ls[3], false);
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+    // ---- O^T += V^T P^T on the V tile in LDS
+    if (more)
+      wait_vmem<8>();
+    else
+      wait_vmem<0>();
+    barrier();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int drow = 32 * db + lr;
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(Vb + drow * 256 + ((g0 ^ (drow & 31)) << 3));
-        const bf16x4_t hi4 = *reinterpret_cast<const bf16x4_t *>(Vb + drow * 256 + ((g1 ^ (drow & 31)) << 3));
-        const bf16x8_t a = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[db] = mfma32(a, pb, acc_o[db]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Vs[drow * 16 + ((2 * s + hi) ^ (drow & 15))]);
+        acc_o[db] = mfma32(a, pb[s], acc_o[db]);
       }
     }
+    wait_lds();
+    barrier();  // every wave has its V operands
+    if (more) tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -160,7 +214,7 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(const __bf16 *__restrict
       v[3] = (__bf16)(acc_o[db][4 * r4 + 3] * inv);
       *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
     }
-  if (lse != nullptr && hi == 0) lse[((int64_t)b * g.H + h) * g.N + qrow] = (m_run + log2f(l_tot)) * LN2;
+  if (lse != nullptr && hi == 0) lse[bh * g.N + qrow] = (m_run + log2f(l_tot)) * LN2;
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row, keys one at a time from LDS.
@@ -187,7 +241,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
     for (int e = t; e < 64 * 64; e += 64) {
       const int r = e >> 6, c = e & 63;
       Ks[r][c] = k[head + ((int64_t)j * 64 + r) * 64 + c];  // row r = key, c = channel
-      Vs[c][r] = vt[head + ((int64_t)j * 64 + r) * 64 + c];  // channel-major: r = channel, c = key
+      Vs[cols_key(c)][r] = vt[head + ((int64_t)j * 64 + r) * 64 + c];  // channel-major: r = channel, c = position
     }
     __syncthreads();
     for (int x = 0; x < 64; ++x) {
@@ -211,12 +265,11 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
 
 hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
                               const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st) {
-  const dim3 grid(g.nt, g.H, g.B);
   if (dt == VEDA_BF16)
-    attn_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk,
-                                           scale * LOG2E, (__bf16 *)o, lse, g);
+    attn_bf16_kernel<<<dim3(g.nt * g.H * g.B), 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v,
+                                                             kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g);
   else
-    attn_f32_kernel<<<grid, 64, 0, st>>>((const float *)q, (const float *)k, (const float *)v, kv_idx, kk, scale,
+    attn_f32_kernel<<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, (const float *)v, kv_idx, kk, scale,
                                          (float *)o, lse, g);
   return hipGetLastError();
 }

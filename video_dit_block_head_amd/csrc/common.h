@@ -19,6 +19,7 @@ struct Geo {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -29,6 +30,15 @@ __device__ __forceinline__ int64_t tile_row_token(int j, int o, int pt, int ph, 
   const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
   const int ow = o % pw, oh = (o / pw) % ph, ot = o / (pw * ph);
   return ((int64_t)(jt * pt + ot) * Hs + (jh * ph + oh)) * Ws + (jw * pw + ow);
+}
+
+// Channel-major tiles (VEDA_TILE_COLS) store, in each group of 16 consecutive positions,
+// the tile's tokens (keys) 0-3, 8-11, 4-7, 12-15 of that group: key at position p.  This is
+// the order in which the S^T accumulator of a 32x32 MFMA block reaches the k-slots of the
+// next MFMA's B operand, so the matching V^T operand is one contiguous 16-byte read.
+__host__ __device__ __forceinline__ int cols_key(int p) {
+  const int q = p & 15;
+  return (p & ~15) | (q < 4 || q >= 12 ? q : (q < 8 ? q + 4 : q - 4));
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h16) { return __uint_as_float(h16 << 16); }

@@ -30,9 +30,9 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(uint8_t *__restrict__ 
   }
 }
 
-// Column layout, bf16: each thread moves one 8-token x 8-channel block, transposing it in
-// registers, so that each tile is written channel-major ([d][P]).  Reads of a token row are
-// coalesced across the 16 lanes that share the row.
+// Column layout, bf16: each thread moves one 8-position x 8-channel block, transposing it
+// in registers, so that each tile is written channel-major ([d][P]) with the key order of
+// cols_key().  Reads of a token row are coalesced across the 16 lanes that share the row.
 __global__ void __launch_bounds__(256) gather_cols_bf16_kernel(const uint16_t *__restrict__ raster, int64_t rs_b,
                                                                int64_t rs_n, int64_t rs_h,
                                                                uint16_t *__restrict__ tiled, Geo g, HeadShapes hs) {
@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(256) gather_cols_bf16_kernel(const uint16_t *_
   uint32_t in[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t n = tile_row_token(j, tb * 8 + i, pt, ph, pw, g.Hs, g.Ws);
+    const int64_t n = tile_row_token(j, cols_key(tb * 8 + i), pt, ph, pw, g.Hs, g.Ws);
     const uint4 v = *reinterpret_cast<const uint4 *>(raster + b * rs_b + n * rs_n + h * rs_h + cb * 8);
     in[i][0] = v.x;
     in[i][1] = v.y;
@@ -71,9 +71,9 @@ __global__ void __launch_bounds__(256) gather_cols_f32_kernel(const float *__res
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
   float *tbase = tiled + (((int64_t)b * g.H + h) * g.nt + j) * (int64_t)g.d * g.P;
   for (int e = threadIdx.x; e < g.P * g.d; e += blockDim.x) {
-    const int o = e % g.P, c = e / g.P;
-    const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
-    tbase[(int64_t)c * g.P + o] = raster[b * rs_b + n * rs_n + h * rs_h + c];
+    const int p = e % g.P, c = e / g.P;
+    const int64_t n = tile_row_token(j, cols_key(p), pt, ph, pw, g.Hs, g.Ws);
+    tbase[(int64_t)c * g.P + p] = raster[b * rs_b + n * rs_n + h * rs_h + c];
   }
 }
 
