@@ -136,20 +136,28 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype,
                                  const int32_t *kv_idx, int32_t k, float softmax_scale,
                                  void *o_tiled, float *lse, hipStream_t stream);
 
+/* Workspace (bytes) that veda_oracle_tilemap needs: B*H*n_sel*n_t*P floats. */
+size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel);
+
 /* Oracle tile map.  [Technical Summary §2.1 "Target Construction": max-pooling of the
  * full-attention matrix over query-key tile regions; §2.3: built in two passes on random
  * subsets of query tiles]  For each selected query tile a (q_tiles[b, h, a], or a itself
  * if q_tiles is NULL) and each key tile j:
  *   tilemap[b, h, a, j] = max over queries q of tile, keys x of tile j, of
  *                         exp(s(q, x) - lse(q)),  s = q.x * softmax_scale,
- *   lse(q) = log sum over all N keys of exp(s(q, x))  (pass 1; written to lse if non-NULL,
- *   [B, H, n_sel * P] f32).  q_tiled, k_tiled: VEDA_TILE_ROWS.
+ *   lse(q) = log sum over all N keys of exp(s(q, x)).
+ * Pass 1 sweeps the keys once, accumulating lse(q) and keeping the row max of s over each
+ * key tile in `workspace`; pass 2 normalises those maxima and pools them over the queries.
+ *   q_tiled, k_tiled: VEDA_TILE_ROWS
  *   q_tiles: DEVICE int32 [B, H, n_sel] in [0, n_t) (entries outside are clamped), or
- *            NULL (then n_sel must be n_t). */
+ *            NULL (then n_sel must be n_t)
+ *   tilemap: out [B, H, n_sel, n_t] f32;  lse: out [B, H, n_sel * P] f32, nullable
+ *   workspace: >= veda_oracle_tilemap_workspace_bytes(g, n_sel) bytes of device memory */
 veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
                                 const void *q_tiled, const void *k_tiled, float softmax_scale,
                                 const int32_t *q_tiles, int32_t n_sel,
-                                float *tilemap, float *lse, hipStream_t stream);
+                                float *tilemap, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 const char *veda_status_str(veda_status s);
 int veda_last_hip_error(void);

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 9, syms
+    assert len(syms) == 10, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -117,11 +117,16 @@ def test_attn_validation(L):
 def test_tilemap_validation(L):
     g = geom()
     f = L.veda_oracle_tilemap
-    assert f(g.ref, V.BF16, A, A, 0.088, None, 5, A, None, None) == SHAPE     # NULL list needs n_sel = n_t
-    assert f(g.ref, V.BF16, A, A, 0.088, A, 0, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, A, 0.088, A, 33, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, None, 0.088, A, 4, A, None, None) == NULL
-    assert f(g.ref, V.BF16, A, A, 0.088, MIS, 4, A, None, None) == ALIGN
+    big = 1 << 40
+    assert f(g.ref, V.BF16, A, A, 0.088, None, 5, A, None, A, big, None) == SHAPE   # NULL list needs n_sel = n_t
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 0, A, None, A, big, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 33, A, None, A, big, None) == SHAPE
+    assert f(g.ref, V.BF16, A, None, 0.088, A, 4, A, None, A, big, None) == NULL
+    assert f(g.ref, V.BF16, A, A, 0.088, MIS, 4, A, None, A, big, None) == ALIGN
+    need = L.veda_oracle_tilemap_workspace_bytes(g.ref, 4)
+    assert need == 1 * 2 * 4 * 32 * 128 * 4
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 4, A, None, None, big, None) == WS
+    assert f(g.ref, V.BF16, A, A, 0.088, A, 4, A, None, A, need - 1, None) == WS
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

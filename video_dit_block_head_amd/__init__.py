@@ -73,7 +73,8 @@ def lib():
                                           vp, sz, vp]),
             "veda_topk_mask": (i32, [i64, i32, vp, i32, vp, vp, vp]),
             "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]),
-            "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp]),
+            "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
+            "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
             "veda_status_str": (ctypes.c_char_p, [i32]),
             "veda_last_hip_error": (ctypes.c_int, []),
             "veda_version": (ctypes.c_char_p, []),
@@ -166,7 +167,14 @@ def veda_sparse_attn_fwd(geom, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_sca
         _stream(stream)))
 
 
-def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse=None, stream=None):
+def veda_oracle_tilemap_workspace_bytes(geom, n_sel):
+    return int(lib().veda_oracle_tilemap_workspace_bytes(geom.ref, int(n_sel)))
+
+
+def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse=None, workspace=None,
+                        stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("veda_oracle_tilemap", lib().veda_oracle_tilemap(
         geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), float(softmax_scale),
-        _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _stream(stream)))
+        _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
+        ws_bytes, _stream(stream)))

@@ -137,9 +137,19 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
                                        stream));
 }
 
+size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {
+  if (g == nullptr || g->batch < 1 || g->heads < 1 || g->tile < 1 || n_sel < 1) return 0;
+  Geo geo{};
+  geo.B = g->batch;
+  geo.H = g->heads;
+  geo.P = g->tile;
+  geo.nt = (int32_t)((int64_t)g->t * g->h * g->w / g->tile);
+  return tilemap_workspace_bytes(geo, n_sel);
+}
+
 veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
                                 float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
-                                float *lse, hipStream_t stream) {
+                                float *lse, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   veda_status s = check_geom(g, dtype, &geo, &hs);
@@ -147,10 +157,12 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void
   if (!q_tiled || !k_tiled || !tilemap) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
   if (geo.nt > TILEMAP_MAX_NT) return VEDA_ERR_UNSUPPORTED;
-  const void *ptrs[] = {q_tiled, k_tiled, q_tiles, tilemap, lse};
+  const void *ptrs[] = {q_tiled, k_tiled, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
-  return hip_status(launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, stream));
+  if (workspace == nullptr || workspace_bytes < tilemap_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
+  return hip_status(
+      launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, workspace, stream));
 }
 
 const char *veda_status_str(veda_status s) {

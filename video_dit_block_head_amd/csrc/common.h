@@ -100,4 +100,54 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_col
   }
 }
 
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes at base + off land at LDS byte
+// m0_addr + 16 * i.  Issued as inline asm so that the compiler does not treat the pending
+// LDS write as aliasing every LDS read (it would wait for all copies before each read);
+// completion is tracked by the explicit vmcnt waits below.  No output registers; M0 is
+// set by the compiler through the "{m0}" operand.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t m0_addr) {
+  // s_nop: one wait state between the SALU write of M0 and an LDS-DMA load that reads it.
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0_addr) : "memory");
+}
+
+// The calling wave copies rows [32w, 32w+32) of a 128 x 256-byte tile into LDS, 4 rows per
+// instruction; LDS slot (r, s) receives global chunk (r, s ^ (r & 15)).  off[e] is the
+// lane's byte offset in the tile for instruction e.
+__device__ __forceinline__ void tile_to_lds(const char *src, uint32_t lds_base, int w, const uint32_t (&off)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dma16(src, off[e], lds_base + (uint32_t)((32 * w + 4 * e) * 256));
+}
+
+// Per-lane byte offsets of tile_to_lds for wave w: instruction e covers rows 32w+4e .. +3,
+// lane -> (row 32w + 4e + lane/16, slot lane%16), source chunk slot ^ (row & 15).
+__device__ __forceinline__ void tile_dma_offsets(int w, int lane, uint32_t (&off)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 32 * w + 4 * e + (lane >> 4);
+    off[e] = (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+  }
+}
+
+// Explicit waits for the copies above (the compiler does not know about them).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// blockIdx.x -> logical tile: XCD x (= blockIdx.x % 8) takes a contiguous range.
+__device__ __forceinline__ int xcd_tile(int bid, int nb) {
+  const int per = nb >> 3;
+  return bid < (per << 3) ? (bid & 7) * per + (bid >> 3) : bid;
+}
+
 }  // namespace veda

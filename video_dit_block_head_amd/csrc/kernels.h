@@ -21,7 +21,8 @@ hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int
 hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
                               const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st);
 
+size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
-                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, hipStream_t st);
+                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st);
 
 }  // namespace veda

@@ -2,12 +2,14 @@
 // (query tile x key tile) region.  [Technical Summary: Veda, §2.1 "Target Construction";
 // §2.3: ground-truth heatmaps in two passes, on subsets of query tiles]
 //
-// One workgroup per selected query tile, two passes over all N keys inside one launch:
-//  pass 1: per query row, running max and sum of exp2 -> log2-domain LSE;
-//  pass 2: S^T recomputed bit-identically; per key tile the row max of s*c - lse, then the
-//          max over the tile's 128 queries (kept per wave in LDS, combined at the end);
-//          M = exp2 of that.
-// bf16 path uses the same MFMA S^T = K Q^T blocking as the attention kernel.
+// bf16 path: one workgroup (4 waves x 32 queries) per selected query tile.
+//  pass 1 (one sweep over all N keys): S^T = K Q^T per key tile (MFMA, same blocking as the
+//          attention kernel; K tiles double-buffered in LDS through direct-to-LDS copies);
+//          per query row the running log-sum-exp (log2 domain, lazy max) and the row max of
+//          each key tile, m[q][j] = max_x s(q, x) * c, written to the workspace;
+//  pass 2: M[j] = exp2(max over the tile's queries of m[q][j] - lse2[q]), from the
+//          workspace (no second Q K^T).
+// exp is monotone, so this is the max over the region of exp(s - lse).
 #include "common.h"
 #include "kernels.h"
 
@@ -15,95 +17,105 @@ namespace veda {
 
 static constexpr float TM_LOG2E = 1.4426950408889634f;
 static constexpr float TM_LN2 = 0.6931471805599453f;
+static constexpr float TM_SLACK = 8.0f;  // lazy running-max slack (log2 units)
 static constexpr int TM_MAX_NT = 1280;
 
-__device__ __forceinline__ void stage_k(const uint4 *__restrict__ ksrc, uint4 *Ks, int t) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ci = t + 256 * e;
-    const int r = ci >> 4, c = ci & 15;
-    Ks[r * 16 + (c ^ (r & 15))] = ksrc[ci];
-  }
+size_t tilemap_workspace_bytes(const Geo &g, int n_sel) {
+  return (size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float);
 }
 
-// Row max (over this lane's 64 keys and its partner lane's) of S^T for the wave's queries.
-__device__ __forceinline__ void tile_scores_t(const uint4 *Ks, const bf16x8_t (&qf)[8], int lr, int hi,
-                                              f32x16_t (&acc)[4]) {
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
-    const int row = 32 * kb + lr;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + hi;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + (c ^ (row & 15))]);
-      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc[kb], 0, 0, 0);
-    }
-  }
-}
-
-__global__ void __launch_bounds__(256) tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-                                                           float c2, const int32_t *__restrict__ q_tiles, int n_sel,
-                                                           float *__restrict__ out, float *__restrict__ lse_out,
-                                                           Geo g) {
-  const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, hi = lane >> 5;
-  const int64_t bh = (int64_t)b * g.H + h;
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
+                    const int32_t *__restrict__ q_tiles, int n_sel, float *__restrict__ out,
+                    float *__restrict__ lse_out, float *__restrict__ rowmax, Geo g) {
+  const int L = xcd_tile(blockIdx.x, gridDim.x);
+  const int a = L % n_sel;
+  const int64_t bh = L / n_sel;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) : a;  // clamped
-  const __bf16 *qh = q + bh * (int64_t)g.N * 128, *kh = k + bh * (int64_t)g.N * 128;
+  const __bf16 *qh = q + bh * (int64_t)g.N * 128;
+  const char *kh = reinterpret_cast<const char *>(k + bh * (int64_t)g.N * 128);
+  float *rm = rowmax + (bh * n_sel + a) * (int64_t)g.nt * 128;   // [j][128 queries]
 
-  __shared__ uint4 Ks[128 * 16];
-  __shared__ float wmax[4][TM_MAX_NT];
+  __shared__ uint4 Kb[2][128 * 16];
+  __shared__ float lse_s[128];
 
   const int qrow = i * 128 + 32 * w + lr;
   bf16x8_t qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qh + (int64_t)qrow * 128 + 16 * s + 8 * hi);
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
-  f32x16_t acc[4];
+  uint32_t off[8];
+  tile_dma_offsets(w, lane, off);
+  const uint32_t kb_lds[2] = {lds_addr(Kb[0]), lds_addr(Kb[1])};
+  tile_to_lds(kh, kb_lds[0], w, off);
+  if (g.nt > 1) tile_to_lds(kh + 32768, kb_lds[1], w, off);
+
   float m_run = -1e30f, l_run = 0.f;
-  for (int j = 0; j < g.nt; ++j) {  // pass 1
-    __syncthreads();
-    stage_k(reinterpret_cast<const uint4 *>(kh + (int64_t)j * 128 * 128), Ks, t);
-    __syncthreads();
-    tile_scores_t(Ks, qf, lr, hi, acc);
+  for (int j = 0; j < g.nt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < g.nt)
+      wait_vmem<8>();  // tile j+1's copies may still be in flight
+    else
+      wait_vmem<0>();
+    barrier();
+    f32x16_t acc[4];
+    const uint4 *Ks = Kb[buf];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+      const int row = 32 * kb + lr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (row & 15))]);
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[s], acc[kb], 0, 0, 0);
+      }
+    }
+    wait_lds();
+    barrier();  // every wave has read this buffer
+    if (j + 2 < g.nt) tile_to_lds(kh + (int64_t)(j + 2) * 32768, kb_lds[buf], w, off);
+
     float mx = -1e30f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    float lsum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    if (hi == 0) rm[(int64_t)j * 128 + 32 * w + lr] = mx;
+    if (__ballot(mx > m_run + TM_SLACK)) {
+      const float m_new = fmaxf(m_run, mx);
+      l_run *= __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+    }
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lsum += exp2f(fmaf(acc[kb][r], c2, -m_new));
-    l_run = fmaf(l_run, exp2f(m_run - m_new), lsum);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) ls[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[kb][r], c2, -m_run));
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   }
   const float lse2 = m_run + log2f(l_run + __shfl_xor(l_run, 32));
-  if (lse_out != nullptr && hi == 0) lse_out[bh * (int64_t)n_sel * 128 + (int64_t)a * 128 + 32 * w + lr] = lse2 * TM_LN2;
-
-  for (int j = 0; j < g.nt; ++j) {  // pass 2
-    __syncthreads();
-    stage_k(reinterpret_cast<const uint4 *>(kh + (int64_t)j * 128 * 128), Ks, t);
-    __syncthreads();
-    tile_scores_t(Ks, qf, lr, hi, acc);
-    float mx = -1e30f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
-    float x = fmaf(mx, c2, -lse2);
-    x = wave_max(x);
-    if (lane == 0) wmax[w][j] = x;
+  if (hi == 0) {
+    lse_s[32 * w + lr] = lse2;
+    if (lse_out != nullptr) lse_out[(bh * n_sel + a) * 128 + 32 * w + lr] = lse2 * TM_LN2;
   }
-  __syncthreads();
+  __syncthreads();  // row maxima (global) and lse_s (LDS) visible to the workgroup
+
   float *dst = out + (bh * n_sel + a) * (int64_t)g.nt;
-  for (int j = t; j < g.nt; j += 256)
-    dst[j] = exp2f(fmaxf(fmaxf(wmax[0][j], wmax[1][j]), fmaxf(wmax[2][j], wmax[3][j])));
+  for (int j = t; j < g.nt; j += 256) {
+    const float4 *src = reinterpret_cast<const float4 *>(rm + (int64_t)j * 128);
+    float x = -INFINITY;
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      const float4 v = src[c];
+      x = fmaxf(x, fmaxf(fmaxf(v.x - lse_s[4 * c], v.y - lse_s[4 * c + 1]),
+                         fmaxf(v.z - lse_s[4 * c + 2], v.w - lse_s[4 * c + 3])));
+    }
+    dst[j] = __builtin_amdgcn_exp2f(x);
+  }
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row.
@@ -152,14 +164,14 @@ __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict
 }
 
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
-                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, hipStream_t st) {
-  const dim3 grid(n_sel, g.H, g.B);
+                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st) {
   if (dt == VEDA_BF16)
-    tilemap_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel,
-                                              tilemap, lse, g);
+    tilemap_bf16_kernel<<<dim3(n_sel * g.H * g.B), 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
+                                                                 scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse,
+                                                                 (float *)ws, g);
   else
-    tilemap_f32_kernel<<<grid, 64, 0, st>>>((const float *)q, (const float *)k, scale, q_tiles, n_sel, tilemap, lse,
-                                            g);
+    tilemap_f32_kernel<<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale, q_tiles,
+                                                             n_sel, tilemap, lse, g);
   return hipGetLastError();
 }
 

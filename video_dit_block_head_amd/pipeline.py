@@ -8,8 +8,8 @@ import math
 
 import torch
 
-from . import (BF16, COLS, ROWS, Geom, veda_oracle_tilemap, veda_sparse_attn_fwd, veda_tile_gather,
-               veda_trippool_score, veda_trippool_workspace_bytes)
+from . import (COLS, ROWS, Geom, veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes, veda_sparse_attn_fwd,
+               veda_tile_gather, veda_trippool_score, veda_trippool_workspace_bytes)
 
 
 class SparseAttention:
@@ -33,6 +33,7 @@ class SparseAttention:
         nbytes = veda_trippool_workspace_bytes(g, self.w1.shape[-1], self.w2.shape[-1])
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self._idx = {}
+        self._tm_ws = {}
 
     def idx_buffer(self, k):
         if k not in self._idx:
@@ -64,7 +65,11 @@ class SparseAttention:
         return out
 
     def tilemap(self, q_tiles, n_sel, out, lse=None):
-        veda_oracle_tilemap(self.geom, self.q_t, self.k_t, self.softmax_scale, q_tiles, n_sel, out, lse)
+        if n_sel not in self._tm_ws:
+            nbytes = veda_oracle_tilemap_workspace_bytes(self.geom, n_sel)
+            self._tm_ws[n_sel] = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        veda_oracle_tilemap(self.geom, self.q_t, self.k_t, self.softmax_scale, q_tiles, n_sel, out, lse,
+                            self._tm_ws[n_sel])
         return out
 
     def forward(self, q, k, v, topk, out):
