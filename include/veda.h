@@ -102,8 +102,8 @@ size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int
  *   probs:      out [B, H, n_t, n_t] f32 row softmax, nullable
  *   q_desc, k_desc: out [B, H, n_t, 3d] f32, nullable
  *   topk, idx:  topk in [1, n_t] with idx out [B, H, n_t, topk] int32; or topk = 0, idx NULL
- * At least one of scores / probs / idx must be requested.  mlp_out <= 64,
- * mlp_hidden <= 256 (multiples of 4).  workspace >= veda_trippool_workspace_bytes. */
+ * At least one of scores / probs / idx must be requested.  Implemented for
+ * mlp_hidden = 256 and mlp_out = 64.  workspace >= veda_trippool_workspace_bytes. */
 veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype,
                                 const void *q_tiled, const void *k_tiled,
                                 const float *w1_q, const float *w2_q,

@@ -82,6 +82,7 @@ def test_score_validation(L):
     assert score(L, g, topk=6, idx=None) == NULL
     assert score(L, g, topk=33) == SHAPE                       # n_t = 32
     assert score(L, g, hidden=512) == UNSUP
+    assert score(L, g, hidden=128) == UNSUP
     assert score(L, g, out=128) == UNSUP
     assert score(L, g, ws=None) == WS
     need = L.veda_trippool_workspace_bytes(g.ref, 256, 64)

@@ -100,7 +100,7 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void
   if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
   if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
   if (topk < 0 || topk > geo.nt) return VEDA_ERR_SHAPE;
-  if (mlp_hidden < 1 || mlp_hidden > 256 || mlp_out < 1 || mlp_out > 64) return VEDA_ERR_UNSUPPORTED;
+  if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
   for (const void *p : ptrs)

@@ -1,251 +1,243 @@
 // Distilled tile scoring: TripPool descriptors -> per-head MLP -> tile scores -> row
 // softmax / top-k.  [Technical Summary: Veda, §2.1 Distilled Tile Scoring]
 //
-//  pool_kernel   HBM-bound stream over Q and K tiles; one workgroup per (tile, head, b, Q|K).
-//  mlp_kernel    y = GELU(desc W1) W2 on 32 descriptors per workgroup, fp32 FMA.
-//  score_kernel  16 query-tile rows per workgroup, one wave per 4 rows; row held in
-//                registers (lane owns columns lane, lane+64, ...); softmax and top-k are
-//                wave-level (ballot/popcount), deterministic.
-//  topk_kernel   standalone top-k, one wave per row.
+//  pool_mlp_kernel   32 tiles of one (head, batch, Q|K) per workgroup.  Each wave streams 8
+//                    tiles (HBM-bound: 16-byte loads, 32 per lane in flight) into their
+//                    [mean|max|min] descriptors, then the workgroup runs the MLP on fp32
+//                    MFMA (v_mfma_f32_32x32x2f32): layer 1 32x3d @ 3d x256 (64 hidden units
+//                    per wave), exact-erf GELU, layer 2 32x256 @ 256x64 (two K halves summed
+//                    in a fixed order).  Other workgroups' streaming overlaps this one's MFMA.
+//  score_topk_kernel 16 query-tile rows per workgroup: S = y_q y_k^T on fp32 MFMA
+//                    (v_mfma_f32_16x16x4f32) into an LDS row block, then one wave per row
+//                    for softmax and top-k (ballot/popcount; deterministic).
+//  topk_kernel       standalone top-k, one wave per row.
 #include "common.h"
 #include "kernels.h"
 
 namespace veda {
 
-static constexpr int MLP_ROWS = 32;
+static constexpr int PM_ROWS = 32;    // descriptors per workgroup
+static constexpr int PM_DS = 385;     // LDS row stride (floats) of the descriptor block
+static constexpr int PM_HS = 257;     // LDS row stride (floats) of the hidden block
+static constexpr int MLP_HIDDEN = 256, MLP_OUT = 64;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out) {
   (void)hidden;
   const size_t nt = (size_t)g.B * g.H * g.nt;
-  return 2 * align256(nt * 3 * g.d * sizeof(float)) + align256(2 * nt * mlp_out * sizeof(float));
+  return align256(2 * nt * mlp_out * sizeof(float));
 }
 
-// ---------------------------------------------------------------------------------------
-// TripPool.  Thread (row group rg = t/16, chunk = t%16) accumulates rows rg, rg+16, ... of
-// its 16-byte channel chunk; partials are combined in a fixed order (deterministic).
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// EB: element bytes (2: bf16 with d = P = 128; 4: f32 with d = P = 64).  Rows are 256 bytes.
 template <int EB>
-__global__ void __launch_bounds__(256) pool_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
-                                                   float *__restrict__ qdesc, float *__restrict__ kdesc, Geo g) {
-  constexpr int EPC = 16 / EB;
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
-  const uint8_t *src = (which ? k : q) + ((((int64_t)b * g.H + h) * g.N + (int64_t)j * g.P) * g.d) * EB;
-  const int chunk = threadIdx.x & 15, rg = threadIdx.x >> 4;
-  float s[EPC], mx[EPC], mn[EPC];
+__global__ void __launch_bounds__(256) pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
+                                                       const float *__restrict__ w1q, const float *__restrict__ w2q,
+                                                       const float *__restrict__ w1k, const float *__restrict__ w2k,
+                                                       float *__restrict__ y, float *__restrict__ qdesc,
+                                                       float *__restrict__ kdesc, Geo g) {
+  constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
+  constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
+  constexpr int D = EB == 2 ? 128 : 64;   // head dim
+  constexpr int D3 = 3 * D;
+  const int r0 = blockIdx.x * PM_ROWS, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ float Ds[PM_ROWS * PM_DS];   // descriptors, then the hidden layer
+  __shared__ float part[2][32][33];       // layer-2 partial sums of the second K half
+
+  // ---- TripPool: wave w pools tiles r0 + 8w .. r0 + 8w + 7.  Lane (rg = lane/16, c = lane%16)
+  // accumulates rows rg, rg + 4, ... of its 16-byte channel chunk c; the 4 row groups are
+  // combined as (g0 + g1) + (g2 + g3) by lane exchanges.
+  const uint8_t *src0 = (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
+  const int rg = lane >> 4, c = lane & 15;
+  for (int tt = 0; tt < 8; ++tt) {
+    const int row = 8 * w + tt, j = r0 + row;
+    float s[EPC], mx[EPC], mn[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) {
-    s[e] = 0.f;
-    mx[e] = -INFINITY;
-    mn[e] = INFINITY;
-  }
-  const int64_t row_bytes = (int64_t)g.d * EB;
-  for (int o = rg; o < g.P; o += 16) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(src + o * row_bytes + chunk * 16);
-    float x[EPC];
-    if (EB == 2) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int e = 0; e < EPC; ++e) {
+      s[e] = 0.f;
+      mx[e] = -INFINITY;
+      mn[e] = INFINITY;
+    }
+    if (j < g.nt) {
+      const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
+      uint4 v[P / 4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(w[e] << 16);
-        x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      for (int i = 0; i < P / 4; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + (rg + 4 * i) * 256);
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i) {
+        float x[EPC];
+        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        if (EB == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(wd[e] << 16);
+            x[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          s[e] += x[e];
+          mx[e] = fmaxf(mx[e], x[e]);
+          mn[e] = fminf(mn[e], x[e]);
+        }
       }
-    } else {
-      x[0] = __uint_as_float(v.x);
-      x[1] = __uint_as_float(v.y);
-      x[2] = __uint_as_float(v.z);
-      x[3] = __uint_as_float(v.w);
     }
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      s[e] += x[e];
-      mx[e] = fmaxf(mx[e], x[e]);
-      mn[e] = fminf(mn[e], x[e]);
+      s[e] += __shfl_xor(s[e], 16);
+      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], 16));
+      mn[e] = fminf(mn[e], __shfl_xor(mn[e], 16));
+      s[e] += __shfl_xor(s[e], 32);
+      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], 32));
+      mn[e] = fminf(mn[e], __shfl_xor(mn[e], 32));
     }
-  }
-  __shared__ float part[3][16][128];
+    if (rg == 0) {
+      const bool ok = j < g.nt;
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) {
-    part[0][rg][chunk * EPC + e] = s[e];
-    part[1][rg][chunk * EPC + e] = mx[e];
-    part[2][rg][chunk * EPC + e] = mn[e];
-  }
-  __syncthreads();
-  if (threadIdx.x < g.d) {
-    const int c = threadIdx.x;
-    float ss = 0.f, xx = -INFINITY, nn = INFINITY;
-    for (int r = 0; r < 16; ++r) {
-      ss += part[0][r][c];
-      xx = fmaxf(xx, part[1][r][c]);
-      nn = fminf(nn, part[2][r][c]);
-    }
-    float *dst = (which ? kdesc : qdesc) + (((int64_t)b * g.H + h) * g.nt + j) * 3 * g.d;
-    dst[c] = ss * (1.0f / (float)g.P);  // P is a power of two: exact
-    dst[g.d + c] = xx;
-    dst[2 * g.d + c] = nn;
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// Per-head MLP on MLP_ROWS descriptors.  Layer 1: thread t owns hidden unit t for all rows
-// (descriptors transposed in LDS so a k-step is 8 broadcast 16-byte reads).  Layer 2:
-// thread (o = t%64, group = t/64) owns output o for rows 8*group .. 8*group+7.
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
-
-__global__ void __launch_bounds__(256) mlp_kernel(const float *__restrict__ qdesc, const float *__restrict__ kdesc,
-                                                  const float *__restrict__ w1q, const float *__restrict__ w2q,
-                                                  const float *__restrict__ w1k, const float *__restrict__ w2k,
-                                                  float *__restrict__ y, Geo g, int hidden, int mout) {
-  constexpr int R = MLP_ROWS, RS = R + 4;  // padded row stride (floats)
-  const int D3 = 3 * g.d;
-  const int r0 = blockIdx.x * R, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
-  const float *desc = (which ? kdesc : qdesc) + (((int64_t)b * g.H + h) * g.nt) * D3;
-  const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * hidden;
-  const float *W2 = (which ? w2k : w2q) + (int64_t)h * hidden * mout;
-  __shared__ __attribute__((aligned(16))) float buf[384 * RS];  // descT [D3][RS], then hidT [hidden][RS]
-  const int t = threadIdx.x;
-  for (int e = t; e < R * D3; e += 256) {
-    const int r = e / D3, c = e % D3;
-    buf[c * RS + r] = (r0 + r < g.nt) ? desc[(int64_t)(r0 + r) * D3 + c] : 0.f;
-  }
-  __syncthreads();
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (t < hidden) {
-    for (int c = 0; c < D3; ++c) {
-      const float w = W1[(int64_t)c * hidden + t];
-      const float4 *dv = reinterpret_cast<const float4 *>(&buf[c * RS]);
-#pragma unroll
-      for (int r4 = 0; r4 < R / 4; ++r4) {
-        const float4 dd = dv[r4];
-        acc[4 * r4 + 0] = fmaf(dd.x, w, acc[4 * r4 + 0]);
-        acc[4 * r4 + 1] = fmaf(dd.y, w, acc[4 * r4 + 1]);
-        acc[4 * r4 + 2] = fmaf(dd.z, w, acc[4 * r4 + 2]);
-        acc[4 * r4 + 3] = fmaf(dd.w, w, acc[4 * r4 + 3]);
+      for (int e = 0; e < EPC; ++e) {
+        Ds[row * PM_DS + c * EPC + e] = ok ? s[e] * (1.0f / (float)P) : 0.f;  // P is a power of two
+        Ds[row * PM_DS + D + c * EPC + e] = ok ? mx[e] : 0.f;
+        Ds[row * PM_DS + 2 * D + c * EPC + e] = ok ? mn[e] : 0.f;
       }
     }
   }
-  __syncthreads();  // every thread is done reading descT
-  if (t < hidden) {
-    float4 *hv = reinterpret_cast<float4 *>(&buf[t * RS]);
+  __syncthreads();
+  float *dout = which ? kdesc : qdesc;
+  if (dout != nullptr) {
+    for (int e = t; e < PM_ROWS * D3; e += 256) {
+      const int row = e / D3, col = e % D3;
+      if (r0 + row < g.nt) dout[(((int64_t)b * g.H + h) * g.nt + r0 + row) * D3 + col] = Ds[row * PM_DS + col];
+    }
+  }
+
+  // ---- layer 1 on fp32 MFMA: wave w owns hidden units 64w .. 64w + 63 (two 32-wide blocks).
+  // 32x32x2 operands: A[m = lane%32][k = lane/32], B[k = lane/32][n = lane%32].
+  const int m = lane & 31, kh = lane >> 5;
+  const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * MLP_HIDDEN + 64 * w + m;
+  f32x16_t acc0, acc1;
 #pragma unroll
-    for (int r4 = 0; r4 < R / 4; ++r4)
-      hv[r4] = make_float4(gelu_erf(acc[4 * r4]), gelu_erf(acc[4 * r4 + 1]), gelu_erf(acc[4 * r4 + 2]),
-                           gelu_erf(acc[4 * r4 + 3]));
+  for (int r = 0; r < 16; ++r) {
+    acc0[r] = 0.f;
+    acc1[r] = 0.f;
+  }
+#pragma unroll 8
+  for (int s2 = 0; s2 < D3 / 2; ++s2) {
+    const int kk = 2 * s2 + kh;
+    const float av = Ds[m * PM_DS + kk];
+    const float b0 = W1[kk * MLP_HIDDEN], b1 = W1[kk * MLP_HIDDEN + 32];
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
+  }
+  __syncthreads();  // descriptors consumed: the block now holds the hidden layer
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+    Ds[row * PM_HS + 64 * w + m] = gelu_erf(acc0[r]);
+    Ds[row * PM_HS + 64 * w + 32 + m] = gelu_erf(acc1[r]);
   }
   __syncthreads();
-  const int o = t & 63, grp = t >> 6;
-  if (o < mout) {
-    float a2[8];
+
+  // ---- layer 2: wave w -> output block nb = w & 1, hidden half kq = w >> 1
+  const int nb = w & 1, kq = w >> 1;
+  const float *W2 = (which ? w2k : w2q) + (int64_t)h * MLP_HIDDEN * MLP_OUT + 32 * nb + m;
+  f32x16_t acc2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a2[i] = 0.f;
-    for (int c = 0; c < hidden; ++c) {
-      const float w = W2[(int64_t)c * mout + o];
-      const float4 *hv = reinterpret_cast<const float4 *>(&buf[c * RS + grp * 8]);
-      const float4 x0 = hv[0], x1 = hv[1];
-      a2[0] = fmaf(x0.x, w, a2[0]);
-      a2[1] = fmaf(x0.y, w, a2[1]);
-      a2[2] = fmaf(x0.z, w, a2[2]);
-      a2[3] = fmaf(x0.w, w, a2[3]);
-      a2[4] = fmaf(x1.x, w, a2[4]);
-      a2[5] = fmaf(x1.y, w, a2[5]);
-      a2[6] = fmaf(x1.z, w, a2[6]);
-      a2[7] = fmaf(x1.w, w, a2[7]);
-    }
-    float *yo = y + ((((int64_t)which * g.B + b) * g.H + h) * g.nt) * mout;
+  for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
+#pragma unroll 8
+  for (int s2 = 0; s2 < MLP_HIDDEN / 4; ++s2) {
+    const int kk = 128 * kq + 2 * s2 + kh;
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ds[m * PM_HS + kk], W2[kk * MLP_OUT], acc2, 0, 0, 0);
+  }
+  if (kq == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = r0 + grp * 8 + i;
-      if (r < g.nt) yo[(int64_t)r * mout + o] = a2[i];
+    for (int r = 0; r < 16; ++r) part[nb][8 * (r >> 2) + 4 * kh + (r & 3)][m] = acc2[r];
+  }
+  __syncthreads();
+  if (kq == 0) {
+    float *yo = y + (((int64_t)which * g.B + b) * g.H + h) * (int64_t)g.nt * MLP_OUT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (r0 + row < g.nt) yo[(int64_t)(r0 + row) * MLP_OUT + 32 * nb + m] = acc2[r] + part[nb][row][m];
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Tile scores S = scale * y_q y_k^T for 16 query-tile rows, then per-row outputs.
-// Each dot product uses four interleaved fp32 partial sums (lower rounding error).
+// Scores for 16 query-tile rows: S = scale * y_q y_k^T on 16x16x4 fp32 MFMA (A[m = lane%16]
+// [k = lane/16], B[k = lane/16][n = lane%16], D[m = 4*(lane/16) + r][n = lane%16]); two
+// accumulation chains (even / odd k steps) summed at the end.  Then one wave per row.
 template <int MAXM>
-__global__ void __launch_bounds__(256) score_kernel(const float *__restrict__ y, Geo g, int mout, float scale,
-                                                    float *__restrict__ scores, float *__restrict__ probs, int topk,
-                                                    int32_t *__restrict__ idx) {
+__global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict__ y, Geo g, float scale,
+                                                         float *__restrict__ scores, float *__restrict__ probs,
+                                                         int topk, int32_t *__restrict__ idx) {
+  constexpr int SW = 64 * MAXM + 1;
+  __shared__ float S[16 * SW];
   const int i0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
   const int nt = g.nt;
-  const float *yq = y + (((int64_t)b * g.H + h) * nt) * mout;
-  const float *yk = y + ((((int64_t)g.B + b) * g.H + h) * nt) * mout;
-  __shared__ __attribute__((aligned(16))) float sq[16][64];
-  __shared__ __attribute__((aligned(16))) float sk[64][68];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  for (int e = t; e < 16 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    sq[r][c] = (i0 + r < nt && c < mout) ? yq[(int64_t)(i0 + r) * mout + c] : 0.f;
-  }
-  float sc[4][MAXM];
+  const float *yq = y + (((int64_t)b * g.H + h) * nt) * MLP_OUT;
+  const float *yk = y + ((((int64_t)g.B + b) * g.H + h) * nt) * MLP_OUT;
+  const int m = lane & 15, kq = lane >> 4;
+  float qa[16];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    __syncthreads();
-    for (int e = t; e < 64 * 64; e += 256) {
-      const int r = e >> 6, c = e & 63, jj = 64 * m + r;
-      sk[r][c] = (jj < nt && c < mout) ? yk[(int64_t)jj * mout + c] : 0.f;
-    }
-    __syncthreads();
-    float acc[4][4];
+  for (int s2 = 0; s2 < 16; ++s2) qa[s2] = (i0 + m < nt) ? yq[(int64_t)(i0 + m) * MLP_OUT + 4 * s2 + kq] : 0.f;
+  const int nblk = (nt + 15) >> 4;
+  for (int kb = w; kb < nblk; kb += 4) {
+    const int key = 16 * kb + m;
+    const float *kr = yk + (int64_t)min(key, nt - 1) * MLP_OUT + kq;
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) acc[rr][p] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < 64; c += 4) {
-      const float4 kv = *reinterpret_cast<const float4 *>(&sk[lane][c]);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float4 qv = *reinterpret_cast<const float4 *>(&sq[4 * w + rr][c]);
-        acc[rr][0] = fmaf(qv.x, kv.x, acc[rr][0]);
-        acc[rr][1] = fmaf(qv.y, kv.y, acc[rr][1]);
-        acc[rr][2] = fmaf(qv.z, kv.z, acc[rr][2]);
-        acc[rr][3] = fmaf(qv.w, kv.w, acc[rr][3]);
-      }
+    for (int s2 = 0; s2 < 16; s2 += 2) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s2], kr[4 * s2], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s2 + 1], kr[4 * s2 + 4], a1, 0, 0, 0);
     }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) sc[rr][m] = ((acc[rr][0] + acc[rr][1]) + (acc[rr][2] + acc[rr][3])) * scale;
+    for (int r = 0; r < 4; ++r) S[(4 * kq + r) * SW + key] = (a0[r] + a1[r]) * scale;
   }
-#pragma unroll
+  __syncthreads();
+#pragma unroll 1
   for (int rr = 0; rr < 4; ++rr) {
-    const int i = i0 + 4 * w + rr;
-    if (i >= nt) continue;  // wave-uniform
-    const int64_t row = ((int64_t)b * g.H + h) * nt + i;
+    const int row = 4 * w + rr, i = i0 + row;
+    if (i >= nt) break;  // wave-uniform
+    const int64_t grow = ((int64_t)b * g.H + h) * nt + i;
+    float sc[MAXM];
+#pragma unroll
+    for (int mm = 0; mm < MAXM; ++mm) sc[mm] = S[row * SW + min(64 * mm + lane, 64 * MAXM - 1)];
     if (scores != nullptr) {
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        const int jj = 64 * m + lane;
-        if (jj < nt) scores[row * nt + jj] = sc[rr][m];
-      }
+      for (int mm = 0; mm < MAXM; ++mm)
+        if (64 * mm + lane < nt) scores[grow * nt + 64 * mm + lane] = sc[mm];
     }
     if (probs != nullptr) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m)
-        if (64 * m + lane < nt) mx = fmaxf(mx, sc[rr][m]);
+      for (int mm = 0; mm < MAXM; ++mm)
+        if (64 * mm + lane < nt) mx = fmaxf(mx, sc[mm]);
       mx = wave_max(mx);
       float e[MAXM], sum = 0.f;
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        e[m] = (64 * m + lane < nt) ? expf(sc[rr][m] - mx) : 0.f;
-        sum += e[m];
+      for (int mm = 0; mm < MAXM; ++mm) {
+        e[mm] = (64 * mm + lane < nt) ? expf(sc[mm] - mx) : 0.f;
+        sum += e[mm];
       }
       sum = wave_sum(sum);
       const float inv = 1.0f / sum;
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        const int jj = 64 * m + lane;
-        if (jj < nt) probs[row * nt + jj] = e[m] * inv;
-      }
+      for (int mm = 0; mm < MAXM; ++mm)
+        if (64 * mm + lane < nt) probs[grow * nt + 64 * mm + lane] = e[mm] * inv;
     }
     if (topk > 0) {
       uint32_t key[MAXM];
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) key[m] = (64 * m + lane < nt) ? float_key(sc[rr][m]) : 0u;
-      wave_topk<MAXM>(key, nt, topk, lane, idx + row * topk, nullptr);
+      for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nt) ? float_key(sc[mm]) : 0u;
+      wave_topk<MAXM>(key, nt, topk, lane, idx + grow * topk, nullptr);
     }
   }
 }
@@ -268,38 +260,33 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
 
 // ---------------------------------------------------------------------------------------
 template <int MAXM>
-static void launch_score_t(const Geo &g, const float *y, int mout, float scale, float *scores, float *probs, int topk,
+static void launch_score_t(const Geo &g, const float *y, float scale, float *scores, float *probs, int topk,
                            int32_t *idx, hipStream_t st) {
-  score_kernel<MAXM><<<dim3((g.nt + 15) / 16, g.H, g.B), 256, 0, st>>>(y, g, mout, scale, scores, probs, topk, idx);
+  score_topk_kernel<MAXM><<<dim3((g.nt + 15) / 16, g.H, g.B), 256, 0, st>>>(y, g, scale, scores, probs, topk, idx);
 }
 
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st) {
-  const size_t nt_all = (size_t)g.B * g.H * g.nt;
-  uint8_t *p = (uint8_t *)ws;
-  float *qd = q_desc ? q_desc : (float *)p;
-  p += align256(nt_all * 3 * g.d * sizeof(float));
-  float *kd = k_desc ? k_desc : (float *)p;
-  p += align256(nt_all * 3 * g.d * sizeof(float));
-  float *y = (float *)p;
-
-  const dim3 pg(g.nt, g.H, 2 * g.B);
+  (void)hidden;
+  (void)mlp_out;
+  float *y = (float *)ws;
+  const dim3 pg((g.nt + PM_ROWS - 1) / PM_ROWS, g.H, 2 * g.B);
   if (dt == VEDA_BF16)
-    pool_kernel<2><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, qd, kd, g);
+    pool_mlp_kernel<2><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
+                                           k_desc, g);
   else
-    pool_kernel<4><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, qd, kd, g);
-  mlp_kernel<<<dim3((g.nt + MLP_ROWS - 1) / MLP_ROWS, g.H, 2 * g.B), 256, 0, st>>>(qd, kd, w1q, w2q, w1k, w2k, y, g,
-                                                                                 hidden, mlp_out);
+    pool_mlp_kernel<4><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
+                                           k_desc, g);
   if (g.nt <= 64)
-    launch_score_t<1>(g, y, mlp_out, scale, scores, probs, topk, idx, st);
+    launch_score_t<1>(g, y, scale, scores, probs, topk, idx, st);
   else if (g.nt <= 256)
-    launch_score_t<4>(g, y, mlp_out, scale, scores, probs, topk, idx, st);
+    launch_score_t<4>(g, y, scale, scores, probs, topk, idx, st);
   else if (g.nt <= 640)
-    launch_score_t<10>(g, y, mlp_out, scale, scores, probs, topk, idx, st);
+    launch_score_t<10>(g, y, scale, scores, probs, topk, idx, st);
   else
-    launch_score_t<20>(g, y, mlp_out, scale, scores, probs, topk, idx, st);
+    launch_score_t<20>(g, y, scale, scores, probs, topk, idx, st);
   return hipGetLastError();
 }
 
