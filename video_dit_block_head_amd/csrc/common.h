@@ -7,6 +7,19 @@
 
 namespace veda {
 
+// Number of compute units of the current device (cached per device; host side).
+inline int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Per-head tile shapes, passed to kernels by value (1.5 KB of kernel arguments).
 struct HeadShapes {
   int32_t s[VEDA_MAX_HEADS][3];

@@ -4,9 +4,10 @@
 //  pool_mlp_kernel   32 tiles of one (head, batch, Q|K) per workgroup.  Each wave streams 8
 //                    tiles (HBM-bound: 16-byte loads, 32 per lane in flight) into their
 //                    [mean|max|min] descriptors, then the workgroup runs the MLP on fp32
-//                    MFMA (v_mfma_f32_32x32x2f32): layer 1 32x3d @ 3d x256 (64 hidden units
-//                    per wave), exact-erf GELU, layer 2 32x256 @ 256x64 (two K halves summed
-//                    in a fixed order).  Other workgroups' streaming overlaps this one's MFMA.
+//                    MFMA: layer 1 32x3d @ 3d x256 (v_mfma_f32_32x32x2f32, 64 hidden units
+//                    per wave), exact-erf GELU, layer 2 32x256 @ 256x64
+//                    (v_mfma_f32_16x16x4f32, 16 outputs per wave).  Three workgroups per
+//                    CU, so other workgroups' streaming overlaps one's MFMA work.
 //  score_topk_kernel 16 query-tile rows per workgroup: S = y_q y_k^T on fp32 MFMA
 //                    (v_mfma_f32_16x16x4f32) into an LDS row block, then one wave per row
 //                    for softmax and top-k (ballot/popcount; deterministic).
@@ -31,9 +32,19 @@ size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out) {
 
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+// ---------------------------------------------------------------------------------------
+// TripPool + MLP on 32 tiles of one (Q|K, batch, head) per workgroup (4 waves; three
+// workgroups fit a CU, so other workgroups stream while one runs its MLP).
+//   pooling: wave w pools tiles 8w .. 8w + 7, 32 16-byte loads per lane in flight;
+//   layer 1: fp32 MFMA 32x32x2 (A[m = lane%32][k = lane/32], B[k = lane/32][n = lane%32]),
+//            64 hidden units per wave, weights prefetched PF steps ahead in registers;
+//   GELU (exact erf) into the hidden block, in place of the descriptors;
+//   layer 2: fp32 MFMA 16x16x4, 16 outputs per wave for all 32 rows (no cross-wave sum).
 // EB: element bytes (2: bf16 with d = P = 128; 4: f32 with d = P = 64).  Rows are 256 bytes.
+static constexpr int PM_HST = 260;    // hidden block row stride (floats)
+
 template <int EB>
-__global__ void __launch_bounds__(256) pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3))) pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
                                                        const float *__restrict__ w1q, const float *__restrict__ w2q,
                                                        const float *__restrict__ w1k, const float *__restrict__ w2k,
                                                        float *__restrict__ y, float *__restrict__ qdesc,
@@ -42,16 +53,21 @@ __global__ void __launch_bounds__(256) pool_mlp_kernel(const uint8_t *__restrict
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
   constexpr int D3 = 3 * D;
-  const int r0 = blockIdx.x * PM_ROWS, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
+  constexpr int PF = 8;                   // weight prefetch distance (MFMA steps)
+  // Items ordered (b, h, Q|K, group); each XCD walks a contiguous range, so the workgroups
+  // that share a head's weights share that XCD's L2.
+  const int ngrp = (g.nt + PM_ROWS - 1) / PM_ROWS;
+  const int L = xcd_tile(blockIdx.x, gridDim.x);
+  const int r0 = (L % ngrp) * PM_ROWS, which = (L / ngrp) & 1, h = (L / (2 * ngrp)) % g.H,
+            b = L / (2 * ngrp * g.H);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ float Ds[PM_ROWS * PM_DS];   // descriptors, then the hidden layer
-  __shared__ float part[2][32][33];       // layer-2 partial sums of the second K half
 
-  // ---- TripPool: wave w pools tiles r0 + 8w .. r0 + 8w + 7.  Lane (rg = lane/16, c = lane%16)
-  // accumulates rows rg, rg + 4, ... of its 16-byte channel chunk c; the 4 row groups are
-  // combined as (g0 + g1) + (g2 + g3) by lane exchanges.
+  // ---- TripPool: lane (rg = lane/16, c = lane%16) accumulates rows rg, rg + 4, ... of its
+  // 16-byte channel chunk c; the 4 row groups are combined as (g0 + g1) + (g2 + g3).
   const uint8_t *src0 = (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
   const int rg = lane >> 4, c = lane & 15;
+#pragma unroll 1
   for (int tt = 0; tt < 8; ++tt) {
     const int row = 8 * w + tt, j = r0 + row;
     float s[EPC], mx[EPC], mn[EPC];
@@ -116,55 +132,75 @@ __global__ void __launch_bounds__(256) pool_mlp_kernel(const uint8_t *__restrict
     }
   }
 
-  // ---- layer 1 on fp32 MFMA: wave w owns hidden units 64w .. 64w + 63 (two 32-wide blocks).
-  // 32x32x2 operands: A[m = lane%32][k = lane/32], B[k = lane/32][n = lane%32].
-  const int m = lane & 31, kh = lane >> 5;
-  const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * MLP_HIDDEN + 64 * w + m;
-  f32x16_t acc0, acc1;
+  // ---- layer 1: hidden units 64 w .. 64 w + 63
+  {
+    const int m = lane & 31, kh = lane >> 5;
+    const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * MLP_HIDDEN + 64 * w + m;
+    f32x16_t acc0, acc1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc0[r] = 0.f;
-    acc1[r] = 0.f;
-  }
-#pragma unroll 8
-  for (int s2 = 0; s2 < D3 / 2; ++s2) {
-    const int kk = 2 * s2 + kh;
-    const float av = Ds[m * PM_DS + kk];
-    const float b0 = W1[kk * MLP_HIDDEN], b1 = W1[kk * MLP_HIDDEN + 32];
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
-  }
-  __syncthreads();  // descriptors consumed: the block now holds the hidden layer
+    for (int r = 0; r < 16; ++r) {
+      acc0[r] = 0.f;
+      acc1[r] = 0.f;
+    }
+    float wr[PF][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-    Ds[row * PM_HS + 64 * w + m] = gelu_erf(acc0[r]);
-    Ds[row * PM_HS + 64 * w + 32 + m] = gelu_erf(acc1[r]);
-  }
-  __syncthreads();
-
-  // ---- layer 2: wave w -> output block nb = w & 1, hidden half kq = w >> 1
-  const int nb = w & 1, kq = w >> 1;
-  const float *W2 = (which ? w2k : w2q) + (int64_t)h * MLP_HIDDEN * MLP_OUT + 32 * nb + m;
-  f32x16_t acc2;
+    for (int pp = 0; pp < PF; ++pp) {
+      wr[pp][0] = W1[(2 * pp + kh) * MLP_HIDDEN];
+      wr[pp][1] = W1[(2 * pp + kh) * MLP_HIDDEN + 32];
+    }
+#pragma unroll 1
+    for (int sb = 0; sb < D3 / 2; sb += PF) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
-#pragma unroll 8
-  for (int s2 = 0; s2 < MLP_HIDDEN / 4; ++s2) {
-    const int kk = 128 * kq + 2 * s2 + kh;
-    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ds[m * PM_HS + kk], W2[kk * MLP_OUT], acc2, 0, 0, 0);
-  }
-  if (kq == 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[nb][8 * (r >> 2) + 4 * kh + (r & 3)][m] = acc2[r];
-  }
-  __syncthreads();
-  if (kq == 0) {
-    float *yo = y + (((int64_t)which * g.B + b) * g.H + h) * (int64_t)g.nt * MLP_OUT;
+      for (int pp = 0; pp < PF; ++pp) {
+        const int kk = 2 * (sb + pp) + kh;
+        const float b0 = wr[pp][0], b1 = wr[pp][1];
+        // unconditional prefetch (row clamped in range): no branch, so the waits stay exact
+        const int kn = min(kk + 2 * PF, D3 - 2 + kh);
+        const float av = Ds[m * PM_DS + kk];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
+        wr[pp][0] = W1[kn * MLP_HIDDEN];
+        wr[pp][1] = W1[kn * MLP_HIDDEN + 32];
+        __builtin_amdgcn_sched_barrier(0);  // keep each step's prefetch a full ring ahead of its use
+      }
+    }
+    __syncthreads();  // descriptors consumed: the block now holds the hidden layer
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (r0 + row < g.nt) yo[(int64_t)(r0 + row) * MLP_OUT + 32 * nb + m] = acc2[r] + part[nb][row][m];
+      Ds[row * PM_HST + 64 * w + m] = gelu_erf(acc0[r]);
+      Ds[row * PM_HST + 64 * w + 32 + m] = gelu_erf(acc1[r]);
+    }
+  }
+  __syncthreads();
+
+  // ---- layer 2: outputs 16 w .. 16 w + 15, rows in two 16-row blocks, all 256 hidden units;
+  // A[m = lane%16][k = lane/16], B[k = lane/16][n = lane%16], D[m = 4*(lane/16) + r][n].
+  {
+    const int m = lane & 15, kq = lane >> 4;
+    const float *W2 = (which ? w2k : w2q) + (int64_t)h * MLP_HIDDEN * MLP_OUT + 16 * w + m;
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    float wr[PF];
+#pragma unroll
+    for (int pp = 0; pp < PF; ++pp) wr[pp] = W2[(4 * pp + kq) * MLP_OUT];
+#pragma unroll 1
+    for (int sb = 0; sb < MLP_HIDDEN / 4; sb += PF) {
+#pragma unroll
+      for (int pp = 0; pp < PF; ++pp) {
+        const int kk = 4 * (sb + pp) + kq;
+        const float bv = wr[pp];
+        a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ds[m * PM_HST + kk], bv, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ds[(16 + m) * PM_HST + kk], bv, a1, 0, 0, 0);
+        wr[pp] = W2[min(kk + 4 * PF, MLP_HIDDEN - 4 + kq) * MLP_OUT];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    float *yo = y + (((int64_t)which * g.B + b) * g.H + h) * (int64_t)g.nt * MLP_OUT + 16 * w + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row0 = r0 + 4 * kq + r, row1 = row0 + 16;
+      if (row0 < g.nt) yo[(int64_t)row0 * MLP_OUT] = a0[r];
+      if (row1 < g.nt) yo[(int64_t)row1 * MLP_OUT] = a1[r];
     }
   }
 }
@@ -179,25 +215,49 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
                                                          int topk, int32_t *__restrict__ idx) {
   constexpr int SW = 64 * MAXM + 1;
   __shared__ float S[16 * SW];
-  const int i0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
-  const int nt = g.nt;
+  const int nt = g.nt, nrb = (nt + 15) >> 4;
+  const int L = xcd_tile(blockIdx.x, gridDim.x);  // each XCD walks contiguous heads
+  const int i0 = (L % nrb) * 16, h = (L / nrb) % g.H, b = L / (nrb * g.H);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const float *yq = y + (((int64_t)b * g.H + h) * nt) * MLP_OUT;
   const float *yk = y + ((((int64_t)g.B + b) * g.H + h) * nt) * MLP_OUT;
+  // The contraction slot kq of step s carries channel 16 kq + s, so each lane's 16 operand
+  // values are one contiguous 64-byte run (four 16-byte loads).
   const int m = lane & 15, kq = lane >> 4;
-  float qa[16];
+  float4 qa[4];
+  {
+    const float4 *qr = reinterpret_cast<const float4 *>(yq + (int64_t)min(i0 + m, nt - 1) * MLP_OUT + 16 * kq);
 #pragma unroll
-  for (int s2 = 0; s2 < 16; ++s2) qa[s2] = (i0 + m < nt) ? yq[(int64_t)(i0 + m) * MLP_OUT + 4 * s2 + kq] : 0.f;
+    for (int e = 0; e < 4; ++e) qa[e] = qr[e];
+  }
   const int nblk = (nt + 15) >> 4;
-  for (int kb = w; kb < nblk; kb += 4) {
-    const int key = 16 * kb + m;
-    const float *kr = yk + (int64_t)min(key, nt - 1) * MLP_OUT + kq;
+  float4 kb_next[4];
+  int kb = w;
+  if (kb < nblk) {
+    const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)min(16 * kb + m, nt - 1) * MLP_OUT + 16 * kq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kb_next[e] = kr[e];
+  }
+#pragma unroll 1
+  for (; kb < nblk; kb += 4) {
+    float4 kv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kv[e] = kb_next[e];
+    if (kb + 4 < nblk) {
+      const float4 *kr =
+          reinterpret_cast<const float4 *>(yk + (int64_t)min(16 * (kb + 4) + m, nt - 1) * MLP_OUT + 16 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kb_next[e] = kr[e];
+    }
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s2 = 0; s2 < 16; s2 += 2) {
-      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s2], kr[4 * s2], a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s2 + 1], kr[4 * s2 + 4], a1, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].x, kv[e].x, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].y, kv[e].y, a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].z, kv[e].z, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].w, kv[e].w, a1, 0, 0, 0);
     }
+    const int key = 16 * kb + m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[(4 * kq + r) * SW + key] = (a0[r] + a1[r]) * scale;
   }
@@ -262,7 +322,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
 template <int MAXM>
 static void launch_score_t(const Geo &g, const float *y, float scale, float *scores, float *probs, int topk,
                            int32_t *idx, hipStream_t st) {
-  score_topk_kernel<MAXM><<<dim3((g.nt + 15) / 16, g.H, g.B), 256, 0, st>>>(y, g, scale, scores, probs, topk, idx);
+  score_topk_kernel<MAXM><<<dim3(((g.nt + 15) / 16) * g.H * g.B), 256, 0, st>>>(y, g, scale, scores, probs, topk,
+                                                                                 idx);
 }
 
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
@@ -272,7 +333,7 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
-  const dim3 pg((g.nt + PM_ROWS - 1) / PM_ROWS, g.H, 2 * g.B);
+  const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
   if (dt == VEDA_BF16)
     pool_mlp_kernel<2><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
                                            k_desc, g);
