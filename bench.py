@@ -51,10 +51,11 @@ def traffic_from_counters(launch_bytes_unit="GB"):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, wl, kk, n_sel):
+def cpu_baseline(cfg, wl, kk, n_sel, budget_s=15.0):
     """Time the CPU oracle (as it stands) on a bounded sample of one step and scale each
-    stage to the full step: 2 heads; all tiles for gather / scoring / scatter; 32 query
-    tiles per head for attention; 4 query tiles per head for the tile map."""
+    stage to the full step.  Per sampled head: gather / scoring / scatter of all tiles,
+    attention for 64 query tiles, the tile map for 4 query tiles.  Heads are taken in
+    order until about `budget_s` seconds of CPU work have been measured."""
     import numpy as np
     import oracle.veda_oracle as O
     try:
@@ -62,13 +63,13 @@ def cpu_baseline(cfg, wl, kk, n_sel):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = None
-    heads = [0, cfg.heads // 2]
     P, nt, H = cfg.tile, cfg.n_tiles, cfg.heads
-    n_att, n_map = 32, 4
+    n_att, n_map = min(64, nt), min(4, n_sel)
     T = time.perf_counter
     acc = dict(gather=0.0, score=0.0, attn=0.0, scatter=0.0, tilemap=0.0)
     t_all = T()
-    for h in heads:
+    done = 0
+    for h in range(H):   # consecutive heads cycle through the tile shapes
         t = T()
         perm = O.tile_permutation(cfg.grid, wl.shapes[h])
         qt, kt, vt = (O.to_tiles(wl.head(w, 0, h), perm) for w in ("q", "k", "v"))
@@ -88,8 +89,11 @@ def cpu_baseline(cfg, wl, kk, n_sel):
         O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=wl.sample_tiles(h)[:n_map])
         acc["tilemap"] += T() - t
         del out
+        done += 1
+        if T() - t_all >= budget_s:
+            break
     wall = T() - t_all
-    nh = len(heads)
+    nh = done
     scale = dict(gather=H / nh, score=H / nh, attn=H * nt / (nh * n_att), scatter=H / nh,
                  tilemap=H * n_sel / (nh * n_map))
     step_s = sum(acc[s] * scale[s] for s in acc)
@@ -100,6 +104,7 @@ def cpu_baseline(cfg, wl, kk, n_sel):
                    f"attention for {n_att} query tiles per head, tile map for {n_map} query tiles per head; "
                    f"{wall:.1f} s measured, each stage scaled to the full step"),
         "sample_seconds": round(wall, 2), "extrapolated_step_s": round(step_s, 1),
+        "stage_seconds_measured": {s: round(x, 2) for s, x in acc.items()},
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 

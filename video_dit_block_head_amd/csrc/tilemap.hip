@@ -2,7 +2,7 @@
 // (query tile x key tile) region.  [Technical Summary: Veda, §2.1 "Target Construction";
 // §2.3: ground-truth heatmaps in two passes, on subsets of query tiles]
 //
-// bf16 path: one workgroup (4 waves x 32 queries) per selected query tile.
+// bf16 path: one workgroup (4 waves x 64 queries) per two selected query tiles of a head.
 //  pass 1 (one sweep over all N keys): S^T = K Q^T per key tile (MFMA, same blocking as the
 //          attention kernel; K tiles double-buffered in LDS through direct-to-LDS copies);
 //          per query row the running log-sum-exp (log2 domain, lazy max) and the row max of
@@ -24,28 +24,43 @@ size_t tilemap_workspace_bytes(const Geo &g, int n_sel) {
   return (size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float);
 }
 
+// Two selected query tiles (of one head) per workgroup: they sweep the same K tiles, so wave
+// w takes 64 queries of query tile w/2 as two 32-query blocks that share every K operand
+// read (half the LDS traffic per MFMA) and every K tile is copied once for both tiles.
+static constexpr int TM_QT = 2;
+
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
                     const int32_t *__restrict__ q_tiles, int n_sel, float *__restrict__ out,
                     float *__restrict__ lse_out, float *__restrict__ rowmax, Geo g) {
+  const int ngrp = (n_sel + TM_QT - 1) / TM_QT;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
-  const int a = L % n_sel;
-  const int64_t bh = L / n_sel;
+  const int a0 = (L % ngrp) * TM_QT;
+  const int64_t bh = L / ngrp;
   const int t = threadIdx.x, lane = t & 63, lr = lane & 31, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qt = w >> 1;                     // which of the workgroup's query tiles
+  const int a = min(a0 + qt, n_sel - 1);     // an odd tail repeats the last tile (not written twice)
+  const bool owner = a0 + qt < n_sel;
   const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) : a;  // clamped
   const __bf16 *qh = q + bh * (int64_t)g.N * 128;
   const char *kh = reinterpret_cast<const char *>(k + bh * (int64_t)g.N * 128);
   float *rm = rowmax + (bh * n_sel + a) * (int64_t)g.nt * 128;   // [j][128 queries]
 
   __shared__ uint4 Kb[2][128 * 16];
-  __shared__ float lse_s[128];
+  __shared__ float lse_s[TM_QT][128];
 
-  const int qrow = i * 128 + 32 * w + lr;
-  bf16x8_t qf[8];
+  bf16x8_t qf[2][8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qh + (int64_t)qrow * 128 + 16 * s + 8 * hi);
-  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t qrow = (int64_t)i * 128 + 64 * (w & 1) + 32 * qb + lr;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8_t *>(qh + qrow * 128 + 16 * s + 8 * hi);
+  }
+  asm volatile("" ::"v"(qf[0][0]), "v"(qf[0][1]), "v"(qf[0][2]), "v"(qf[0][3]), "v"(qf[0][4]), "v"(qf[0][5]),
+               "v"(qf[0][6]), "v"(qf[0][7]));
+  asm volatile("" ::"v"(qf[1][0]), "v"(qf[1][1]), "v"(qf[1][2]), "v"(qf[1][3]), "v"(qf[1][4]), "v"(qf[1][5]),
+               "v"(qf[1][6]), "v"(qf[1][7]));
 
   uint32_t off[8];
   tile_dma_offsets(w, lane, off);
@@ -53,7 +68,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   tile_to_lds(kh, kb_lds[0], w, off);
   if (g.nt > 1) tile_to_lds(kh + 32768, kb_lds[1], w, off);
 
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
   for (int j = 0; j < g.nt; ++j) {
     const int buf = j & 1;
     if (j + 1 < g.nt)
@@ -61,60 +76,73 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     else
       wait_vmem<0>();
     barrier();
-    f32x16_t acc[4];
+    f32x16_t acc[2][4];
     const uint4 *Ks = Kb[buf];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        acc[0][kb][r] = 0.f;
+        acc[1][kb][r] = 0.f;
+      }
       const int row = 32 * kb + lr;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (row & 15))]);
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[s], acc[kb], 0, 0, 0);
+        acc[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[0][s], acc[0][kb], 0, 0, 0);
+        acc[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[1][s], acc[1][kb], 0, 0, 0);
       }
     }
     wait_lds();
     barrier();  // every wave has read this buffer
     if (j + 2 < g.nt) tile_to_lds(kh + (int64_t)(j + 2) * 32768, kb_lds[buf], w, off);
 
-    float mx = -1e30f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -1e30f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    if (hi == 0) rm[(int64_t)j * 128 + 32 * w + lr] = mx;
-    if (__ballot(mx > m_run + TM_SLACK)) {
-      const float m_new = fmaxf(m_run, mx);
-      l_run *= __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[qb][kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      if (hi == 0 && owner) rm[(int64_t)j * 128 + 64 * (w & 1) + 32 * qb + lr] = mx;
+      if (__ballot(mx > m_run[qb] + TM_SLACK)) {
+        const float m_new = fmaxf(m_run[qb], mx);
+        l_run[qb] *= __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+      }
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[qb][kb][r], c2, -m_run[qb]));
+      l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[kb][r], c2, -m_run));
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   }
-  const float lse2 = m_run + log2f(l_run + __shfl_xor(l_run, 32));
-  if (hi == 0) {
-    lse_s[32 * w + lr] = lse2;
-    if (lse_out != nullptr) lse_out[(bh * n_sel + a) * 128 + 32 * w + lr] = lse2 * TM_LN2;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lse2 = m_run[qb] + log2f(l_run[qb] + __shfl_xor(l_run[qb], 32));
+    const int qi = 64 * (w & 1) + 32 * qb + lr;
+    if (hi == 0) {
+      lse_s[qt][qi] = lse2;
+      if (lse_out != nullptr && owner) lse_out[(bh * n_sel + a) * 128 + qi] = lse2 * TM_LN2;
+    }
   }
   __syncthreads();  // row maxima (global) and lse_s (LDS) visible to the workgroup
 
-  float *dst = out + (bh * n_sel + a) * (int64_t)g.nt;
-  for (int j = t; j < g.nt; j += 256) {
-    const float4 *src = reinterpret_cast<const float4 *>(rm + (int64_t)j * 128);
+  // pass 2: M[j] = exp2(max over the tile's queries of rowmax - lse)
+  for (int e = t; e < TM_QT * g.nt; e += 256) {
+    const int qq = e / g.nt, j = e % g.nt;
+    if (a0 + qq >= n_sel) continue;
+    const float4 *src = reinterpret_cast<const float4 *>(rowmax + ((bh * n_sel + a0 + qq) * (int64_t)g.nt + j) * 128);
     float x = -INFINITY;
 #pragma unroll 8
     for (int c = 0; c < 32; ++c) {
       const float4 v = src[c];
-      x = fmaxf(x, fmaxf(fmaxf(v.x - lse_s[4 * c], v.y - lse_s[4 * c + 1]),
-                         fmaxf(v.z - lse_s[4 * c + 2], v.w - lse_s[4 * c + 3])));
+      x = fmaxf(x, fmaxf(fmaxf(v.x - lse_s[qq][4 * c], v.y - lse_s[qq][4 * c + 1]),
+                         fmaxf(v.z - lse_s[qq][4 * c + 2], v.w - lse_s[qq][4 * c + 3])));
     }
-    dst[j] = __builtin_amdgcn_exp2f(x);
+    out[(bh * n_sel + a0 + qq) * (int64_t)g.nt + j] = __builtin_amdgcn_exp2f(x);
   }
 }
 
@@ -166,9 +194,8 @@ __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
                           const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st) {
   if (dt == VEDA_BF16)
-    tilemap_bf16_kernel<<<dim3(n_sel * g.H * g.B), 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
-                                                                 scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse,
-                                                                 (float *)ws, g);
+    tilemap_bf16_kernel<<<dim3(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B), 256, 0, st>>>(
+        (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g);
   else
     tilemap_f32_kernel<<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale, q_tiles,
                                                              n_sel, tilemap, lse, g);
