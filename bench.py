@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn ms/call + effective TFLOPS (kept FLOPs) at 90% sparsity, N≈77k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-COUNTERS = os.path.join(ROOT, "profiles", "counters_attn_bf16_large.json")
+COUNTERS = os.path.join(ROOT, "profiles", "counters_attn_bf16_large.txt")
 ATTN_SRC = os.path.join(ROOT, "video_dit_block_head_amd", "csrc", "attn.hip")
 
 
