@@ -57,6 +57,13 @@ __host__ __device__ __forceinline__ int cols_key(int p) {
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key); -0 maps like +0.
+// 16-byte load marked non-temporal: read-once streams do not displace reused data in L2.
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t float_key(float x) {
   uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -79,17 +86,38 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ?
 // Top-k of one row held by a wave: lane `lane` holds columns j = 64*m + lane, m < MAXM,
 // as order-preserving keys (0 for columns >= n_cols).  Writes the indices of the k largest
 // keys, ties to the lower index, ascending, to idx[0..k); optional 0/1 mask[0..n_cols).
-// The k-th largest key is found bit by bit (largest T with count(key >= T) >= k).
+// The k-th largest key is found bit by bit (largest T with count(key >= T) >= k), starting
+// below the bits that every valid key of the row shares, and stopping as soon as exactly k
+// keys are >= the candidate (that set is then the answer, whatever lies below).
 template <int MAXM>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_cols, int k, int lane,
                                           int32_t *__restrict__ idx, uint8_t *__restrict__ mask) {
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    int cnt = 0;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
-    if (cnt >= k) T = cand;
+  for (int m = 0; m < MAXM; ++m) {
+    kmax = max(kmax, key[m]);
+    if (64 * m + lane < n_cols) kmin = min(kmin, key[m]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+  }
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  const uint32_t diff = kmax ^ kmin;
+  uint32_t T = kmax;  // every valid key equal: T is the k-th largest already
+  if (diff != 0u) {
+    const int b0 = 31 - __builtin_clz(diff);
+    T = b0 == 31 ? 0u : (kmax & ~((2u << b0) - 1u));
+    for (int b = b0; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
+      if (cnt >= k) T = cand;
+      if (cnt == k) break;
+    }
   }
   int n_gt = 0;
 #pragma unroll

@@ -2,7 +2,8 @@
 // softmax / top-k.  [Technical Summary: Veda, §2.1 Distilled Tile Scoring]
 //
 //  pool_mlp_kernel   32 tiles of one (head, batch, Q|K) per workgroup.  Each wave streams 8
-//                    tiles (HBM-bound: 16-byte loads, 32 per lane in flight) into their
+//                    tiles (HBM-bound: non-temporal 16-byte loads, 32 per lane in flight, so
+//                    the stream does not evict the MLP weights from L2) into their
 //                    [mean|max|min] descriptors, then the workgroup runs the MLP on fp32
 //                    MFMA: layer 1 32x3d @ 3d x256 (v_mfma_f32_32x32x2f32, 64 hidden units
 //                    per wave), exact-erf GELU, layer 2 32x256 @ 256x64
@@ -81,7 +82,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
       const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
       uint4 v[P / 4];
 #pragma unroll
-      for (int i = 0; i < P / 4; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + (rg + 4 * i) * 256);
+      for (int i = 0; i < P / 4; ++i) v[i] = load_stream16(src + (rg + 4 * i) * 256);
 #pragma unroll
       for (int i = 0; i < P / 4; ++i) {
         float x[EPC];
@@ -231,35 +232,43 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
     for (int e = 0; e < 4; ++e) qa[e] = qr[e];
   }
   const int nblk = (nt + 15) >> 4;
-  float4 kb_next[4];
-  int kb = w;
-  if (kb < nblk) {
+  // Key blocks w, w + 4, w + 8, ... of this wave, loaded SD blocks ahead (a ring of SD
+  // register buffers indexed by constants: the loop is unrolled SD times).
+  constexpr int SD = 3;
+  float4 kv[SD][4];
+#pragma unroll
+  for (int u = 0; u < SD; ++u) {
+    const int kb = w + 4 * u;
     const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)min(16 * kb + m, nt - 1) * MLP_OUT + 16 * kq);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) kb_next[e] = kr[e];
+    for (int e = 0; e < 4; ++e) kv[u][e] = kr[e];   // clamped rows: always in bounds
   }
 #pragma unroll 1
-  for (; kb < nblk; kb += 4) {
-    float4 kv[4];
+  for (int kb0 = w; kb0 < nblk; kb0 += 4 * SD) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) kv[e] = kb_next[e];
-    if (kb + 4 < nblk) {
-      const float4 *kr =
-          reinterpret_cast<const float4 *>(yk + (int64_t)min(16 * (kb + 4) + m, nt - 1) * MLP_OUT + 16 * kq);
+    for (int u = 0; u < SD; ++u) {
+      const int kb = kb0 + 4 * u;
+      if (kb < nblk) {  // wave-uniform
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kb_next[e] = kr[e];
+        for (int e = 0; e < 4; ++e) {
+          a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].x, kv[u][e].x, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].y, kv[u][e].y, a1, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].z, kv[u][e].z, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].w, kv[u][e].w, a1, 0, 0, 0);
+        }
+        const int key = 16 * kb + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[(4 * kq + r) * SW + key] = (a0[r] + a1[r]) * scale;
+        const int kn = kb + 4 * SD;
+        if (kn < nblk) {
+          const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)(16 * kn + m < nt ? 16 * kn + m : nt - 1) *
+                                                                       MLP_OUT + 16 * kq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[u][e] = kr[e];
+        }
+      }
     }
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].x, kv[e].x, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].y, kv[e].y, a1, 0, 0, 0);
-      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].z, kv[e].z, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e].w, kv[e].w, a1, 0, 0, 0);
-    }
-    const int key = 16 * kb + m;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[(4 * kq + r) * SW + key] = (a0[r] + a1[r]) * scale;
   }
   __syncthreads();
 #pragma unroll 1
