@@ -159,6 +159,19 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
                                 float *tilemap, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Per-head squared output error, the objective of the tiling search.  [Technical Summary
+ * §2.2 Head-Aware Tiling, "Offline Selection": each head's tiling is picked on calibration
+ * data by the error between the full-attention and the sparse-attention output]
+ *   a, b: raster [B, N, H, d] contiguous tensors of `dtype` (d = head_dim; d * element
+ *         size a multiple of 16 bytes), e.g. a sparse output and the dense output
+ *   err:    out [B, H] f32, err[b, h] = sum over tokens n and channels c of (a - b)^2
+ *   ref_sq: out [B, H] f32, sum of b^2 (for relative errors), nullable
+ * fp32 accumulation in a fixed order (deterministic).  The shapes only need N >= 1;
+ * veda_geom is not used because the error does not depend on the tiling. */
+veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim,
+                               veda_dtype dtype, const void *a, const void *b, float *err,
+                               float *ref_sq, hipStream_t stream);
+
 const char *veda_status_str(veda_status s);
 int veda_last_hip_error(void);
 /* Library version string. */

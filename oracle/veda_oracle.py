@@ -194,6 +194,49 @@ def recall(idx_est, idx_ref):
 
 
 # ---------------------------------------------------------------------------
+# Head-aware tiling search  [Veda Technical Summary, §2.2 Head-Aware Tiling: each head's
+# (p_t, p_h, p_w) is selected offline on calibration data by the error between the
+# full-attention output and the sparse-attention output]
+# ---------------------------------------------------------------------------
+def head_output_error(o_sparse, o_full):
+    """Squared Frobenius error of one head's output (raster order, [N, d])."""
+    dlt = np.asarray(o_sparse, np.float64) - np.asarray(o_full, np.float64)
+    return float((dlt * dlt).sum())
+
+
+def search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """For every candidate tiling, every head runs the scored sparse attention of one layer
+    (tiling -> TripPool -> MLP -> scores -> top-k -> tile-skipping attention -> un-tiling)
+    and its output is compared with full attention.
+
+    q, k, v: raster [B, N, H, d]; w1 [H, 3d, hidden], w2 [H, hidden, out].
+    Returns (choice [H]: index of the candidate with the least error summed over the batch,
+    ties to the lower index; err [C, B, H]; ref [B, H] = squared norm of the full output).
+    Pinned: a head whose attention is block-local on one candidate's tiles, with an
+    estimator that keeps exactly those tiles, selects that candidate with zero error;
+    with every tile kept, all errors vanish."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, N, H, _ = q.shape
+    err = np.zeros((len(candidates), B, H))
+    ref = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            full = dense_attention(q[b, :, h], k[b, :, h], v[b, :, h], scale)
+            ref[b, h] = float((full * full).sum())
+            for ci, shape in enumerate(candidates):
+                perm = tile_permutation(grid, shape)
+                qt, kt, vt = (to_tiles(x[b, :, h], perm) for x in (q, k, v))
+                yq = mlp(trippool(qt, P), w1[h], w2[h])
+                yk = mlp(trippool(kt, P), w1[h], w2[h])
+                idx = topk_rows(tile_scores(yq, yk, score_scale).astype(np.float32), topk)
+                o = from_tiles(sparse_attention(qt, kt, vt, idx, P, scale), perm)
+                err[ci, b, h] = head_output_error(o, full)
+    total = err.sum(axis=1)
+    choice = np.array([int(np.argmin(total[:, h])) for h in range(H)])
+    return choice, err, ref
+
+
+# ---------------------------------------------------------------------------
 # Index agreement under near-ties
 # ---------------------------------------------------------------------------
 def topk_agrees(score_row, idx_row, k, gap=1e-5):

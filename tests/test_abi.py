@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 11, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -135,3 +135,13 @@ def test_binding_fails_loudly_without_gpu_tensors():
     g = geom()
     with pytest.raises(V.VedaError):
         V.veda_topk_mask(torch.zeros(4, 10), 3, torch.zeros(4, 3, dtype=torch.int32))
+
+
+def test_head_error_validation(L):
+    f = L.veda_head_sq_error
+    assert f(1, 16, 2, 128, 7, A, B_, A, None, None) == DTYPE
+    assert f(0, 16, 2, 128, V.BF16, A, B_, A, None, None) == SHAPE
+    assert f(1, 16, 2, 12, V.BF16, A, B_, A, None, None) == SHAPE     # 24-byte rows
+    assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, None) == ALIGN

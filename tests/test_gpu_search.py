@@ -1,0 +1,92 @@
+"""GPU parity of the head-aware tiling search (per-head output error through the C ABI,
+candidate selection) against the CPU oracle's search.
+
+Tolerances: per-head squared errors within 1e-5 relative of an fp64 sum of the same
+numbers; search errors (relative to the full output) within 2 % + 2e-5 of the oracle's,
+since the library's outputs are bf16; the chosen tiling must match wherever the oracle's
+best two candidates differ by more than 5 %."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.veda_oracle as O
+from workloads import bf16_bits_to_f32, get, make
+from workloads.synth import block_local_case
+
+pytestmark = pytest.mark.gpu
+
+V = pytest.importorskip("video_dit_block_head_amd")
+from video_dit_block_head_amd.pipeline import search_tile_shapes  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_head_sq_error_exact_sum(dtype):
+    say(f"[gpu-search] head error {dtype}")
+    g = torch.Generator().manual_seed(3)
+    B, N, H, d = 2, 777, 5, 128 if dtype == torch.bfloat16 else 64
+    a = torch.randn(B, N, H, d, generator=g).to(dtype)
+    b = torch.randn(B, N, H, d, generator=g).to(dtype)
+    err = torch.empty(B, H, device="cuda")
+    ref = torch.empty(B, H, device="cuda")
+    V.veda_head_sq_error(a.cuda(), b.cuda(), err, ref)
+    torch.cuda.synchronize()
+    a64, b64 = a.double().numpy(), b.double().numpy()
+    want = ((a64 - b64) ** 2).sum(axis=(1, 3))
+    want_ref = (b64 ** 2).sum(axis=(1, 3))
+    assert np.allclose(err.cpu().numpy(), want, rtol=1e-5, atol=0)
+    assert np.allclose(ref.cpu().numpy(), want_ref, rtol=1e-5, atol=0)
+    # deterministic
+    err2 = torch.empty_like(err)
+    V.veda_head_sq_error(a.cuda(), b.cuda(), err2)
+    assert torch.equal(err, err2)
+
+
+def test_search_block_local_case():
+    say("[gpu-search] block-local construction")
+    grid, P, d = (4, 8, 16), 128, 128
+    cands = [(4, 4, 8), (1, 8, 16), (2, 8, 8)]
+    q, k, v, w1, w2 = block_local_case(grid, cands[1], d, heads=3, batch=1)
+    to_dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16).contiguous()
+    choice, err, ref = search_tile_shapes(grid, P, cands, to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(w1),
+                                          torch.from_numpy(w2), 1)
+    rel = (err[:, 0, :] / ref[0][None, :]).cpu().numpy()
+    assert choice == [1, 1, 1]
+    assert np.all(rel[1] < 1e-4), rel
+    assert np.all(rel[0] > 1e-2) and np.all(rel[2] > 1e-2), rel
+
+
+HEADS = [0, 4, 8, 11]  # heads the oracle recomputes (every head tries every candidate)
+
+
+def test_search_small_workload_vs_oracle():
+    cfg = get("small")
+    say(f"[gpu-search] {cfg.name}: generating")
+    wl = make(cfg)
+    cands = sorted(set(wl.shapes), key=wl.shapes.index)
+    kk = cfg.topk[0]
+    up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    say(f"[gpu-search] {cfg.name}: GPU search over {cands}")
+    choice, err, ref = search_tile_shapes(cfg.grid, cfg.tile, cands, up(wl.q), up(wl.k), up(wl.v),
+                                          torch.from_numpy(wl.w1), torch.from_numpy(wl.w2), kk,
+                                          score_scale=cfg.score_scale)
+    rel_g = (err[:, 0, :] / ref[0][None, :]).cpu().numpy()
+    say(f"[gpu-search] {cfg.name}: oracle search on heads {HEADS}")
+    raster = lambda a: bf16_bits_to_f32(a[:, HEADS]).transpose(0, 2, 1, 3)
+    ch_o, err_o, ref_o = O.search_tile_shapes(raster(wl.q), raster(wl.k), raster(wl.v), cfg.grid, cfg.tile, cands,
+                                              wl.w1[HEADS], wl.w2[HEADS], kk, cfg.score_scale,
+                                              1 / math.sqrt(cfg.head_dim))
+    rel_o = err_o[:, 0, :] / ref_o[0][None, :]
+    rel_g = rel_g[:, HEADS]
+    say(f"[gpu-search] relative errors, oracle: {rel_o.round(5).tolist()}")
+    say(f"[gpu-search] relative errors, GPU:    {rel_g.round(5).tolist()}")
+    assert np.all(np.abs(rel_g - rel_o) <= 0.02 * rel_o + 2e-5), np.abs(rel_g - rel_o).max()
+    for a, h in enumerate(HEADS):
+        srt = np.sort(rel_o[:, a])
+        if srt[1] - srt[0] > 0.05 * srt[0] + 1e-4:  # resolvable above the bf16 output noise
+            assert choice[h] == ch_o[a], (h, choice[h], ch_o[a], rel_o[:, a], rel_g[:, a])

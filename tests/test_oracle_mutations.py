@@ -151,6 +151,32 @@ def tilemap_unnormalised(qt, kt, P, scale, q_tiles=None):
     return np.array(out)
 
 
+def search_argmax(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """Picks the worst candidate."""
+    choice, err, ref = O.search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale)
+    return err.sum(axis=1).argmax(axis=0), err, ref
+
+
+def search_no_untiling(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """Compares the tile-major output with the raster-order full output."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, N, H, _ = q.shape
+    err = np.zeros((len(candidates), B, H))
+    ref = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            full = O.dense_attention(q[b, :, h], k[b, :, h], v[b, :, h], scale)
+            ref[b, h] = (full ** 2).sum()
+            for ci, shape in enumerate(candidates):
+                perm = O.tile_permutation(grid, shape)
+                qt, kt, vt = (O.to_tiles(x[b, :, h], perm) for x in (q, k, v))
+                yq = O.mlp(O.trippool(qt, P), w1[h], w2[h])
+                yk = O.mlp(O.trippool(kt, P), w1[h], w2[h])
+                idx = O.topk_rows(O.tile_scores(yq, yk, score_scale).astype(np.float32), topk)
+                err[ci, b, h] = O.head_output_error(O.sparse_attention(qt, kt, vt, idx, P, scale), full)
+    return err.sum(axis=1).argmin(axis=0), err, ref
+
+
 MUTANTS = [
     ("perm: in-tile axes swapped", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_swapped_inner]),
     ("perm: tile order reversed", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_tile_order_colmajor]),
@@ -173,6 +199,8 @@ MUTANTS = [
     ("sparse: wrong kept tile", [pins.pin_sparse_vs_masked_matrix], [sparse_wrong_tile]),
     ("tilemap: mean pooling", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_mean]),
     ("tilemap: not normalised", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_unnormalised]),
+    ("search: argmax", [pins.pin_search_block_local], [search_argmax]),
+    ("search: output left tile-major", [pins.pin_search_block_local, pins.pin_search_all_kept], [search_no_untiling]),
 ]
 
 

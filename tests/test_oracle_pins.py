@@ -372,3 +372,47 @@ def test_tilemap_zero_q_and_bounds():
     q = rng.standard_normal((P * n_t, d)) * 3
     m = O.tilemap(q, k, P, 0.25)
     assert np.all(m <= 1.0 + 1e-15) and np.all(m.max(axis=1) >= 1.0 / (P * n_t))
+
+
+# ------------------------------------------------------------------ tiling search
+SEARCH_GRID, SEARCH_P, SEARCH_D = (4, 8, 8), 64, 64
+SEARCH_CANDIDATES = [(4, 4, 4), (1, 8, 8), (2, 4, 8)]
+
+
+def pin_search_block_local(search_tile_shapes):
+    """Attention confined to the (1, 8, 8) tiles and an estimator that keeps each query
+    tile's own tile (top-1): that candidate reproduces full attention up to e^-50 weights,
+    the others miss most of each query's keys."""
+    from workloads.synth import block_local_case
+    q, k, v, w1, w2 = block_local_case(SEARCH_GRID, SEARCH_CANDIDATES[1], SEARCH_D, heads=2, batch=1)
+    choice, err, ref = search_tile_shapes(q, k, v, SEARCH_GRID, SEARCH_P, SEARCH_CANDIDATES, w1, w2, 1, 0.125,
+                                          1 / math.sqrt(SEARCH_D))
+    assert list(choice) == [1, 1]
+    rel = err[:, 0, :] / ref[0][None, :]
+    assert np.all(rel[1] < 1e-15)
+    assert np.all(rel[0] > 1e-2) and np.all(rel[2] > 1e-2)
+
+
+def pin_search_all_kept(search_tile_shapes):
+    """With every tile kept, the sparse output is full attention for every candidate."""
+    rng = np.random.default_rng(13)
+    N, H, d = 4 * 8 * 8, 1, SEARCH_D
+    q, k, v = (rng.standard_normal((1, N, H, d)) for _ in range(3))
+    w1 = rng.standard_normal((H, 3 * d, 256)) / np.sqrt(3 * d)
+    w2 = rng.standard_normal((H, 256, 64)) / 16
+    _, err, ref = search_tile_shapes(q, k, v, SEARCH_GRID, SEARCH_P, SEARCH_CANDIDATES, w1, w2, 4, 0.125, 0.125)
+    assert np.all(err / ref[None] < 1e-24)
+
+
+def test_search_block_local():
+    pin_search_block_local(O.search_tile_shapes)
+
+
+def test_search_all_kept():
+    pin_search_all_kept(O.search_tile_shapes)
+
+
+def test_head_output_error_closed_form():
+    a = np.arange(12.0).reshape(3, 4)
+    assert O.head_output_error(a, a) == 0.0
+    assert O.head_output_error(a + 0.5, a) == 12 * 0.25

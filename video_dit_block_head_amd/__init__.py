@@ -75,6 +75,7 @@ def lib():
             "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]),
             "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
+            "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
             "veda_status_str": (ctypes.c_char_p, [i32]),
             "veda_last_hip_error": (ctypes.c_int, []),
             "veda_version": (ctypes.c_char_p, []),
@@ -178,3 +179,13 @@ def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, t
         geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), float(softmax_scale),
         _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
         ws_bytes, _stream(stream)))
+
+
+def veda_head_sq_error(a, b, err, ref_sq=None, stream=None):
+    """a, b: contiguous raster [B, N, H, d] tensors of one dtype; err (and ref_sq): [B, H]
+    float32, written with sum (a - b)^2 (and sum b^2) per (batch, head)."""
+    if a.shape != b.shape or a.dtype != b.dtype or a.dim() != 4:
+        raise VedaError("a and b must be [B, N, H, d] tensors of one shape and dtype")
+    B, N, H, d = (int(x) for x in a.shape)
+    _check("veda_head_sq_error", lib().veda_head_sq_error(
+        B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), _p(err, "err"), _p(ref_sq, "ref_sq"), _stream(stream)))

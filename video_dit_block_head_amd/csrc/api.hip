@@ -165,6 +165,20 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void
       launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, workspace, stream));
 }
 
+veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim, veda_dtype dtype,
+                               const void *a, const void *b, float *err, float *ref_sq, hipStream_t stream) {
+  if (dtype != VEDA_F32 && dtype != VEDA_BF16) return VEDA_ERR_DTYPE;
+  if (batch < 1 || n_tokens < 1 || heads < 1 || head_dim < 1 || batch > 65535 || heads > 65535)
+    return VEDA_ERR_SHAPE;
+  const int eb = dtype == VEDA_BF16 ? 2 : 4;
+  if (((int64_t)head_dim * eb) % 16 != 0) return VEDA_ERR_SHAPE;
+  if (!a || !b || !err) return VEDA_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(err) & 3u) ||
+      (reinterpret_cast<uintptr_t>(ref_sq) & 3u))
+    return VEDA_ERR_ALIGN;
+  return hip_status(launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, ref_sq, stream));
+}
+
 const char *veda_status_str(veda_status s) {
   switch (s) {
     case VEDA_OK: return "ok";

@@ -25,4 +25,7 @@ size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
                           const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st);
 
+hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,
+                                const void *b, float *err, float *ref_sq, hipStream_t st);
+
 }  // namespace veda

@@ -8,8 +8,8 @@ import math
 
 import torch
 
-from . import (COLS, ROWS, Geom, veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes, veda_sparse_attn_fwd,
-               veda_tile_gather, veda_trippool_score, veda_trippool_workspace_bytes)
+from . import (COLS, ROWS, Geom, veda_head_sq_error, veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes,
+               veda_sparse_attn_fwd, veda_tile_gather, veda_trippool_score, veda_trippool_workspace_bytes)
 
 
 class SparseAttention:
@@ -84,3 +84,38 @@ def dense_index(geom: Geom, device="cuda"):
     g = geom
     return (torch.arange(g.n_tiles, dtype=torch.int32, device=device)
             .expand(g.batch, g.heads, g.n_tiles, g.n_tiles).contiguous())
+
+
+def search_tile_shapes(grid, tile, candidates, q, k, v, w1, w2, topk, score_scale=0.125, softmax_scale=None,
+                       device="cuda"):
+    """Head-aware tiling search on calibration inputs: every candidate tiling runs the
+    scored sparse attention of the layer for all heads, and each head keeps the candidate
+    whose output is closest to full attention (squared error summed over the batch; ties
+    to the earlier candidate).
+
+    q, k, v: raster [B, N, H, d] GPU tensors; candidates: list of (p_t, p_h, p_w).
+    Returns (choice: list of candidate indices per head, err [C, B, H] and ref [B, H] as
+    float32 GPU tensors, ref being the squared norm of the full output).  The outputs,
+    errors and norms come from the library's kernels; only the argmin is taken here."""
+    B, N, H, d = (int(x) for x in q.shape)
+    dt = q.dtype
+    if not candidates:
+        raise ValueError("no candidate tilings")
+    err = torch.empty((len(candidates), B, H), dtype=torch.float32, device=device)
+    ref = torch.empty((B, H), dtype=torch.float32, device=device)
+    full = torch.empty_like(q)
+    # full attention: every key tile kept (the un-tiled output does not depend on the tiling)
+    sa = SparseAttention(Geom(B, H, d, grid, tile, [candidates[0]] * H), dt, w1, w2, score_scale=score_scale,
+                         softmax_scale=softmax_scale, device=device)
+    sa.gather(q, k, v)
+    sa.attend(dense_index(sa.geom, device))
+    sa.scatter(full)
+    out = torch.empty_like(q)
+    for ci, shape in enumerate(candidates):
+        sa = SparseAttention(Geom(B, H, d, grid, tile, [tuple(shape)] * H), dt, w1, w2, score_scale=score_scale,
+                             softmax_scale=softmax_scale, device=device)
+        sa.forward(q, k, v, topk, out)
+        veda_head_sq_error(out, full, err[ci], ref if ci == 0 else None)
+    total = err.sum(dim=1).cpu()
+    choice = [int(torch.argmin(total[:, h]).item()) for h in range(H)]
+    return choice, err, ref
