@@ -159,6 +159,30 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
                                 float *tilemap, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
+ * gradients of every Q and K tile, per-row KL terms). */
+size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel);
+
+/* One distillation step of the per-head tile-score estimator.  [Technical Summary §2.1
+ * "Optimization": a row-wise KL divergence between the full-attention reference and the
+ * predicted tile-score distribution; stop-gradient on the features feeding the estimator]
+ * With one MLP per head shared by the Q-tile and K-tile descriptors (w1 [H, 3d, 256],
+ * w2 [H, 256, 64] f32, as in veda_trippool_score with w*_k = w*_q), for each sampled query
+ * tile a of (b, h), i = q_tiles[b, h, a] (clamped to [0, n_t)):
+ *   p = target[b, h, a, :] / sum_j target[b, h, a, j]   (e.g. the veda_oracle_tilemap rows)
+ *   s = score_scale * y_q[i] . y_k[j]  for every key tile j
+ *   loss = mean over the B*H*n_sel rows of KL(p || softmax(s))   (out [1] f32)
+ *   dw1, dw2 = d loss / d w1, w2 (out, same shapes as w1, w2); descriptors are constants.
+ * If lr != 0 the weights are then updated in place: w -= lr * dw.  Deterministic.
+ *   q_tiled, k_tiled: VEDA_TILE_ROWS;  q_tiles: DEVICE int32 [B, H, n_sel] (required; a
+ *   tile sampled twice counts twice);  target: [B, H, n_sel, n_t] f32, rows with a
+ *   positive sum;  workspace: >= veda_distill_workspace_bytes(g, n_sel) bytes. */
+veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
+                              float *w1, float *w2, int32_t mlp_hidden, int32_t mlp_out, float score_scale,
+                              const int32_t *q_tiles, int32_t n_sel, const float *target, float *loss,
+                              float *dw1, float *dw2, float lr, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Per-head squared output error, the objective of the tiling search.  [Technical Summary
  * §2.2 Head-Aware Tiling, "Offline Selection": each head's tiling is picked on calibration
  * data by the error between the full-attention and the sparse-attention output]

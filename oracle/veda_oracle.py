@@ -237,6 +237,75 @@ def search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, 
 
 
 # ---------------------------------------------------------------------------
+# Distillation of the estimator  [Veda Technical Summary, §2.1 Distilled Tile Scoring,
+# "Optimization": row-wise KL divergence between the full-attention reference and the
+# predicted tile-score distribution; stop-gradient on the features feeding the estimator]
+# ---------------------------------------------------------------------------
+def gelu_grad(x):
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x).  Pinned: central differences of gelu."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+
+
+def kl_rows(p, s):
+    """KL(p || softmax(s)) per row, with 0 log 0 = 0.  Pinned: zero when p = softmax(s),
+    a hand-worked two-entry row, non-negativity."""
+    p, s = np.asarray(p, np.float64), np.asarray(s, np.float64)
+    m = s.max(axis=1, keepdims=True)
+    logq = s - m - np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(p > 0, p * (np.log(np.where(p > 0, p, 1.0)) - logq), 0.0)
+    return t.sum(axis=1)
+
+
+def distill_loss(descs, w1, w2, q_tiles, targets, score_scale):
+    """Mean over every sampled row of KL(target row normalised to sum 1 || softmax of the
+    estimator's logits).  descs: list over (b, h) of (D_q [n_t, 3d], D_k [n_t, 3d]) with
+    head index h_of[k]; w1 [H, 3d, hid], w2 [H, hid, out]; q_tiles[(b, h)]: [n_sel];
+    targets[(b, h)]: [n_sel, n_t]."""
+    total, rows = 0.0, 0
+    for (bh, h), (dq, dk) in descs.items():
+        yq = mlp(dq, w1[h], w2[h])
+        yk = mlp(dk, w1[h], w2[h])
+        sel = np.asarray(q_tiles[bh])
+        s = tile_scores(yq[sel], yk, score_scale)
+        t = np.asarray(targets[bh], np.float64)
+        total += kl_rows(t / t.sum(axis=1, keepdims=True), s).sum()
+        rows += len(sel)
+    return total / rows
+
+
+def distill_grads(descs, w1, w2, q_tiles, targets, score_scale):
+    """Loss and its gradients with respect to w1, w2 (same arguments as distill_loss), by
+    the chain rule written out: dL/ds = (softmax(s) - p) / rows; dy_q, dy_k from
+    s = scale y_q y_k^T; through y = GELU(D W1) W2 with D constant.  Pinned: central
+    differences of distill_loss."""
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    g1, g2 = np.zeros_like(w1), np.zeros_like(w2)
+    rows = sum(len(np.asarray(q_tiles[bh])) for bh, _ in descs)
+    total = 0.0
+    for (bh, h), (dq, dk) in descs.items():
+        zq, zk = np.asarray(dq, np.float64) @ w1[h], np.asarray(dk, np.float64) @ w1[h]
+        hq, hk = gelu(zq), gelu(zk)
+        yq, yk = hq @ w2[h], hk @ w2[h]
+        sel = np.asarray(q_tiles[bh])
+        s = tile_scores(yq[sel], yk, score_scale)
+        t = np.asarray(targets[bh], np.float64)
+        p = t / t.sum(axis=1, keepdims=True)
+        total += kl_rows(p, s).sum()
+        ds = (row_softmax(s) - p) / rows
+        dyq = np.zeros_like(yq)
+        np.add.at(dyq, sel, score_scale * ds @ yk)
+        dyk = score_scale * ds.T @ yq[sel]
+        g2[h] += hq.T @ dyq + hk.T @ dyk
+        dzq = (dyq @ w2[h].T) * gelu_grad(zq)
+        dzk = (dyk @ w2[h].T) * gelu_grad(zk)
+        g1[h] += np.asarray(dq, np.float64).T @ dzq + np.asarray(dk, np.float64).T @ dzk
+    return total / rows, g1, g2
+
+
+# ---------------------------------------------------------------------------
 # Index agreement under near-ties
 # ---------------------------------------------------------------------------
 def topk_agrees(score_row, idx_row, k, gap=1e-5):

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 13, syms
     for s in syms:
         assert hasattr(L, s), s
 

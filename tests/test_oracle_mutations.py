@@ -177,6 +177,50 @@ def search_no_untiling(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, 
     return err.sum(axis=1).argmin(axis=0), err, ref
 
 
+def gelu_grad_no_density(x):
+    """Drops the x phi(x) term."""
+    x = np.asarray(x, np.float64)
+    return 0.5 * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def kl_reversed(p, s):
+    """KL(softmax(s) || p) instead of KL(p || softmax(s))."""
+    p, s = np.asarray(p, np.float64), np.asarray(s, np.float64)
+    q = O.row_softmax(s)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(q > 0, q * (np.log(q) - np.log(np.where(p > 0, p, 1e-300))), 0.0)
+    return t.sum(axis=1)
+
+
+def distill_grads_sign(descs, w1, w2, q_tiles, targets, score_scale):
+    """dL/ds = p - softmax(s) (wrong sign)."""
+    loss, g1, g2 = O.distill_grads(descs, w1, w2, q_tiles, targets, score_scale)
+    return loss, -g1, -g2
+
+
+def distill_grads_no_dyk(descs, w1, w2, q_tiles, targets, score_scale):
+    """Forgets that the key-tile outputs depend on the weights too."""
+    w1, w2 = np.asarray(w1, np.float64), np.asarray(w2, np.float64)
+    g1, g2 = np.zeros_like(w1), np.zeros_like(w2)
+    rows = sum(len(np.asarray(q_tiles[bh])) for bh, _ in descs)
+    total = 0.0
+    for (bh, h), (dq, dk) in descs.items():
+        zq = np.asarray(dq, np.float64) @ w1[h]
+        hq = O.gelu(zq)
+        yq, yk = hq @ w2[h], O.mlp(dk, w1[h], w2[h])
+        sel = np.asarray(q_tiles[bh])
+        s = O.tile_scores(yq[sel], yk, score_scale)
+        t = np.asarray(targets[bh], np.float64)
+        p = t / t.sum(axis=1, keepdims=True)
+        total += O.kl_rows(p, s).sum()
+        ds = (O.row_softmax(s) - p) / rows
+        dyq = np.zeros_like(yq)
+        np.add.at(dyq, sel, score_scale * ds @ yk)
+        g2[h] += hq.T @ dyq
+        g1[h] += np.asarray(dq, np.float64).T @ ((dyq @ w2[h].T) * O.gelu_grad(zq))
+    return total / rows, g1, g2
+
+
 MUTANTS = [
     ("perm: in-tile axes swapped", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_swapped_inner]),
     ("perm: tile order reversed", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_tile_order_colmajor]),
@@ -200,6 +244,10 @@ MUTANTS = [
     ("tilemap: mean pooling", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_mean]),
     ("tilemap: not normalised", [pins.pin_tilemap_hand, pins.pin_tilemap_bruteforce], [tilemap_unnormalised]),
     ("search: argmax", [pins.pin_search_block_local], [search_argmax]),
+    ("gelu': density term dropped", [pins.pin_gelu_grad_fd], [gelu_grad_no_density]),
+    ("kl: direction reversed", [pins.pin_kl_rows], [kl_reversed]),
+    ("distill: gradient sign", [pins.pin_distill_fd], [distill_grads_sign]),
+    ("distill: key-tile path dropped", [pins.pin_distill_fd], [distill_grads_no_dyk]),
     ("search: output left tile-major", [pins.pin_search_block_local, pins.pin_search_all_kept], [search_no_untiling]),
 ]
 

@@ -416,3 +416,80 @@ def test_head_output_error_closed_form():
     a = np.arange(12.0).reshape(3, 4)
     assert O.head_output_error(a, a) == 0.0
     assert O.head_output_error(a + 0.5, a) == 12 * 0.25
+
+
+# ------------------------------------------------------------------ distillation
+def pin_gelu_grad_fd(gelu_grad):
+    x = np.array([-6.0, -2.5, -1.0, -0.3, 0.0, 0.4, 1.0, 2.2, 5.0])
+    h = 1e-6
+    fd = (O.gelu(x + h) - O.gelu(x - h)) / (2 * h)
+    assert np.allclose(gelu_grad(x), fd, rtol=0, atol=1e-8)
+    assert math.isclose(float(gelu_grad(np.array(0.0))), 0.5, abs_tol=1e-15)
+
+
+def pin_kl_rows(kl_rows):
+    s = np.array([[0.3, -1.2, 2.0, 0.1]])
+    q = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    assert abs(kl_rows(q, s)[0]) < 1e-15
+    assert math.isclose(kl_rows(np.array([[1.0, 0.0]]), np.array([[0.0, 0.0]]))[0], math.log(2.0), rel_tol=1e-14)
+    # p = (0.5, 0.5), q = (0.2, 0.8): 0.5 log(0.5/0.2) + 0.5 log(0.5/0.8)
+    s2 = np.log(np.array([[0.2, 0.8]]))
+    want = 0.5 * math.log(2.5) + 0.5 * math.log(0.625)
+    assert math.isclose(kl_rows(np.array([[0.5, 0.5]]), s2)[0], want, rel_tol=1e-13)
+    rng = np.random.default_rng(21)
+    p = rng.random((5, 7))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.all(kl_rows(p, rng.standard_normal((5, 7))) >= 0)
+
+
+def _distill_case(seed=22, H=2, B=2, nt=6, d3=12, hid=5, out=4, n_sel=3):
+    rng = np.random.default_rng(seed)
+    descs = {(b * H + h, h): (rng.standard_normal((nt, d3)), rng.standard_normal((nt, d3)))
+             for b in range(B) for h in range(H)}
+    w1 = rng.standard_normal((H, d3, hid)) / np.sqrt(d3)
+    w2 = rng.standard_normal((H, hid, out)) / np.sqrt(hid)
+    q_tiles = {bh: np.array([0, 4, 4][:n_sel]) if bh == 1 else rng.choice(nt, n_sel, replace=False)
+               for bh, _ in descs}
+    targets = {bh: rng.random((n_sel, nt)) ** 3 for bh, _ in descs}
+    return descs, w1, w2, q_tiles, targets
+
+
+def pin_distill_fd(distill_grads):
+    """Central differences of the loss in every weight (one head's query tile sampled twice)."""
+    descs, w1, w2, q_tiles, targets = _distill_case()
+    loss, g1, g2 = distill_grads(descs, w1, w2, q_tiles, targets, 0.3)
+    assert math.isclose(loss, O.distill_loss(descs, w1, w2, q_tiles, targets, 0.3), rel_tol=1e-12)
+    h = 1e-6
+    for w, g in ((w1, g1), (w2, g2)):
+        fd = np.zeros_like(w)
+        for idx in np.ndindex(*w.shape):
+            wp, wm = w.copy(), w.copy()
+            wp[idx] += h
+            wm[idx] -= h
+            lp = O.distill_loss(descs, wp if w is w1 else w1, wp if w is w2 else w2, q_tiles, targets, 0.3)
+            lm = O.distill_loss(descs, wm if w is w1 else w1, wm if w is w2 else w2, q_tiles, targets, 0.3)
+            fd[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(g, fd, rtol=1e-5, atol=1e-9), np.abs(g - fd).max()
+
+
+def test_gelu_grad_fd():
+    pin_gelu_grad_fd(O.gelu_grad)
+
+
+def test_kl_rows():
+    pin_kl_rows(O.kl_rows)
+
+
+def test_distill_grads_fd():
+    pin_distill_fd(O.distill_grads)
+
+
+def test_distill_zero_at_match():
+    """If the target rows are the estimator's own distribution, loss and gradients vanish."""
+    descs, w1, w2, q_tiles, _ = _distill_case(seed=23)
+    targets = {}
+    for (bh, h), (dq, dk) in descs.items():
+        s = O.tile_scores(O.mlp(dq, w1[h], w2[h])[q_tiles[bh]], O.mlp(dk, w1[h], w2[h]), 0.3)
+        targets[bh] = O.row_softmax(s) * 7.0   # any positive scale: rows are normalised
+    loss, g1, g2 = O.distill_grads(descs, w1, w2, q_tiles, targets, 0.3)
+    assert abs(loss) < 1e-15 and np.abs(g1).max() < 1e-15 and np.abs(g2).max() < 1e-15

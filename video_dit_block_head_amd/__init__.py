@@ -76,6 +76,9 @@ def lib():
             "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
             "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "veda_distill_workspace_bytes": (sz, [G, i32]),
+            "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
+                                        vp]),
             "veda_status_str": (ctypes.c_char_p, [i32]),
             "veda_last_hip_error": (ctypes.c_int, []),
             "veda_version": (ctypes.c_char_p, []),
@@ -189,3 +192,19 @@ def veda_head_sq_error(a, b, err, ref_sq=None, stream=None):
     B, N, H, d = (int(x) for x in a.shape)
     _check("veda_head_sq_error", lib().veda_head_sq_error(
         B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), _p(err, "err"), _p(ref_sq, "ref_sq"), _stream(stream)))
+
+
+def veda_distill_workspace_bytes(geom, n_sel):
+    return int(lib().veda_distill_workspace_bytes(geom.ref, int(n_sel)))
+
+
+def veda_distill_step(geom, q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1, dw2, score_scale=0.125, lr=0.0,
+                      workspace=None, stream=None):
+    """One KL distillation step of the per-head estimator (shared Q/K MLP).  w1, w2 are
+    updated in place when lr != 0; loss [1], dw1, dw2 are outputs."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("veda_distill_step", lib().veda_distill_step(
+        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), _p(w1, "w1"), _p(w2, "w2"),
+        int(w1.shape[-1]), int(w2.shape[-1]), float(score_scale), _p(q_tiles, "q_tiles"), int(q_tiles.shape[-1]),
+        _p(target, "target"), _p(loss, "loss"), _p(dw1, "dw1"), _p(dw2, "dw2"), float(lr), _p(workspace, "workspace"),
+        ws_bytes, _stream(stream)))

@@ -165,6 +165,37 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void
       launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, workspace, stream));
 }
 
+size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel) {
+  if (g == nullptr || g->batch < 1 || g->heads < 1 || g->tile < 1 || g->head_dim < 1 || n_sel < 1) return 0;
+  Geo geo{};
+  geo.B = g->batch;
+  geo.H = g->heads;
+  geo.d = g->head_dim;
+  geo.P = g->tile;
+  geo.nt = (int32_t)((int64_t)g->t * g->h * g->w / g->tile);
+  return distill_workspace_bytes(geo, n_sel);
+}
+
+veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
+                              float *w1, float *w2, int32_t mlp_hidden, int32_t mlp_out, float score_scale,
+                              const int32_t *q_tiles, int32_t n_sel, const float *target, float *loss, float *dw1,
+                              float *dw2, float lr, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_tiled || !k_tiled || !w1 || !w2 || !q_tiles || !target || !loss || !dw1 || !dw2) return VEDA_ERR_NULL;
+  if (n_sel < 1 || n_sel > geo.nt) return VEDA_ERR_SHAPE;
+  if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
+  if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1, dw2, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < distill_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
+  return hip_status(launch_distill(geo, dtype, q_tiled, k_tiled, w1, w2, score_scale, q_tiles, n_sel, target, loss,
+                                   dw1, dw2, lr, workspace, stream));
+}
+
 veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim, veda_dtype dtype,
                                const void *a, const void *b, float *err, float *ref_sq, hipStream_t stream) {
   if (dtype != VEDA_F32 && dtype != VEDA_BF16) return VEDA_ERR_DTYPE;

@@ -1,0 +1,333 @@
+// Distillation step of the tile-score estimator.  [Technical Summary: Veda, §2.1 Distilled
+// Tile Scoring, "Optimization": a row-wise KL divergence aligns the estimator's tile-score
+// distribution with the full-attention reference; the backbone features that feed the
+// estimator are stop-gradient, so only the per-head MLP is trained]
+//
+// For every sampled query tile a (tile i = q_tiles[b, h, a]) of every head:
+//   p_a = M[b, h, a, :] / sum_j M[b, h, a, j]        (max-pooled map, normalised per row)
+//   s_a = score_scale * y_q[i] . y_k[:]              (estimator logits of that row)
+//   L   = mean over all B*H*n_sel rows of KL(p_a || softmax(s_a))
+// and the gradients of L with respect to W1 [H, 3d, 256] and W2 [H, 256, 64] (one MLP per
+// head, shared by the Q-tile and K-tile descriptors), y = GELU(D W1) W2.
+//   dL/ds_a = (softmax(s_a) - p_a) / R
+//   dy_q[i] = score_scale * sum over the rows a of tile i of dL/ds_a . y_k
+//   dy_k[j] = score_scale * sum_a dL/ds_a[j] y_q[i_a]
+//   dW2 = sum over Q and K rows of H1^T dy,  dZ1 = (dy W2^T) * GELU'(Z1),  dW1 = sum D^T dZ1
+// Kernels (all deterministic: fixed-order reductions, no atomics):
+//   pool_mlp (score.hip)  descriptors D and outputs y of every Q and K tile
+//   kl_grad_kernel        one wave per sampled row: logits, softmax, KL, dL/ds, and that
+//                         row's contribution g_a = score_scale * dL/ds_a . y_k
+//   dyq_kernel            dy_q[i] = sum of g_a over the rows a sampling tile i
+//   dyk_kernel            dy_k[j] (one wave per key tile)
+//   mlp_bwd_rows_kernel   per 32 rows: Z1 = D W1, H1 = GELU(Z1), dZ1 = (dy W2^T) GELU'(Z1)
+//   atb_kernel            dW1 = D^T dZ1 and dW2 = H1^T dy per head, 64 x 64 output tiles
+//   loss_kernel, sgd_kernel
+// The step is small next to the forward path (a few GFLOP); plain fp32 VALU arithmetic.
+#include "common.h"
+#include "kernels.h"
+
+namespace veda {
+
+static constexpr int DS_HID = 256, DS_OUT = 64;
+
+static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout (floats): y [2][B][H][n_t][64] | D [2][B][H][n_t][3d] | dS [B][H][n_sel][n_t]
+// | G [B][H][n_sel][64] | dY [2][B][H][n_t][64] | H1 [2][B][H][n_t][256] | dZ1 (same) | loss [B*H*n_sel]
+struct DistillWs {
+  float *y, *desc, *ds, *gq, *dy, *h1, *dz1, *loss;
+};
+
+static size_t ws_parts(const Geo &g, int n_sel, size_t *off) {
+  const size_t rows = 2 * (size_t)g.B * g.H * g.nt, sel = (size_t)g.B * g.H * n_sel;
+  const size_t sz[8] = {rows * DS_OUT, rows * 3 * g.d, sel * g.nt, sel * DS_OUT,
+                        rows * DS_OUT, rows * DS_HID, rows * DS_HID, sel};
+  size_t o = 0;
+  for (int i = 0; i < 8; ++i) {
+    off[i] = o;
+    o += al256(sz[i] * sizeof(float));
+  }
+  return o;
+}
+
+size_t distill_workspace_bytes(const Geo &g, int n_sel) {
+  size_t off[8];
+  return ws_parts(g, n_sel, off);
+}
+
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad(float x) {
+  // d/dx [x Phi(x)] = Phi(x) + x phi(x)
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
+
+// One wave per sampled row (b, h, a); 4 rows per workgroup.
+template <int MAXM>
+__global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ y, const int32_t *__restrict__ q_tiles,
+                                                      int n_sel, const float *__restrict__ target, float scale,
+                                                      float inv_rows, float *__restrict__ ds, float *__restrict__ gq,
+                                                      float *__restrict__ loss_rows, Geo g) {
+  __shared__ float dsl[4][64 * MAXM];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;  // (b*H + h)*n_sel + a
+  if (row >= (int64_t)g.B * g.H * n_sel) return;      // whole wave; no barrier follows
+  const int64_t bh = row / n_sel;
+  const int nt = g.nt;
+  const int i = min(max(q_tiles[row], 0), nt - 1);
+  const float *yq = y + (bh * nt + i) * DS_OUT;
+  const float *yk = y + (((int64_t)g.B * g.H + bh) * nt) * DS_OUT;
+  const float *m = target + row * nt;
+  float s[MAXM], mt[MAXM];
+  float mx = -INFINITY, msum = 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXM; ++u) {
+    const int j = 64 * u + lane;
+    s[u] = -INFINITY;
+    mt[u] = 0.f;
+    if (j < nt) {
+      const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)j * DS_OUT);
+      const float4 *qr = reinterpret_cast<const float4 *>(yq);
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < DS_OUT / 4; ++c) {
+        const float4 a = qr[c], b = kr[c];
+        acc = fmaf(a.x, b.x, acc);
+        acc = fmaf(a.y, b.y, acc);
+        acc = fmaf(a.z, b.z, acc);
+        acc = fmaf(a.w, b.w, acc);
+      }
+      s[u] = acc * scale;
+      mt[u] = m[j];
+      mx = fmaxf(mx, s[u]);
+      msum += mt[u];
+    }
+  }
+  mx = wave_max(mx);
+  msum = wave_sum(msum);
+  float se = 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXM; ++u)
+    if (64 * u + lane < nt) se += expf(s[u] - mx);
+  se = wave_sum(se);
+  const float lse = mx + logf(se), inv_m = 1.0f / msum;
+  float kl = 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXM; ++u) {
+    const int j = 64 * u + lane;
+    if (j < nt) {
+      const float p = mt[u] * inv_m, logq = s[u] - lse;
+      if (p > 0.f) kl += p * (logf(p) - logq);
+      const float d = (expf(logq) - p) * inv_rows;
+      ds[row * nt + j] = d;
+      dsl[wv][j] = d;
+    }
+  }
+  kl = wave_sum(kl);
+  if (lane == 0) loss_rows[row] = kl;
+  // g_a[c] = scale * sum_j dS[j] y_k[j][c]: lane c walks the row that this wave's lanes
+  // have just written to LDS (the fence completes those writes and orders the reads after)
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  float acc = 0.f;
+  for (int j = 0; j < nt; ++j) acc = fmaf(dsl[wv][j], yk[(int64_t)j * DS_OUT + lane], acc);
+  gq[row * DS_OUT + lane] = acc * scale;
+}
+
+// dy_q[b, h, i][c] = sum over the sampled rows a with tile i of g_a[c], in order of a.
+__global__ void __launch_bounds__(64) dyq_kernel(const int32_t *__restrict__ q_tiles, int n_sel,
+                                                 const float *__restrict__ gq, float *__restrict__ dy, Geo g) {
+  const int i = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int c = threadIdx.x;
+  float acc = 0.f;
+  for (int a = 0; a < n_sel; ++a)
+    if (min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) == i) acc += gq[(bh * n_sel + a) * DS_OUT + c];
+  dy[(bh * g.nt + i) * DS_OUT + c] = acc;
+}
+
+// dy_k[b, h, j][c] = scale * sum_a dS[a][j] y_q[i_a][c], in order of a.
+__global__ void __launch_bounds__(64) dyk_kernel(const int32_t *__restrict__ q_tiles, int n_sel,
+                                                 const float *__restrict__ ds, const float *__restrict__ y,
+                                                 float scale, float *__restrict__ dy, Geo g) {
+  const int j = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int c = threadIdx.x;
+  const int64_t kbase = (int64_t)g.B * g.H;
+  float acc = 0.f;
+  for (int a = 0; a < n_sel; ++a) {
+    const int i = min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1);
+    acc = fmaf(ds[(bh * n_sel + a) * g.nt + j], y[(bh * g.nt + i) * DS_OUT + c], acc);
+  }
+  dy[((kbase + bh) * g.nt + j) * DS_OUT + c] = acc * scale;
+}
+
+// 32 rows of one (Q|K, b, h): Z1 = D W1 (thread u = hidden unit u), H1 = GELU(Z1),
+// dZ1 = (dy W2^T) * GELU'(Z1).
+__global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restrict__ desc, const float *__restrict__ dy,
+                                                           const float *__restrict__ w1, const float *__restrict__ w2,
+                                                           float *__restrict__ h1, float *__restrict__ dz1, Geo g) {
+  const int d3 = 3 * g.d;
+  extern __shared__ float sm[];  // [32][3d] descriptors, then [32][64] dy
+  float *Dl = sm, *Yl = sm + 32 * d3;
+  const int ngrp = (g.nt + 31) / 32;
+  const int grp = blockIdx.x % ngrp;
+  const int64_t wbh = blockIdx.x / ngrp;         // (which*B + b)*H + h
+  const int h = (int)(wbh % g.H);
+  const int r0 = grp * 32, nr = min(32, g.nt - r0);
+  const int u = threadIdx.x;
+  for (int e = u; e < 32 * d3; e += 256) {
+    const int r = e / d3;
+    Dl[e] = r < nr ? desc[(wbh * g.nt + r0 + r) * d3 + e % d3] : 0.f;
+  }
+  for (int e = u; e < 32 * DS_OUT; e += 256) {
+    const int r = e / DS_OUT;
+    Yl[e] = r < nr ? dy[(wbh * g.nt + r0 + r) * DS_OUT + e % DS_OUT] : 0.f;
+  }
+  __syncthreads();
+  const float *W1 = w1 + (int64_t)h * d3 * DS_HID + u;
+  const float *W2 = w2 + ((int64_t)h * DS_HID + u) * DS_OUT;
+  float z[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) z[r] = 0.f;
+  for (int f = 0; f < d3; ++f) {
+    const float wv = W1[(int64_t)f * DS_HID];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) z[r] = fmaf(Dl[r * d3 + f], wv, z[r]);
+  }
+  float dh[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) dh[r] = 0.f;
+  for (int o = 0; o < DS_OUT; ++o) {
+    const float wv = W2[o];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) dh[r] = fmaf(Yl[r * DS_OUT + o], wv, dh[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if (r < nr) {
+      const int64_t o = (wbh * g.nt + r0 + r) * DS_HID + u;
+      h1[o] = gelu_f(z[r]);
+      dz1[o] = dh[r] * gelu_grad(z[r]);
+    }
+  }
+}
+
+// C[h] (M x N) = sum over rows of A[row][m] * B[row][n], rows = the 2*B segments (Q|K, b)
+// of n_t rows of head h; A has row stride lda, B row stride ldb (floats); 64 x 64 tiles,
+// 4 x 4 outputs per thread, rows staged 16 at a time in LDS.
+__global__ void __launch_bounds__(256) atb_kernel(const float *__restrict__ A, int lda, const float *__restrict__ Bm,
+                                                  int ldb, int M, int N, float *__restrict__ C, Geo g) {
+  __shared__ float As[16][64 + 4], Bs[16][64 + 4];
+  const int tm = blockIdx.x, tn = blockIdx.y, h = blockIdx.z;
+  const int t = threadIdx.x, ti = t >> 4, tj = t & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+  const int nseg = 2 * g.B;
+  for (int sgm = 0; sgm < nseg; ++sgm) {
+    const int64_t rbase = ((int64_t)sgm * g.H + h) * g.nt;  // (which*B + b)*H + h
+    for (int r0 = 0; r0 < g.nt; r0 += 16) {
+      __syncthreads();
+      for (int e = t; e < 16 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        const bool ok = r0 + r < g.nt;
+        const int m = 64 * tm + c, n = 64 * tn + c;
+        As[r][c] = ok && m < M ? A[(rbase + r0 + r) * lda + m] : 0.f;
+        Bs[r][c] = ok && n < N ? Bm[(rbase + r0 + r) * ldb + n] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int r = 0; r < 16; ++r) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) av[a] = As[r][4 * ti + a];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bv[b] = Bs[r][4 * tj + b];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int m = 64 * tm + 4 * ti + a;
+    if (m >= M) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = 64 * tn + 4 * tj + b;
+      if (n < N) C[((int64_t)h * M + m) * N + n] = acc[a][b];
+    }
+  }
+}
+
+// loss = (sum of the row KLs) / rows, summed in a fixed order by one workgroup.
+__global__ void __launch_bounds__(256) loss_kernel(const float *__restrict__ rows, int64_t n, float *__restrict__ loss) {
+  __shared__ float red[256];
+  float acc = 0.f;
+  for (int64_t e = threadIdx.x; e < n; e += 256) acc += rows[e];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = red[0] / (float)n;
+}
+
+__global__ void __launch_bounds__(256) sgd_kernel(float *__restrict__ w, const float *__restrict__ dw, float lr,
+                                                  int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) w[e] -= lr * dw[e];
+}
+
+template <int MAXM>
+static void launch_kl(const Geo &g, const float *y, const int32_t *q_tiles, int n_sel, const float *target,
+                      float scale, float inv_rows, const DistillWs &w, hipStream_t st) {
+  const int64_t rows = (int64_t)g.B * g.H * n_sel;
+  kl_grad_kernel<MAXM><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(y, q_tiles, n_sel, target, scale, inv_rows,
+                                                                       w.ds, w.gq, w.loss, g);
+}
+
+hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void *k, float *w1, float *w2,
+                          float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
+                          float *dw1, float *dw2, float lr, void *ws, hipStream_t st) {
+  size_t off[8];
+  ws_parts(g, n_sel, off);
+  char *base = static_cast<char *>(ws);
+  DistillWs w{(float *)(base + off[0]), (float *)(base + off[1]), (float *)(base + off[2]), (float *)(base + off[3]),
+              (float *)(base + off[4]), (float *)(base + off[5]), (float *)(base + off[6]), (float *)(base + off[7])};
+  const int d3 = 3 * g.d;
+  const size_t desc_half = (size_t)g.B * g.H * g.nt * d3;
+  // forward: descriptors and MLP outputs of every Q and K tile (shared weights)
+  launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st);
+  const int64_t rows = (int64_t)g.B * g.H * n_sel;
+  const float inv_rows = 1.0f / (float)rows;
+  if (g.nt <= 64)
+    launch_kl<1>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+  else if (g.nt <= 256)
+    launch_kl<4>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+  else if (g.nt <= 640)
+    launch_kl<10>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+  else
+    launch_kl<20>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+  const dim3 gi(g.nt, g.B * g.H);
+  dyq_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.gq, w.dy, g);
+  dyk_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.ds, w.y, score_scale, w.dy, g);
+  const int ngrp = (g.nt + 31) / 32;
+  const size_t smem = (size_t)(32 * d3 + 32 * DS_OUT) * sizeof(float);
+  mlp_bwd_rows_kernel<<<dim3(ngrp * 2 * g.B * g.H), 256, smem, st>>>(w.desc, w.dy, w1, w2, w.h1, w.dz1, g);
+  atb_kernel<<<dim3((d3 + 63) / 64, DS_HID / 64, g.H), 256, 0, st>>>(w.desc, d3, w.dz1, DS_HID, d3, DS_HID, dw1, g);
+  atb_kernel<<<dim3(DS_HID / 64, 1, g.H), 256, 0, st>>>(w.h1, DS_HID, w.dy, DS_OUT, DS_HID, DS_OUT, dw2, g);
+  loss_kernel<<<1, 256, 0, st>>>(w.loss, rows, loss);
+  if (lr != 0.f) {
+    const int64_t n1 = (int64_t)g.H * d3 * DS_HID, n2 = (int64_t)g.H * DS_HID * DS_OUT;
+    sgd_kernel<<<dim3((unsigned)((n1 + 255) / 256)), 256, 0, st>>>(w1, dw1, lr, n1);
+    sgd_kernel<<<dim3((unsigned)((n2 + 255) / 256)), 256, 0, st>>>(w2, dw2, lr, n2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace veda

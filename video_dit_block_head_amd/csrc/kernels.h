@@ -15,6 +15,11 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st);
 
+// TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL.
+hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
+                           const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
+                           float *k_desc, hipStream_t st);
+
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);
 
@@ -24,6 +29,12 @@ hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const 
 size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
                           const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st);
+
+// Distillation step (see distill.hip).
+size_t distill_workspace_bytes(const Geo &g, int n_sel);
+hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void *k, float *w1, float *w2,
+                          float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
+                          float *dw1, float *dw2, float lr, void *ws, hipStream_t st);
 
 hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,
                                 const void *b, float *err, float *ref_sq, hipStream_t st);

@@ -335,13 +335,9 @@ static void launch_score_t(const Geo &g, const float *y, float scale, float *sco
                                                                                  idx);
 }
 
-hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
-                        const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
-                        float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
-                        void *ws, hipStream_t st) {
-  (void)hidden;
-  (void)mlp_out;
-  float *y = (float *)ws;
+hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
+                           const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
+                           float *k_desc, hipStream_t st) {
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
   if (dt == VEDA_BF16)
     pool_mlp_kernel<2><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
@@ -349,6 +345,17 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
   else
     pool_mlp_kernel<4><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
                                            k_desc, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
+                        const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
+                        float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
+                        void *ws, hipStream_t st) {
+  (void)hidden;
+  (void)mlp_out;
+  float *y = (float *)ws;
+  launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, st);
   else if (g.nt <= 256)

@@ -8,8 +8,9 @@ import math
 
 import torch
 
-from . import (COLS, ROWS, Geom, veda_head_sq_error, veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes,
-               veda_sparse_attn_fwd, veda_tile_gather, veda_trippool_score, veda_trippool_workspace_bytes)
+from . import (COLS, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
+               veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes, veda_sparse_attn_fwd, veda_tile_gather,
+               veda_trippool_score, veda_trippool_workspace_bytes)
 
 
 class SparseAttention:
@@ -71,6 +72,24 @@ class SparseAttention:
         veda_oracle_tilemap(self.geom, self.q_t, self.k_t, self.softmax_scale, q_tiles, n_sel, out, lse,
                             self._tm_ws[n_sel])
         return out
+
+    def distill_step(self, q_tiles, target, lr=0.0):
+        """One KL distillation step of this layer's estimator on the gathered Q, K: the
+        sampled query tiles q_tiles [B, H, n_sel] (int32) against target rows
+        [B, H, n_sel, n_t] (e.g. tilemap() of the same tiles).  Returns (loss [1], dw1, dw2);
+        with lr != 0 the weights are updated in place.  Needs one MLP shared by Q and K."""
+        if self.w1_k is not self.w1 or self.w2_k is not self.w2:
+            raise ValueError("the distillation step trains one MLP per head shared by Q and K")
+        n_sel = int(q_tiles.shape[-1])
+        key = ("distill", n_sel)
+        if key not in self._tm_ws:
+            nbytes = veda_distill_workspace_bytes(self.geom, n_sel)
+            self._tm_ws[key] = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        loss = torch.empty(1, dtype=torch.float32, device=self.device)
+        dw1, dw2 = torch.empty_like(self.w1), torch.empty_like(self.w2)
+        veda_distill_step(self.geom, self.q_t, self.k_t, self.w1, self.w2, q_tiles, target, loss, dw1, dw2,
+                          score_scale=self.score_scale, lr=lr, workspace=self._tm_ws[key])
+        return loss, dw1, dw2
 
     def forward(self, q, k, v, topk, out):
         self.gather(q, k, v)
