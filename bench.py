@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--topk", type=int, default=None, help="kept key tiles (default: the workload's headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the 0%%-skipping attention comparison")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip timing the distillation step and the per-head error kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -227,6 +229,38 @@ def main():
                  "ideal_speedup": round(nt / kk, 2)}
         del didx
 
+    # the rows built beyond the forward path, timed outside the step
+    nxt = None
+    if not args.no_next:
+        say("[bench] distillation step and per-head error kernel")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sa.distill_step(qtl, tmap)  # warm-up (allocates its workspace once)
+        torch.cuda.synchronize()
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            sa.distill_step(qtl, tmap)
+        e1.record()
+        torch.cuda.synchronize()
+        distill_ms = e0.elapsed_time(e1) / reps
+        err = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        ref = torch.empty_like(err)
+        V.veda_head_sq_error(out, q, err, ref)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            V.veda_head_sq_error(out, q, err, ref)
+        e1.record()
+        torch.cuda.synchronize()
+        herr_ms = e0.elapsed_time(e1) / reps
+        herr_bytes = 2 * B * N * H * d * 2
+        nxt = {"distill_step_ms": round(distill_ms, 4),
+               "distill_step_qk_read_gbps": round(2 * B * H * N * d * 2 / (distill_ms * 1e-3) / 1e9, 1),
+               "distill_sampled_query_tiles_per_head": n_sel,
+               "head_sq_error_ms": round(herr_ms, 4),
+               "head_sq_error_gbps": round(herr_bytes / (herr_ms * 1e-3) / 1e9, 1),
+               "head_sq_error_frac_hbm_peak": round(herr_bytes / (herr_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
     if args.copy_calibration:
         n = 1 << 29  # 1 GiB of bf16
         src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
@@ -268,6 +302,7 @@ def main():
         "scoring_frac_hbm_peak": round(score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "stages_median_ms": {s: round(x, 4) for s, x in med.items()},
         "dense": dense,
+        "next_rows": nxt,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -3,15 +3,17 @@
 // head is chosen on calibration data by the error between the full-attention output and
 // the sparse-attention output]
 //
-// One workgroup per (batch, head): 512 threads stream that head's d-element rows of both
-// raster tensors in 16-byte pieces, accumulate sum (a - b)^2 and sum b^2 in fp32 per
-// thread, and reduce in a fixed order (deterministic).  HBM-bound.
+// One workgroup per (batch, head): 1024 threads stream that head's d-element rows of both
+// raster tensors in 16-byte pieces (8 pieces of each tensor in flight per thread),
+// accumulate sum (a - b)^2 and sum b^2 in fp32 per thread, and reduce in a fixed order
+// (deterministic).  HBM-bound; the parallelism is B*H workgroups.
 #include "common.h"
 #include "kernels.h"
 
 namespace veda {
 
-static constexpr int SE_THREADS = 512;
+static constexpr int SE_THREADS = 1024;
+static constexpr int SE_UNROLL = 8;
 
 template <int EB>
 __global__ void __launch_bounds__(SE_THREADS) head_sq_error_kernel(const uint8_t *__restrict__ a,
@@ -25,33 +27,42 @@ __global__ void __launch_bounds__(SE_THREADS) head_sq_error_kernel(const uint8_t
   const int64_t base = ((int64_t)bb * n_tokens * heads + h) * head_dim * EB;
   float se = 0.f, sr = 0.f;
   const int64_t total = (int64_t)n_tokens * cpr;
-  for (int64_t e = t; e < total; e += SE_THREADS) {
-    const int64_t n = e / cpr;
-    const int c = (int)(e % cpr);
-    const int64_t o = base + n * row_stride + (int64_t)c * 16;
-    const uint4 va = *reinterpret_cast<const uint4 *>(a + o);
-    const uint4 vb = *reinterpret_cast<const uint4 *>(b + o);
+  auto accum = [&](const uint4 &va, const uint4 &vb) {
     const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float xa[2], xb[2];
-      int m = 1;
       if (EB == 2) {
-        xa[0] = __uint_as_float(wa[i] << 16);
-        xa[1] = __uint_as_float(wa[i] & 0xFFFF0000u);
-        xb[0] = __uint_as_float(wb[i] << 16);
-        xb[1] = __uint_as_float(wb[i] & 0xFFFF0000u);
-        m = 2;
+        const float a0 = __uint_as_float(wa[i] << 16), a1 = __uint_as_float(wa[i] & 0xFFFF0000u);
+        const float b0 = __uint_as_float(wb[i] << 16), b1 = __uint_as_float(wb[i] & 0xFFFF0000u);
+        se = fmaf(a0 - b0, a0 - b0, se);
+        se = fmaf(a1 - b1, a1 - b1, se);
+        sr = fmaf(b0, b0, sr);
+        sr = fmaf(b1, b1, sr);
       } else {
-        xa[0] = __uint_as_float(wa[i]);
-        xb[0] = __uint_as_float(wb[i]);
-      }
-      for (int j = 0; j < m; ++j) {
-        const float dlt = xa[j] - xb[j];
-        se = fmaf(dlt, dlt, se);
-        sr = fmaf(xb[j], xb[j], sr);
+        const float a0 = __uint_as_float(wa[i]), b0 = __uint_as_float(wb[i]);
+        se = fmaf(a0 - b0, a0 - b0, se);
+        sr = fmaf(b0, b0, sr);
       }
     }
+  };
+  // SE_UNROLL pieces per thread in flight: all loads of a step are issued before any use
+  int64_t e0 = t;
+  for (; e0 + (SE_UNROLL - 1) * SE_THREADS < total; e0 += SE_UNROLL * SE_THREADS) {
+    uint4 va[SE_UNROLL], vb[SE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SE_UNROLL; ++u) {
+      const int64_t e = e0 + (int64_t)u * SE_THREADS, n = e / cpr;
+      const int64_t o = base + n * row_stride + (e % cpr) * 16;
+      va[u] = *reinterpret_cast<const uint4 *>(a + o);
+      vb[u] = *reinterpret_cast<const uint4 *>(b + o);
+    }
+#pragma unroll
+    for (int u = 0; u < SE_UNROLL; ++u) accum(va[u], vb[u]);
+  }
+  for (int64_t e = e0; e < total; e += SE_THREADS) {  // tail: fewer than SE_UNROLL pieces left
+    const int64_t n = e / cpr;
+    const int64_t o = base + n * row_stride + (e % cpr) * 16;
+    accum(*reinterpret_cast<const uint4 *>(a + o), *reinterpret_cast<const uint4 *>(b + o));
   }
   __shared__ float red[2][SE_THREADS];
   red[0][t] = se;
