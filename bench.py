@@ -38,15 +38,16 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_from_counters(launch_bytes_unit="GB"):
+def traffic_from_counters(path):
     """HBM bytes per attention launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     counts, scaled by the same counters' reading of a plain copy of known size.  None if
-    the attention source changed since the counters were taken."""
+    the attention source changed since the counters were taken, or they were taken on the
+    other path."""
     if not os.path.exists(COUNTERS):
         return None
     rec = json.load(open(COUNTERS))
     sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if rec.get("attn_source_sha256") != sha:
+    if rec.get("attn_source_sha256") != sha or rec.get("path", "tiled") != path:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -118,6 +119,9 @@ def main():
     ap.add_argument("--topk", type=int, default=None, help="kept key tiles (default: the workload's headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the 0%%-skipping attention comparison")
+    ap.add_argument("--path", choices=["raster", "tiled"], default="raster",
+                    help="raster: the kernels read Q and write O through each head's tiling (K and V are "
+                         "gathered); tiled: explicit gather of Q, K, V and scatter of O")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the distillation step and the per-head error kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -164,20 +168,34 @@ def main():
     tmap = torch.empty((B, H, n_sel, nt), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
-    stages = ["gather", "score_topk", "sparse_attn", "scatter", "tilemap"]
+    if args.path == "tiled":
+        stages = ["gather", "score_topk", "sparse_attn", "scatter", "tilemap"]
 
-    def step(ev):
-        ev[0].record()
-        sa.gather(q, k, v)
-        ev[1].record()
-        idx = sa.score(kk)
-        ev[2].record()
-        sa.attend(idx)
-        ev[3].record()
-        sa.scatter(out)
-        ev[4].record()
-        sa.tilemap(qtl, n_sel, tmap)
-        ev[5].record()
+        def step(ev):
+            ev[0].record()
+            sa.gather(q, k, v)
+            ev[1].record()
+            idx = sa.score(kk)
+            ev[2].record()
+            sa.attend(idx)
+            ev[3].record()
+            sa.scatter(out)
+            ev[4].record()
+            sa.tilemap(qtl, n_sel, tmap)
+            ev[5].record()
+    else:
+        stages = ["gather_kv", "score_topk", "sparse_attn", "tilemap"]
+
+        def step(ev):
+            ev[0].record()
+            sa.gather_kv(k, v)
+            ev[1].record()
+            idx = sa.score_raster(q, kk)
+            ev[2].record()
+            sa.attend_raster(q, idx, out)
+            ev[3].record()
+            sa.tilemap_raster(q, qtl, n_sel, tmap)
+            ev[4].record()
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
@@ -213,13 +231,16 @@ def main():
     if not args.no_dense:
         didx = dense_index(geom)
         say("[bench] dense path (k = n_t)")
-        sa.attend(didx)
+        attend = (lambda ix: sa.attend(ix)) if args.path == "tiled" else (lambda ix: sa.attend_raster(q, ix, out))
+        if args.path == "tiled":
+            sa.gather(q, k, v)
+        attend(didx)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 3
         e0.record()
         for _ in range(reps):
-            sa.attend(didx)
+            attend(didx)
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / reps
@@ -233,6 +254,7 @@ def main():
     nxt = None
     if not args.no_next:
         say("[bench] distillation step and per-head error kernel")
+        sa.gather(q, k, v)  # the distillation step reads tiled Q and K
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         sa.distill_step(qtl, tmap)  # warm-up (allocates its workspace once)
         torch.cuda.synchronize()
@@ -277,7 +299,7 @@ def main():
         say("[bench] CPU oracle baseline (bounded sample)")
         cpu = cpu_baseline(cfg, wl, kk, n_sel)
 
-    traffic = traffic_from_counters()
+    traffic = traffic_from_counters(args.path)
     roof = {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
@@ -292,6 +314,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={B} H={H} d={d} latent {'x'.join(map(str, cfg.grid))} "
                                f"(N={N}), tile {P}, k={kk}/{nt} kept ({100 * (1 - kk / nt):.0f}% skipped)",
+                   "path": args.path,
                    "batch": B, "heads": H, "seq_len": N, "head_dim": d, "tile": P, "topk": kk, "n_tiles": nt,
                    "tile_shapes": sorted(set(wl.shapes)), "tilemap_query_tiles_per_head": n_sel},
         "sparse_attn_ms_per_call": round(attn_ms, 4),

@@ -61,7 +61,7 @@ enum {
 };
 
 typedef enum { VEDA_F32 = 0, VEDA_BF16 = 1 } veda_dtype;
-typedef enum { VEDA_TILE_ROWS = 0, VEDA_TILE_COLS = 1 } veda_layout;
+typedef enum { VEDA_TILE_ROWS = 0, VEDA_TILE_COLS = 1, VEDA_RASTER = 2 } veda_layout;
 
 #define VEDA_MAX_HEADS 128
 
@@ -158,6 +158,35 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
                                 const int32_t *q_tiles, int32_t n_sel,
                                 float *tilemap, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Raster-direct variants (no tiled copies of Q or O, and optionally none of K).
+ * [Technical Summary §2.3 and the paper's future work on fusing the tiling into the
+ * kernels]  They compute exactly what veda_trippool_score, veda_sparse_attn_fwd and
+ * veda_oracle_tilemap compute (bit for bit), but read Q (and write O) in the raster layout
+ * [B, N, H, d] with element strides rs_b, rs_n, rs_h (d contiguous, 16-byte aligned rows
+ * and strides), going through each head's tiling in the kernels: row r of tile j of head h
+ * is raster token origin_h(j) + intra_h(r).  k_layout says where K is: VEDA_RASTER (with
+ * the same strides as Q) or VEDA_TILE_ROWS (tile-major [B, H, N, d], from
+ * veda_tile_gather; K tiles are then contiguous 32 KB copies, which the attention and
+ * tile-map kernels prefer).  V stays VEDA_TILE_COLS.  The output of
+ * veda_sparse_attn_fwd_raster is raster (same strides) and its lse is [B, H, N] in raster
+ * token order; the tile-map lse keeps its [B, H, n_sel * P] tile-row order.  Extra status:
+ * VEDA_ERR_UNSUPPORTED if an in-tile token offset times the token stride reaches 2^31
+ * bytes.  Other arguments, outputs and workspaces as in the tiled calls. */
+veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
+                                       veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
+                                       const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
+                                       int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
+                                       float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
+                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
+                                        const void *v_cols, const int32_t *kv_idx, int32_t k_kept,
+                                        float softmax_scale, void *o_raster, float *lse, hipStream_t stream);
+veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
+                                       veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
+                                       float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
+                                       float *lse, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
  * gradients of every Q and K tile, per-row KL terms). */

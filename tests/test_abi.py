@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 16, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -145,3 +145,22 @@ def test_head_error_validation(L):
     assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, None) == NULL
     assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, None) == NULL
     assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, None) == ALIGN
+
+
+def test_raster_validation(L):
+    g = geom()
+    f = L.veda_sparse_attn_fwd_raster
+    st = (4096 * 2 * 128, 2 * 128, 128)
+    RAS = V.RASTER
+    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, A, 4, 0.088, A, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, None, RAS, *st, A, A, 4, 0.088, A, None, None) == NULL
+    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, A, 4, 0.088, A, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, A, 4, 0.088, A, None, None) == SHAPE   # K layout
+    # in-tile token offset x token stride beyond 2^31 bytes
+    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, A, 4, 0.088,
+             A, None, None) == UNSUP
+    s = L.veda_trippool_score_raster
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, A, 1 << 30,
+             None) == NULL
+    t = L.veda_oracle_tilemap_raster
+    assert t(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, A, 0, A, None, A, 1 << 40, None) == SHAPE

@@ -376,3 +376,42 @@ def test_topk_mask_standalone(n_cols, k):
     m = np.zeros((rows, n_cols), np.uint8)
     np.put_along_axis(m, ref, 1, axis=1)
     assert np.array_equal(host(mask), m)
+
+
+# ----------------------------------------------------------------------------- raster path
+@pytest.mark.parametrize("k_raster", [False, True], ids=["k_tiled", "k_raster"])
+def test_raster_path_matches_tiled(r, k_raster):
+    """The raster-direct calls (Q and O raster; K raster or tiled) give bit-identical
+    results to the tiled calls, which the tests above check against the oracle."""
+    cfg, sa = r.cfg, r.sa
+    B, H, N, nt = cfg.batch, cfg.heads, cfg.n_tokens, cfg.n_tiles
+    say(f"[gpu-parity] {cfg.name}: raster-direct path, K {'raster' if k_raster else 'tiled'}")
+    kk_ = r.k if k_raster else None
+    scores, probs = torch.empty_like(r.scores), torch.empty_like(r.probs)
+    qd, kd = torch.empty_like(r.qd), torch.empty_like(r.kd)
+    idx = sa.score_raster(r.q, r.kk, k=kk_, scores=scores, probs=probs, q_desc=qd, k_desc=kd).clone()
+    assert torch.equal(qd, r.qd) and torch.equal(kd, r.kd)
+    assert torch.equal(scores, r.scores) and torch.equal(probs, r.probs)
+    assert torch.equal(idx, r.idx)
+    out = torch.zeros_like(r.out)
+    lse = torch.empty_like(r.lse)
+    sa.attend_raster(r.q, idx, out, lse, k=kk_)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                       r.out.view(torch.int16) if r.out.dtype == torch.bfloat16 else r.out)
+    lse_t, lse_r = r.lse.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            perm = O.tile_permutation(cfg.grid, r.wl.shapes[h])
+            assert bitwise_equal(lse_r[b, h, perm], lse_t[b, h])
+    n_sel = min(8, nt)
+    qtl = torch.from_numpy(np.stack([r.q_tiles(h)[:n_sel] for h in range(H)]).astype(np.int32)[None]
+                           .repeat(B, 0)).cuda().contiguous()
+    m_t = torch.empty((B, H, n_sel, nt), dtype=torch.float32, device="cuda")
+    m_r = torch.empty_like(m_t)
+    l_t = torch.empty((B, H, n_sel * cfg.tile), dtype=torch.float32, device="cuda")
+    l_r = torch.empty_like(l_t)
+    sa.tilemap(qtl, n_sel, m_t, l_t)
+    sa.tilemap_raster(r.q, qtl, n_sel, m_r, l_r, k=kk_)
+    torch.cuda.synchronize()
+    assert torch.equal(m_t, m_r) and torch.equal(l_t, l_r)

@@ -13,7 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libveda.so")
 
 F32, BF16 = 0, 1
-ROWS, COLS = 0, 1
+ROWS, COLS, RASTER = 0, 1, 2
 MAX_HEADS = 128
 
 
@@ -77,6 +77,12 @@ def lib():
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
             "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
+            "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
+                                                 vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+            "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, i32, f32, vp, vp,
+                                                  vp]),
+            "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
+                                                 vp]),
             "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
                                         vp]),
             "veda_status_str": (ctypes.c_char_p, [i32]),
@@ -207,4 +213,59 @@ def veda_distill_step(geom, q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1
         geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), _p(w1, "w1"), _p(w2, "w2"),
         int(w1.shape[-1]), int(w2.shape[-1]), float(score_scale), _p(q_tiles, "q_tiles"), int(q_tiles.shape[-1]),
         _p(target, "target"), _p(loss, "loss"), _p(dw1, "dw1"), _p(dw2, "dw2"), float(lr), _p(workspace, "workspace"),
+        ws_bytes, _stream(stream)))
+
+
+def _raster_strides(*ts):
+    """Shared element strides (b, n, h) of raster [B, N, H, d] tensors (d contiguous)."""
+    st = tuple(int(x) for x in ts[0].stride()[:3])
+    for t in ts:
+        if t.dim() != 4 or t.stride(-1) != 1 or tuple(int(x) for x in t.stride()[:3]) != st:
+            raise VedaError("raster operands must be [B, N, H, d] with d contiguous and one set of strides")
+    return st
+
+
+def _k_operand(q, k, k_layout, *others):
+    """Strides shared by the raster operands, and the checked K pointer."""
+    if k_layout == RASTER:
+        return _raster_strides(q, k, *others), _p(k, "k", False)
+    if k_layout != ROWS:
+        raise VedaError("k_layout must be RASTER or ROWS")
+    return _raster_strides(q, *others), _p(k, "k")
+
+
+def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125, scores=None,
+                               probs=None, q_desc=None, k_desc=None, topk=0, idx=None, workspace=None,
+                               k_layout=RASTER, stream=None):
+    """veda_trippool_score on raster Q [B, N, H, d] (read through each head's tiling); K
+    raster too, or tile-major with k_layout=ROWS."""
+    w1_k = w1_q if w1_k is None else w1_k
+    w2_k = w2_q if w2_k is None else w2_k
+    rs, kp = _k_operand(q, k, k_layout)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("veda_trippool_score_raster", lib().veda_trippool_score_raster(
+        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, _p(w1_q, "w1_q"), _p(w2_q, "w2_q"),
+        _p(w1_k, "w1_k"), _p(w2_k, "w2_k"), int(w1_q.shape[-1]), int(w2_q.shape[-1]), float(score_scale),
+        _p(scores, "scores"), _p(probs, "probs"), _p(q_desc, "q_desc"), _p(k_desc, "k_desc"), int(topk),
+        _p(idx, "idx"), _p(workspace, "workspace"), ws_bytes, _stream(stream)))
+
+
+def veda_sparse_attn_fwd_raster(geom, q, k, v_cols, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
+                                stream=None):
+    """veda_sparse_attn_fwd with raster Q and output O [B, N, H, d]; K raster or tile-major
+    (k_layout=ROWS); V channel-major tiled; lse [B, H, N] in raster token order."""
+    rs, kp = _k_operand(q, k, k_layout, o)
+    _check("veda_sparse_attn_fwd_raster", lib().veda_sparse_attn_fwd_raster(
+        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, _p(v_cols, "v_cols"),
+        _p(kv_idx, "kv_idx"), int(kk), float(softmax_scale), _p(o, "o", False), _p(lse, "lse"), _stream(stream)))
+
+
+def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilemap, lse=None, workspace=None,
+                               k_layout=RASTER, stream=None):
+    """veda_oracle_tilemap on raster Q [B, N, H, d]; K raster or tile-major (k_layout=ROWS)."""
+    rs, kp = _k_operand(q, k, k_layout)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("veda_oracle_tilemap_raster", lib().veda_oracle_tilemap_raster(
+        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, float(softmax_scale),
+        _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
         ws_bytes, _stream(stream)))

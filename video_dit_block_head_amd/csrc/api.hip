@@ -55,6 +55,21 @@ veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *
   return VEDA_OK;
 }
 
+// Raster operands read through the tilings: 16-byte aligned rows and strides, and every
+// in-tile token offset (the per-lane part of a copy address) below 2^31 bytes.
+veda_status check_raster(const Geo &geo, const HeadShapes &hs, veda_dtype dt, int64_t rs_b, int64_t rs_n,
+                         int64_t rs_h) {
+  if (rs_b < 0 || rs_n < 0 || rs_h < 0) return VEDA_ERR_SHAPE;
+  const int64_t epc = dt == VEDA_BF16 ? 8 : 4, eb = dt == VEDA_BF16 ? 2 : 4;
+  if (rs_b % epc || rs_n % epc || rs_h % epc) return VEDA_ERR_ALIGN;
+  for (int h = 0; h < geo.H; ++h) {
+    const int64_t pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
+    const int64_t intra_max = ((pt - 1) * geo.Hs + (ph - 1)) * geo.Ws + (pw - 1);
+    if (intra_max * rs_n * eb >= ((int64_t)1 << 31)) return VEDA_ERR_UNSUPPORTED;
+  }
+  return VEDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +126,37 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream));
 }
 
+veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
+                                       const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
+                                       int64_t rs_h,
+                                       const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
+                                       int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
+                                       float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_raster || !k_raster || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
+  if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
+  if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
+  if (topk < 0 || topk > geo.nt) return VEDA_ERR_SHAPE;
+  if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
+  if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
+    return VEDA_ERR_WORKSPACE;
+  const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
+  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
+  return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
+                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs, &rv,
+                                 k_layout == VEDA_RASTER));
+}
+
 veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k, int32_t *idx,
                            uint8_t *mask, hipStream_t stream) {
   if (rows < 0 || n_cols < 1 || n_cols > 4096 || k < 1 || k > n_cols) return VEDA_ERR_SHAPE;
@@ -135,6 +181,26 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   return hip_status(launch_sparse_attn(geo, dtype, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse,
                                        stream));
+}
+
+veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
+                                        const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
+                                        int64_t rs_h,
+                                        const void *v_cols, const int32_t *kv_idx, int32_t k, float softmax_scale,
+                                        void *o_raster, float *lse, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_raster || !k_raster || !v_cols || !kv_idx || !o_raster) return VEDA_ERR_NULL;
+  if (k < 1 || k > geo.nt) return VEDA_ERR_SHAPE;
+  const void *ptrs[] = {q_raster, k_raster, v_cols, kv_idx, o_raster, lse};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
+                                              rs_h, v_cols, kv_idx, k, softmax_scale, o_raster, lse, stream));
 }
 
 size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {
@@ -174,6 +240,30 @@ size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel) {
   geo.P = g->tile;
   geo.nt = (int32_t)((int64_t)g->t * g->h * g->w / g->tile);
   return distill_workspace_bytes(geo, n_sel);
+}
+
+veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
+                                       const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
+                                       int64_t rs_h,
+                                       float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
+                                       float *lse, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (!q_raster || !k_raster || !tilemap) return VEDA_ERR_NULL;
+  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
+  if (geo.nt > TILEMAP_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_raster, k_raster, q_tiles, tilemap, lse, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (workspace == nullptr || workspace_bytes < tilemap_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
+  const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
+  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
+  return hip_status(launch_tilemap(geo, dtype, q_raster, k_raster, softmax_scale, q_tiles, n_sel, tilemap, lse,
+                                   workspace, stream, &hs, &rv, k_layout == VEDA_RASTER));
 }
 
 veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,

@@ -36,20 +36,31 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t &a, const bf16x8_t &b,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
+// the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
+// order; RK: the same for K.  Otherwise tile-major.  V is always channel-major tiled.
+template <bool RQ, bool RK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
                  const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
-                 float *__restrict__ lse, Geo g) {
+                 float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv) {
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int i = L % g.nt;
   const int64_t bh = L / g.nt;
+  const int hh = (int)(bh % g.H), bb = (int)(bh / g.H);
   const int t = threadIdx.x, lane = t & 63, lr = lane & 31, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
   const int64_t head = bh * (int64_t)g.N * 128;
-  const __bf16 *qh = q + head;
-  const char *kh = reinterpret_cast<const char *>(k + head), *vh = reinterpret_cast<const char *>(vt + head);
+  const int pt = hs.s[hh][0], ph = hs.s[hh][1], pw = hs.s[hh][2];
+  // raster: byte offset of (b, n = 0, h); a tile's rows are origin(j) + intra(r) tokens on
+  const int64_t rhead = (int64_t)bb * rv.sb + (int64_t)hh * rv.sh;
+  const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead : reinterpret_cast<const char *>(k + head);
+  const char *vh = reinterpret_cast<const char *>(vt + head);
   const int32_t *list = kv_idx + (bh * g.nt + i) * kk;
   const int last = g.nt - 1;
+  auto k_tile = [&](int j) -> const char * {
+    return RK ? kh + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn : kh + (int64_t)j * 32768;
+  };
 
   __shared__ uint4 Ks[128 * 16];
   __shared__ uint4 Vs[128 * 16];
@@ -57,16 +68,25 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   // Q fragments first, consumed by an empty asm so that they have arrived before the first
   // copy is issued (otherwise the compiler sinks the loads and waits for them in the loop).
   const int qrow = i * 128 + 32 * w + lr;
+  // this lane's query row: tiled row qrow, or its raster token
+  const int64_t qtok = RQ ? tile_origin(i, pt, ph, pw, g.Hs, g.Ws) + tile_intra(32 * w + lr, ph, pw, g.Hs, g.Ws) : 0;
+  const __bf16 *qp = RQ ? reinterpret_cast<const __bf16 *>(reinterpret_cast<const char *>(q) + rhead + qtok * rv.sn)
+                        : q + head + (int64_t)qrow * 128;
   bf16x8_t qf[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qh + (int64_t)qrow * 128 + 16 * s + 8 * hi);
+  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
-  uint32_t off[8];
+  uint32_t off[8], koff[8];
   tile_dma_offsets(w, lane, off);
+  if (RK)
+    tile_dma_offsets_raster(w, lane, ph, pw, g.Hs, g.Ws, rv.sn, koff);
+  else
+#pragma unroll
+    for (int e = 0; e < 8; ++e) koff[e] = off[e];
   const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
   int jn = min(max(list[0], 0), last);  // out-of-range entries are clamped
-  tile_to_lds(kh + (int64_t)jn * 32768, ks_lds, w, off);
+  tile_to_lds(k_tile(jn), ks_lds, w, koff);
   tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
 
   f32x16_t acc_o[4];
@@ -97,7 +117,7 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
     barrier();  // every wave has its K operands: the buffer may be refilled
     if (more) {
       jn = min(max(list[tt + 1], 0), last);
-      tile_to_lds(kh + (int64_t)jn * 32768, ks_lds, w, off);
+      tile_to_lds(k_tile(jn), ks_lds, w, koff);
     }
 
     // ---- online softmax (log2 domain)
@@ -158,7 +178,8 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
-  __bf16 *orow = o + head + (int64_t)qrow * 128;
+  __bf16 *orow = RQ ? reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(o) + rhead + qtok * rv.sn)
+                    : o + head + (int64_t)qrow * 128;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -171,22 +192,31 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
       v[3] = (__bf16)(acc_o[db][4 * r4 + 3] * inv);
       *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
     }
-  if (lse != nullptr && hi == 0) lse[bh * g.N + qrow] = (m_run + log2f(l_tot)) * LN2;
+  if (lse != nullptr && hi == 0) lse[bh * g.N + (RQ ? qtok : (int64_t)qrow)] = (m_run + log2f(l_tot)) * LN2;
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row, keys one at a time from LDS.
+template <bool RQ, bool RK>
 __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ vt, const int32_t *__restrict__ kv_idx,
                                                       int kk, float scale, float *__restrict__ o,
-                                                      float *__restrict__ lse, Geo g) {
+                                                      float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t head = ((int64_t)b * g.H + h) * (int64_t)g.N * 64;
   const int32_t *list = kv_idx + (((int64_t)b * g.H + h) * g.nt + i) * kk;
+  const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
+  const int64_t rhead = (int64_t)b * rv.sb + (int64_t)h * rv.sh;  // raster bytes of (b, 0, h)
+  // element index of (tiled row, channel) of Q/O (raster if RQ) or K (raster if RK)
+  auto at = [&](bool raster, int row, int c) -> int64_t {
+    if (!raster) return head + (int64_t)row * 64 + c;
+    const int64_t tok = tile_origin(row / 64, pt, ph, pw, g.Hs, g.Ws) + tile_intra(row % 64, ph, pw, g.Hs, g.Ws);
+    return (rhead + tok * rv.sn) / 4 + c;
+  };
   const int qrow = i * 64 + t;
   float qr[64], acc[64];
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    qr[c] = q[head + (int64_t)qrow * 64 + c];
+    qr[c] = q[at(RQ, qrow, c)];
     acc[c] = 0.f;
   }
   __shared__ float Ks[64][65];
@@ -197,7 +227,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
     __syncthreads();
     for (int e = t; e < 64 * 64; e += 64) {
       const int r = e >> 6, c = e & 63;
-      Ks[r][c] = k[head + ((int64_t)j * 64 + r) * 64 + c];  // row r = key, c = channel
+      Ks[r][c] = k[at(RK, j * 64 + r, c)];  // row r = key, c = channel
       Vs[cols_key(c)][r] = vt[head + ((int64_t)j * 64 + r) * 64 + c];  // channel-major: r = channel, c = position
     }
     __syncthreads();
@@ -216,18 +246,42 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
   }
   const float inv = 1.0f / l;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) o[head + (int64_t)qrow * 64 + c] = acc[c] * inv;
-  if (lse != nullptr) lse[((int64_t)b * g.H + h) * g.N + qrow] = m + logf(l);
+  for (int c = 0; c < 64; ++c) o[at(RQ, qrow, c)] = acc[c] * inv;
+  if (lse != nullptr) {
+    const int64_t pos = RQ ? tile_origin(i, pt, ph, pw, g.Hs, g.Ws) + tile_intra(t, ph, pw, g.Hs, g.Ws) : qrow;
+    lse[((int64_t)b * g.H + h) * g.N + pos] = m + logf(l);
+  }
+}
+
+template <bool RQ, bool RK>
+static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
+                          const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
+                          float *lse, hipStream_t st) {
+  if (dt == VEDA_BF16)
+    attn_bf16_kernel<RQ, RK><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs, rv);
+  else
+    attn_f32_kernel<RQ, RK><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
+                                                                 (const float *)v, kv_idx, kk, scale, (float *)o, lse,
+                                                                 g, hs, rv);
 }
 
 hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
                               const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st) {
-  if (dt == VEDA_BF16)
-    attn_bf16_kernel<<<dim3(g.nt * g.H * g.B), 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v,
-                                                             kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g);
+  launch_attn_t<false, false>(g, HeadShapes{}, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
+                                     bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
+                                     const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
+                                     hipStream_t st) {
+  const int64_t eb = dt == VEDA_BF16 ? 2 : 4;
+  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
+  if (k_raster)
+    launch_attn_t<true, true>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   else
-    attn_f32_kernel<<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, (const float *)v, kv_idx, kk, scale,
-                                         (float *)o, lse, g);
+    launch_attn_t<true, false>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 

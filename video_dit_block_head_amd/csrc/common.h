@@ -45,6 +45,25 @@ __device__ __forceinline__ int64_t tile_row_token(int j, int o, int pt, int ph, 
   return ((int64_t)(jt * pt + ot) * Hs + (jh * ph + oh)) * Ws + (jw * pw + ow);
 }
 
+// The same token as origin(j) + intra(o): the first is uniform over a tile, the second is
+// the same for row o of every tile of a head.
+__device__ __forceinline__ int64_t tile_origin(int j, int pt, int ph, int pw, int Hs, int Ws) {
+  const int ntw = Ws / pw, nth = Hs / ph;
+  const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
+  return ((int64_t)(jt * pt) * Hs + jh * ph) * Ws + jw * pw;
+}
+// ph and pw are powers of two (they divide the tile, 64 or 128 tokens).
+__device__ __forceinline__ int tile_intra(int o, int ph, int pw, int Hs, int Ws) {
+  const int lw = __builtin_ctz(pw), lh = __builtin_ctz(ph);
+  return ((o >> (lw + lh)) * Hs + ((o >> lw) & (ph - 1))) * Ws + (o & (pw - 1));
+}
+
+// Raster [B, N, H, d] tensor seen by a kernel: byte strides of batch, token and head (the
+// d elements of a token's head row are contiguous).
+struct RasterView {
+  int64_t sb, sn, sh;
+};
+
 // Channel-major tiles (VEDA_TILE_COLS) store, in each group of 16 consecutive positions,
 // the tile's tokens (keys) 0-3, 8-11, 4-7, 12-15 of that group: key at position p.  This is
 // the order in which the S^T accumulator of a 32x32 MFMA block reaches the k-slots of the
@@ -171,6 +190,20 @@ __device__ __forceinline__ void tile_dma_offsets(int w, int lane, uint32_t (&off
   for (int e = 0; e < 8; ++e) {
     const int r = 32 * w + 4 * e + (lane >> 4);
     off[e] = (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+  }
+}
+
+// The same copy from a raster tensor: row r of the tile is the token at intra(r) tokens
+// from the tile's origin, so the per-lane offsets are those of tile_dma_offsets with the
+// row's byte offset replaced by intra(row) * (token stride); the tile's origin goes into
+// the scalar base address.  Offsets stay below 4 GiB for every supported grid.
+__device__ __forceinline__ void tile_dma_offsets_raster(int w, int lane, int ph, int pw, int Hs, int Ws,
+                                                        int64_t sn, uint32_t (&off)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 32 * w + 4 * e + (lane >> 4);
+    const int chunk = (lane & 15) ^ (r & 15);
+    off[e] = (uint32_t)((int64_t)tile_intra(r, ph, pw, Hs, Ws) * sn + chunk * 16);
   }
 }
 

@@ -8,17 +8,20 @@ namespace veda {
 hipError_t launch_gather(const Geo &g, const HeadShapes &hs, veda_dtype dt, void *raster, int64_t rs_b,
                          int64_t rs_n, int64_t rs_h, void *tiled, veda_layout layout, int inverse, hipStream_t st);
 
-// Scoring: pool -> MLP -> scores / softmax / top-k.  ws layout: see score.hip.
+// Scoring: pool -> MLP -> scores / softmax / top-k.  ws layout: see score.hip.  With rv
+// (and hs) set, Q is a raster tensor read through each head's tiling, and K too if k_raster.
 size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out);
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
-                        void *ws, hipStream_t st);
+                        void *ws, hipStream_t st, const HeadShapes *hs = nullptr, const RasterView *rv = nullptr,
+                        bool k_raster = false);
 
 // TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL.
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
-                           float *k_desc, hipStream_t st);
+                           float *k_desc, hipStream_t st, const HeadShapes *hs = nullptr,
+                           const RasterView *rv = nullptr, bool k_raster = false);
 
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);
@@ -26,9 +29,17 @@ hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int
 hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
                               const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st);
 
+// Q and O in raster layout [B, N, H, d] (element strides rs_*), K raster or tile-major,
+// V channel-major tiled.
+hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
+                                     bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
+                                     const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
+                                     hipStream_t st);
+
 size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
-                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st);
+                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st,
+                          const HeadShapes *hs = nullptr, const RasterView *rv = nullptr, bool k_raster = false);
 
 // Distillation step (see distill.hip).
 size_t distill_workspace_bytes(const Geo &g, int n_sel);

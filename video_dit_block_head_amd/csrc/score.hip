@@ -44,12 +44,14 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 // EB: element bytes (2: bf16 with d = P = 128; 4: f32 with d = P = 64).  Rows are 256 bytes.
 static constexpr int PM_HST = 260;    // hidden block row stride (floats)
 
-template <int EB>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3))) pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
-                                                       const float *__restrict__ w1q, const float *__restrict__ w2q,
-                                                       const float *__restrict__ w1k, const float *__restrict__ w2k,
-                                                       float *__restrict__ y, float *__restrict__ qdesc,
-                                                       float *__restrict__ kdesc, Geo g) {
+// RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through each
+// head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
+template <int EB, bool RQ, bool RK>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
+pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
+                const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
+                float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, Geo g, HeadShapes hs,
+                RasterView rv) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
@@ -66,7 +68,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 
   // ---- TripPool: lane (rg = lane/16, c = lane%16) accumulates rows rg, rg + 4, ... of its
   // 16-byte channel chunk c; the 4 row groups are combined as (g0 + g1) + (g2 + g3).
-  const uint8_t *src0 = (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
+  const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
+  const bool rast = which ? RK : RQ;  // uniform over the workgroup
+  const uint8_t *src0 = rast ? (which ? k : q) + (int64_t)b * rv.sb + (int64_t)h * rv.sh
+                             : (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
   const int rg = lane >> 4, c = lane & 15;
 #pragma unroll 1
   for (int tt = 0; tt < 8; ++tt) {
@@ -79,29 +84,41 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
       mn[e] = INFINITY;
     }
     if (j < g.nt) {
-      const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
-      uint4 v[P / 4];
+      // raster rows: 32-bit offsets from the tile's origin, half a tile (16 loads) at a time
+      constexpr int NL = (RQ || RK) ? P / 8 : P / 4;
+#pragma unroll 1
+      for (int part = 0; part < P / 4 / NL; ++part) {
+        uint4 v[NL];
+        if ((RQ || RK) && rast) {
+          const uint8_t *src = src0 + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn + c * 16;
 #pragma unroll
-      for (int i = 0; i < P / 4; ++i) v[i] = load_stream16(src + (rg + 4 * i) * 256);
-#pragma unroll
-      for (int i = 0; i < P / 4; ++i) {
-        float x[EPC];
-        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        if (EB == 2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(wd[e] << 16);
-            x[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
-          }
+          for (int i = 0; i < NL; ++i)
+            v[i] = load_stream16(src + (uint32_t)(tile_intra(rg + 4 * (NL * part + i), ph, pw, g.Hs, g.Ws) * (int)rv.sn));
         } else {
+          const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
+          for (int i = 0; i < NL; ++i) v[i] = load_stream16(src + (rg + 4 * (NL * part + i)) * 256);
         }
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          s[e] += x[e];
-          mx[e] = fmaxf(mx[e], x[e]);
-          mn[e] = fminf(mn[e], x[e]);
+        for (int i = 0; i < NL; ++i) {
+          float x[EPC];
+          const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          if (EB == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = __uint_as_float(wd[e] << 16);
+              x[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            s[e] += x[e];
+            mx[e] = fmaxf(mx[e], x[e]);
+            mn[e] = fminf(mn[e], x[e]);
+          }
         }
       }
     }
@@ -335,27 +352,49 @@ static void launch_score_t(const Geo &g, const float *y, float scale, float *sco
                                                                                  idx);
 }
 
+template <int EB, bool RQ, bool RK>
+static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
+                              const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
+                              float *q_desc, float *k_desc, hipStream_t st) {
+  const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
+  pool_mlp_kernel<EB, RQ, RK><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y,
+                                                  q_desc, k_desc, g, hs, rv);
+}
+
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
-                           float *k_desc, hipStream_t st) {
-  const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
-  if (dt == VEDA_BF16)
-    pool_mlp_kernel<2><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
-                                           k_desc, g);
-  else
-    pool_mlp_kernel<4><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y, q_desc,
-                                           k_desc, g);
+                           float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
+                           bool k_raster) {
+  const HeadShapes hs0{};
+  const RasterView rv0{0, 0, 0};
+  const bool bf = dt == VEDA_BF16;
+  if (rv == nullptr) {
+    if (bf)
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+    else
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+  } else if (k_raster) {
+    if (bf)
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+    else
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+  } else {
+    if (bf)
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+    else
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
-                        void *ws, hipStream_t st) {
+                        void *ws, hipStream_t st, const HeadShapes *hs, const RasterView *rv, bool k_raster) {
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
-  launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+  launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster);
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, st);
   else if (g.nt <= 256)

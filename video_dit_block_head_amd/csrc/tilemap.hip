@@ -29,10 +29,13 @@ size_t tilemap_workspace_bytes(const Geo &g, int n_sel) {
 // read (half the LDS traffic per MFMA) and every K tile is copied once for both tiles.
 static constexpr int TM_QT = 2;
 
+// RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through the
+// head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
+template <bool RQ, bool RK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
                     const int32_t *__restrict__ q_tiles, int n_sel, float *__restrict__ out,
-                    float *__restrict__ lse_out, float *__restrict__ rowmax, Geo g) {
+                    float *__restrict__ lse_out, float *__restrict__ rowmax, Geo g, HeadShapes hs, RasterView rv) {
   const int ngrp = (n_sel + TM_QT - 1) / TM_QT;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int a0 = (L % ngrp) * TM_QT;
@@ -43,8 +46,15 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   const int a = min(a0 + qt, n_sel - 1);     // an odd tail repeats the last tile (not written twice)
   const bool owner = a0 + qt < n_sel;
   const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) : a;  // clamped
+  const int hh = (int)(bh % g.H), bb = (int)(bh / g.H);
+  const int pt = hs.s[hh][0], ph = hs.s[hh][1], pw = hs.s[hh][2];
+  const int64_t rhead = (int64_t)bb * rv.sb + (int64_t)hh * rv.sh;
   const __bf16 *qh = q + bh * (int64_t)g.N * 128;
-  const char *kh = reinterpret_cast<const char *>(k + bh * (int64_t)g.N * 128);
+  const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead
+                          : reinterpret_cast<const char *>(k + bh * (int64_t)g.N * 128);
+  auto k_tile = [&](int j) -> const char * {
+    return RK ? kh + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn : kh + (int64_t)j * 32768;
+  };
   float *rm = rowmax + (bh * n_sel + a) * (int64_t)g.nt * 128;   // [j][128 queries]
 
   __shared__ uint4 Kb[2][128 * 16];
@@ -53,9 +63,14 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   bf16x8_t qf[2][8];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t qrow = (int64_t)i * 128 + 64 * (w & 1) + 32 * qb + lr;
+    const int r = 64 * (w & 1) + 32 * qb + lr;
+    const __bf16 *qp =
+        RQ ? reinterpret_cast<const __bf16 *>(reinterpret_cast<const char *>(q) + rhead +
+                                                  (tile_origin(i, pt, ph, pw, g.Hs, g.Ws) +
+                                                   tile_intra(r, ph, pw, g.Hs, g.Ws)) * rv.sn)
+               : qh + ((int64_t)i * 128 + r) * 128;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8_t *>(qh + qrow * 128 + 16 * s + 8 * hi);
+    for (int s = 0; s < 8; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
   }
   asm volatile("" ::"v"(qf[0][0]), "v"(qf[0][1]), "v"(qf[0][2]), "v"(qf[0][3]), "v"(qf[0][4]), "v"(qf[0][5]),
                "v"(qf[0][6]), "v"(qf[0][7]));
@@ -63,10 +78,13 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
                "v"(qf[1][6]), "v"(qf[1][7]));
 
   uint32_t off[8];
-  tile_dma_offsets(w, lane, off);
+  if (RK)
+    tile_dma_offsets_raster(w, lane, ph, pw, g.Hs, g.Ws, rv.sn, off);
+  else
+    tile_dma_offsets(w, lane, off);
   const uint32_t kb_lds[2] = {lds_addr(Kb[0]), lds_addr(Kb[1])};
-  tile_to_lds(kh, kb_lds[0], w, off);
-  if (g.nt > 1) tile_to_lds(kh + 32768, kb_lds[1], w, off);
+  tile_to_lds(k_tile(0), kb_lds[0], w, off);
+  if (g.nt > 1) tile_to_lds(k_tile(1), kb_lds[1], w, off);
 
   float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
   for (int j = 0; j < g.nt; ++j) {
@@ -95,7 +113,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     }
     wait_lds();
     barrier();  // every wave has read this buffer
-    if (j + 2 < g.nt) tile_to_lds(kh + (int64_t)(j + 2) * 32768, kb_lds[buf], w, off);
+    if (j + 2 < g.nt) tile_to_lds(k_tile(j + 2), kb_lds[buf], w, off);
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -147,16 +165,27 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row.
+template <bool RQ, bool RK>
 __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                          float scale, const int32_t *__restrict__ q_tiles, int n_sel,
-                                                         float *__restrict__ out, float *__restrict__ lse_out, Geo g) {
+                                                         float *__restrict__ out, float *__restrict__ lse_out, Geo g,
+                                                         HeadShapes hs, RasterView rv) {
   const int a = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t bh = (int64_t)b * g.H + h;
   const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) : a;
   const float *qh = q + bh * (int64_t)g.N * 64, *kh = k + bh * (int64_t)g.N * 64;
+  const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
+  const int64_t rhead = (int64_t)b * rv.sb + (int64_t)h * rv.sh;
+  // element index of (tiled row, channel) of Q or K in either layout
+  auto at = [&](bool raster, int row, int c) -> int64_t {
+    if (!raster) return (int64_t)row * 64 + c;
+    const int64_t tok = tile_origin(row / 64, pt, ph, pw, g.Hs, g.Ws) + tile_intra(row % 64, ph, pw, g.Hs, g.Ws);
+    return (rhead + tok * rv.sn) / 4 + c;
+  };
+  const float *qb = RQ ? q : qh, *kb = RK ? k : kh;
   float qr[64];
 #pragma unroll
-  for (int c = 0; c < 64; ++c) qr[c] = qh[(int64_t)(i * 64 + t) * 64 + c];
+  for (int c = 0; c < 64; ++c) qr[c] = qb[at(RQ, i * 64 + t, c)];
   __shared__ float Ks[64][65];
   __shared__ float wm[TM_MAX_NT];
   float m = -1e30f, l = 0.f;
@@ -164,7 +193,7 @@ __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict
     const float lse = m + logf(l);
     for (int j = 0; j < g.nt; ++j) {
       __syncthreads();
-      for (int e = t; e < 64 * 64; e += 64) Ks[e >> 6][e & 63] = kh[((int64_t)j * 64 + (e >> 6)) * 64 + (e & 63)];
+      for (int e = t; e < 64 * 64; e += 64) Ks[e >> 6][e & 63] = kb[at(RK, j * 64 + (e >> 6), e & 63)];
       __syncthreads();
       float tmax = -1e30f;
       for (int x = 0; x < 64; ++x) {
@@ -191,14 +220,28 @@ __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict
   for (int j = t; j < g.nt; j += 64) out[(bh * n_sel + a) * (int64_t)g.nt + j] = expf(wm[j]);
 }
 
-hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
-                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st) {
+template <bool RQ, bool RK>
+static void launch_tilemap_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
+                             const void *k, float scale, const int32_t *q_tiles, int n_sel, float *tilemap,
+                             float *lse, void *ws, hipStream_t st) {
   if (dt == VEDA_BF16)
-    tilemap_bf16_kernel<<<dim3(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B), 256, 0, st>>>(
-        (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g);
+    tilemap_bf16_kernel<RQ, RK><<<dim3(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B), 256, 0, st>>>(
+        (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
   else
-    tilemap_f32_kernel<<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale, q_tiles,
-                                                             n_sel, tilemap, lse, g);
+    tilemap_f32_kernel<RQ, RK><<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale,
+                                                                     q_tiles, n_sel, tilemap, lse, g, hs, rv);
+}
+
+hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
+                          const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st,
+                          const HeadShapes *hs, const RasterView *rv, bool k_raster) {
+  if (rv == nullptr)
+    launch_tilemap_t<false, false>(g, HeadShapes{}, RasterView{0, 0, 0}, dt, q, k, scale, q_tiles, n_sel, tilemap,
+                                   lse, ws, st);
+  else if (k_raster)
+    launch_tilemap_t<true, true>(g, *hs, *rv, dt, q, k, scale, q_tiles, n_sel, tilemap, lse, ws, st);
+  else
+    launch_tilemap_t<true, false>(g, *hs, *rv, dt, q, k, scale, q_tiles, n_sel, tilemap, lse, ws, st);
   return hipGetLastError();
 }
 

@@ -8,9 +8,10 @@ import math
 
 import torch
 
-from . import (COLS, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
-               veda_oracle_tilemap, veda_oracle_tilemap_workspace_bytes, veda_sparse_attn_fwd, veda_tile_gather,
-               veda_trippool_score, veda_trippool_workspace_bytes)
+from . import (COLS, RASTER, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
+               veda_oracle_tilemap, veda_oracle_tilemap_raster, veda_oracle_tilemap_workspace_bytes,
+               veda_sparse_attn_fwd, veda_sparse_attn_fwd_raster, veda_tile_gather, veda_trippool_score,
+               veda_trippool_score_raster, veda_trippool_workspace_bytes)
 
 
 class SparseAttention:
@@ -90,6 +91,47 @@ class SparseAttention:
         veda_distill_step(self.geom, self.q_t, self.k_t, self.w1, self.w2, q_tiles, target, loss, dw1, dw2,
                           score_scale=self.score_scale, lr=lr, workspace=self._tm_ws[key])
         return loss, dw1, dw2
+
+    # ---- raster-direct path: Q and O stay in the raster layout.  K is read raster (pass k)
+    # or from its tiled copy (k=None: gather_kv first); V is always tiled.
+    def gather_kv(self, k, v):
+        veda_tile_gather(self.geom, k, self.k_t, ROWS)
+        veda_tile_gather(self.geom, v, self.v_t, COLS)
+
+    def gather_v(self, v):
+        veda_tile_gather(self.geom, v, self.v_t, COLS)
+
+    def _k(self, k):
+        return (self.k_t, ROWS) if k is None else (k, RASTER)
+
+    def score_raster(self, q, topk, k=None, scores=None, probs=None, q_desc=None, k_desc=None):
+        idx = self.idx_buffer(topk) if topk > 0 else None
+        kt, lay = self._k(k)
+        veda_trippool_score_raster(self.geom, q, kt, self.w1, self.w2, self.w1_k, self.w2_k, self.score_scale,
+                                   scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc, topk=topk, idx=idx,
+                                   workspace=self.ws, k_layout=lay)
+        return idx
+
+    def attend_raster(self, q, idx, out, lse=None, k=None):
+        kt, lay = self._k(k)
+        veda_sparse_attn_fwd_raster(self.geom, q, kt, self.v_t, idx, int(idx.shape[-1]), self.softmax_scale, out,
+                                    lse, k_layout=lay)
+        return out
+
+    def tilemap_raster(self, q, q_tiles, n_sel, out, lse=None, k=None):
+        if n_sel not in self._tm_ws:
+            nbytes = veda_oracle_tilemap_workspace_bytes(self.geom, n_sel)
+            self._tm_ws[n_sel] = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        kt, lay = self._k(k)
+        veda_oracle_tilemap_raster(self.geom, q, kt, self.softmax_scale, q_tiles, n_sel, out, lse,
+                                   self._tm_ws[n_sel], k_layout=lay)
+        return out
+
+    def forward_raster(self, q, k, v, topk, out):
+        """Same result as forward(), without the tiled copies of Q and O."""
+        self.gather_kv(k, v)
+        idx = self.score_raster(q, topk)
+        return self.attend_raster(q, idx, out)
 
     def forward(self, q, k, v, topk, out):
         self.gather(q, k, v)
