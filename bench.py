@@ -267,11 +267,12 @@ def main():
         distill_ms = e0.elapsed_time(e1) / reps
         err = torch.empty((B, H), dtype=torch.float32, device="cuda")
         ref = torch.empty_like(err)
-        V.veda_head_sq_error(out, q, err, ref)
+        hws = torch.empty(V.veda_head_sq_error_workspace_bytes(B, N, H), dtype=torch.uint8, device="cuda")
+        V.veda_head_sq_error(out, q, err, ref, workspace=hws)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
-            V.veda_head_sq_error(out, q, err, ref)
+            V.veda_head_sq_error(out, q, err, ref, workspace=hws)
         e1.record()
         torch.cuda.synchronize()
         herr_ms = e0.elapsed_time(e1) / reps

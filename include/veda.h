@@ -219,11 +219,17 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
  *         size a multiple of 16 bytes), e.g. a sparse output and the dense output
  *   err:    out [B, H] f32, err[b, h] = sum over tokens n and channels c of (a - b)^2
  *   ref_sq: out [B, H] f32, sum of b^2 (for relative errors), nullable
+ *   workspace: device scratch of >= veda_head_sq_error_workspace_bytes(B, N, H) bytes,
+ *         8-byte aligned, caller-owned (one partial pair per head and token chunk)
  * fp32 accumulation in a fixed order (deterministic).  The shapes only need N >= 1;
- * veda_geom is not used because the error does not depend on the tiling. */
+ * veda_geom is not used because the error does not depend on the tiling.  Errors:
+ * VEDA_ERR_WORKSPACE when the workspace is missing or short; VEDA_ERR_UNSUPPORTED when one
+ * token chunk holds 2^31 or more 16-byte pieces. */
+size_t veda_head_sq_error_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t heads);
 veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim,
                                veda_dtype dtype, const void *a, const void *b, float *err,
-                               float *ref_sq, hipStream_t stream);
+                               float *ref_sq, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 const char *veda_status_str(veda_status s);
 int veda_last_hip_error(void);

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 17, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -139,12 +139,19 @@ def test_binding_fails_loudly_without_gpu_tensors():
 
 def test_head_error_validation(L):
     f = L.veda_head_sq_error
-    assert f(1, 16, 2, 128, 7, A, B_, A, None, None) == DTYPE
-    assert f(0, 16, 2, 128, V.BF16, A, B_, A, None, None) == SHAPE
-    assert f(1, 16, 2, 12, V.BF16, A, B_, A, None, None) == SHAPE     # 24-byte rows
-    assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, None) == NULL
-    assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, None) == NULL
-    assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, None) == ALIGN
+    wsb = L.veda_head_sq_error_workspace_bytes(1, 16, 2)
+    assert wsb == 1 * 2 * 1 * 8                                      # one chunk of 16 tokens per head
+    assert L.veda_head_sq_error_workspace_bytes(2, 76800, 40) == 2 * 40 * 256 * 8
+    assert L.veda_head_sq_error_workspace_bytes(0, 16, 2) == 0
+    W = (A, wsb)
+    assert f(1, 16, 2, 128, 7, A, B_, A, None, *W, None) == DTYPE
+    assert f(0, 16, 2, 128, V.BF16, A, B_, A, None, *W, None) == SHAPE
+    assert f(1, 16, 2, 12, V.BF16, A, B_, A, None, *W, None) == SHAPE     # 24-byte rows
+    assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, *W, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, *W, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, *W, None) == ALIGN
+    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, None, wsb, None) == WS
+    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, A, wsb - 1, None) == WS
 
 
 def test_raster_validation(L):

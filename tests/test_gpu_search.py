@@ -25,23 +25,27 @@ def say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_head_sq_error_exact_sum(dtype):
-    say(f"[gpu-search] head error {dtype}")
+@pytest.mark.parametrize("dtype,B,N,H", [(torch.bfloat16, 2, 777, 5), (torch.float32, 2, 777, 5),
+                                         (torch.bfloat16, 1, 70001, 3)])
+def test_head_sq_error_exact_sum(dtype, B, N, H):
+    """Chunked partial sums against the float64 sum: 4 ragged chunks per head at N = 777,
+    the 256-chunk maximum (273-274 tokens each) at N = 70001."""
+    say(f"[gpu-search] head error {dtype} B={B} N={N} H={H}")
     g = torch.Generator().manual_seed(3)
-    B, N, H, d = 2, 777, 5, 128 if dtype == torch.bfloat16 else 64
+    d = 128 if dtype == torch.bfloat16 else 64
     a = torch.randn(B, N, H, d, generator=g).to(dtype)
     b = torch.randn(B, N, H, d, generator=g).to(dtype)
     err = torch.empty(B, H, device="cuda")
     ref = torch.empty(B, H, device="cuda")
-    V.veda_head_sq_error(a.cuda(), b.cuda(), err, ref)
+    ws = torch.empty(V.veda_head_sq_error_workspace_bytes(B, N, H), dtype=torch.uint8, device="cuda")
+    V.veda_head_sq_error(a.cuda(), b.cuda(), err, ref, workspace=ws)
     torch.cuda.synchronize()
     a64, b64 = a.double().numpy(), b.double().numpy()
     want = ((a64 - b64) ** 2).sum(axis=(1, 3))
     want_ref = (b64 ** 2).sum(axis=(1, 3))
     assert np.allclose(err.cpu().numpy(), want, rtol=1e-5, atol=0)
     assert np.allclose(ref.cpu().numpy(), want_ref, rtol=1e-5, atol=0)
-    # deterministic
+    # deterministic, also through a workspace the binding allocates
     err2 = torch.empty_like(err)
     V.veda_head_sq_error(a.cuda(), b.cuda(), err2)
     assert torch.equal(err, err2)

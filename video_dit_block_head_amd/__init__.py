@@ -75,7 +75,8 @@ def lib():
             "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]),
             "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
-            "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "veda_head_sq_error_workspace_bytes": (sz, [i32, i32, i32]),
+            "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
                                                  vp, vp, vp, vp, i32, vp, vp, sz, vp]),
@@ -190,14 +191,26 @@ def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, t
         ws_bytes, _stream(stream)))
 
 
-def veda_head_sq_error(a, b, err, ref_sq=None, stream=None):
+def veda_head_sq_error_workspace_bytes(batch, n_tokens, heads):
+    return int(lib().veda_head_sq_error_workspace_bytes(int(batch), int(n_tokens), int(heads)))
+
+
+def veda_head_sq_error(a, b, err, ref_sq=None, workspace=None, stream=None):
     """a, b: contiguous raster [B, N, H, d] tensors of one dtype; err (and ref_sq): [B, H]
-    float32, written with sum (a - b)^2 (and sum b^2) per (batch, head)."""
+    float32, written with sum (a - b)^2 (and sum b^2) per (batch, head).  workspace: a device
+    buffer of at least veda_head_sq_error_workspace_bytes(B, N, H) bytes; allocated on a's
+    device when None."""
     if a.shape != b.shape or a.dtype != b.dtype or a.dim() != 4:
         raise VedaError("a and b must be [B, N, H, d] tensors of one shape and dtype")
     B, N, H, d = (int(x) for x in a.shape)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(1, veda_head_sq_error_workspace_bytes(B, N, H)), dtype=torch.uint8,
+                                device=a.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("veda_head_sq_error", lib().veda_head_sq_error(
-        B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), _p(err, "err"), _p(ref_sq, "ref_sq"), _stream(stream)))
+        B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), _p(err, "err"), _p(ref_sq, "ref_sq"),
+        _p(workspace, "workspace"), ws_bytes, _stream(stream)))
 
 
 def veda_distill_workspace_bytes(geom, n_sel):

@@ -286,8 +286,14 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
                                    dw1, dw2, lr, workspace, stream));
 }
 
+size_t veda_head_sq_error_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t heads) {
+  if (batch < 1 || n_tokens < 1 || heads < 1) return 0;
+  return (size_t)batch * heads * head_sq_error_chunks(n_tokens) * 2 * sizeof(float);
+}
+
 veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim, veda_dtype dtype,
-                               const void *a, const void *b, float *err, float *ref_sq, hipStream_t stream) {
+                               const void *a, const void *b, float *err, float *ref_sq, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
   if (dtype != VEDA_F32 && dtype != VEDA_BF16) return VEDA_ERR_DTYPE;
   if (batch < 1 || n_tokens < 1 || heads < 1 || head_dim < 1 || batch > 65535 || heads > 65535)
     return VEDA_ERR_SHAPE;
@@ -295,9 +301,15 @@ veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, i
   if (((int64_t)head_dim * eb) % 16 != 0) return VEDA_ERR_SHAPE;
   if (!a || !b || !err) return VEDA_ERR_NULL;
   if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(err) & 3u) ||
-      (reinterpret_cast<uintptr_t>(ref_sq) & 3u))
+      (reinterpret_cast<uintptr_t>(ref_sq) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
     return VEDA_ERR_ALIGN;
-  return hip_status(launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, ref_sq, stream));
+  // one chunk's 16-byte pieces are counted in 32 bits
+  const int64_t chunk_rows = ((int64_t)n_tokens + head_sq_error_chunks(n_tokens) - 1) / head_sq_error_chunks(n_tokens);
+  if (chunk_rows * ((int64_t)head_dim * eb / 16) >= (int64_t)1 << 31) return VEDA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < veda_head_sq_error_workspace_bytes(batch, n_tokens, heads))
+    return VEDA_ERR_WORKSPACE;
+  return hip_status(
+      launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, ref_sq, workspace, stream));
 }
 
 const char *veda_status_str(veda_status s) {

@@ -47,7 +47,8 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
                           float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
                           float *dw1, float *dw2, float lr, void *ws, hipStream_t st);
 
+int head_sq_error_chunks(int n_tokens);  // token chunks per head (one partial pair each)
 hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,
-                                const void *b, float *err, float *ref_sq, hipStream_t st);
+                                const void *b, float *err, float *ref_sq, void *ws, hipStream_t st);
 
 }  // namespace veda

@@ -9,6 +9,7 @@ import math
 import torch
 
 from . import (COLS, RASTER, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
+               veda_head_sq_error_workspace_bytes,
                veda_oracle_tilemap, veda_oracle_tilemap_raster, veda_oracle_tilemap_workspace_bytes,
                veda_sparse_attn_fwd, veda_sparse_attn_fwd_raster, veda_tile_gather, veda_trippool_score,
                veda_trippool_score_raster, veda_trippool_workspace_bytes)
@@ -172,11 +173,12 @@ def search_tile_shapes(grid, tile, candidates, q, k, v, w1, w2, topk, score_scal
     sa.attend(dense_index(sa.geom, device))
     sa.scatter(full)
     out = torch.empty_like(q)
+    ws = torch.empty(veda_head_sq_error_workspace_bytes(B, N, H), dtype=torch.uint8, device=device)
     for ci, shape in enumerate(candidates):
         sa = SparseAttention(Geom(B, H, d, grid, tile, [tuple(shape)] * H), dt, w1, w2, score_scale=score_scale,
                              softmax_scale=softmax_scale, device=device)
         sa.forward(q, k, v, topk, out)
-        veda_head_sq_error(out, full, err[ci], ref if ci == 0 else None)
+        veda_head_sq_error(out, full, err[ci], ref if ci == 0 else None, workspace=ws)
     total = err.sum(dim=1).cpu()
     choice = [int(torch.argmin(total[:, h]).item()) for h in range(H)]
     return choice, err, ref
