@@ -107,10 +107,14 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ?
 // keys, ties to the lower index, ascending, to idx[0..k); optional 0/1 mask[0..n_cols).
 // The k-th largest key is found bit by bit (largest T with count(key >= T) >= k), starting
 // below the bits that every valid key of the row shares, and stopping as soon as exactly k
-// keys are >= the candidate (that set is then the answer, whatever lies below).
+// keys are >= the candidate (that set is then the answer, whatever lies below).  Every later
+// candidate exceeds T, so only keys >= T can still be counted: once at most 128 of them are
+// left they are compacted (through `scratch`, 128 words of the wave's own LDS) into two
+// registers per lane, and the remaining bits cost two ballots instead of MAXM.
 template <int MAXM>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_cols, int k, int lane,
-                                          int32_t *__restrict__ idx, uint8_t *__restrict__ mask) {
+                                          int32_t *__restrict__ idx, uint8_t *__restrict__ mask,
+                                          uint32_t *scratch) {
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) {
@@ -125,24 +129,52 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_col
   kmax = __builtin_amdgcn_readfirstlane(kmax);
   kmin = __builtin_amdgcn_readfirstlane(kmin);
   const uint32_t diff = kmax ^ kmin;
+  const uint64_t lt = lanemask_lt(lane);
   uint32_t T = kmax;  // every valid key equal: T is the k-th largest already
   if (diff != 0u) {
     const int b0 = 31 - __builtin_clz(diff);
     T = b0 == 31 ? 0u : (kmax & ~((2u << b0) - 1u));
-    for (int b = b0; b >= 0; --b) {
+    // keys >= T: all valid keys (they share T's bits), and the padding too when T = 0
+    int alive = T != 0u ? n_cols : 64 * MAXM;
+    bool done = false;
+    int b = b0;
+    for (; b >= 0 && (MAXM <= 2 || alive > 128); --b) {
       const uint32_t cand = T | (1u << b);
       int cnt = 0;
 #pragma unroll
       for (int m = 0; m < MAXM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
-      if (cnt >= k) T = cand;
-      if (cnt == k) break;
+      if (cnt >= k) {
+        T = cand;
+        alive = cnt;
+      }
+      if (cnt == k) {
+        done = true;
+        break;
+      }
+    }
+    if (MAXM > 2 && !done && b >= 0) {
+      int base = 0;
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m) {
+        const bool a = key[m] >= T;
+        const uint64_t am = __ballot(a);
+        if (a) scratch[base + __popcll(am & lt)] = key[m];  // base + rank < alive <= 128
+        base += __popcll(am);
+      }
+      // padding 0 is never counted: every candidate is >= 1
+      const uint32_t c0 = lane < base ? scratch[lane] : 0u, c1 = 64 + lane < base ? scratch[64 + lane] : 0u;
+      for (; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int cnt = __popcll(__ballot(c0 >= cand)) + __popcll(__ballot(c1 >= cand));
+        if (cnt >= k) T = cand;
+        if (cnt == k) break;
+      }
     }
   }
   int n_gt = 0;
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) n_gt += __popcll(__ballot(key[m] > T));
   const int need = k - n_gt;
-  const uint64_t lt = lanemask_lt(lane);
   int base = 0, ties = 0;
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) {

@@ -302,7 +302,8 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
   const int d3 = 3 * g.d;
   const size_t desc_half = (size_t)g.B * g.H * g.nt * d3;
   // forward: descriptors and MLP outputs of every Q and K tile (shared weights)
-  launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st);
+  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st);
+  if (pe != hipSuccess) return pe;
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
   const float inv_rows = 1.0f / (float)rows;
   if (g.nt <= 64)

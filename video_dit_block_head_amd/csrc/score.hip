@@ -323,7 +323,8 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
       uint32_t key[MAXM];
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nt) ? float_key(sc[mm]) : 0u;
-      wave_topk<MAXM>(key, nt, topk, lane, idx + grow * topk, nullptr);
+      // the row is in registers now: its LDS words serve as the wave's top-k scratch
+      wave_topk<MAXM>(key, nt, topk, lane, idx + grow * topk, nullptr, reinterpret_cast<uint32_t *>(&S[row * SW]));
     }
   }
 }
@@ -331,6 +332,7 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
 template <int MAXM>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ scores, int64_t rows, int n_cols, int k,
                                                    int32_t *__restrict__ idx, uint8_t *__restrict__ mask) {
+  __shared__ uint32_t tk_scratch[4][128];  // per wave
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave
@@ -341,7 +343,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
     const int j = 64 * m + lane;
     key[m] = (j < n_cols) ? float_key(src[j]) : 0u;
   }
-  wave_topk<MAXM>(key, n_cols, k, lane, idx + row * k, mask ? mask + row * n_cols : nullptr);
+  wave_topk<MAXM>(key, n_cols, k, lane, idx + row * k, mask ? mask + row * n_cols : nullptr, tk_scratch[threadIdx.x >> 6]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -394,7 +396,8 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
-  launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster);
+  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster);
+  if (pe != hipSuccess) return pe;
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, st);
   else if (g.nt <= 256)
