@@ -51,30 +51,65 @@ def tile_permutation(grid, shape):
     return tok.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
 
 
+def tile_slots(grid, shape):
+    """Head-aware tiling for any tile shape: slots[r] = raster token index held by row r of
+    the tile-major sequence, or -1 for a slot of the padded grid that holds no token.
+
+    The grid is padded up to whole tiles on every axis (T' = ceil(T/p_t)*p_t, etc.); tiles
+    of the padded grid and rows inside a tile are numbered row-major as in
+    tile_permutation, and a slot is padding when its (t, h, w) lies outside the real grid.
+    Every tile keeps at least one real token.  For a dividing shape this is
+    tile_permutation.  Pinned: hand-derived fixture, explicit-loop construction, each real
+    token exactly once.
+    """
+    T, H, W = grid
+    pt, ph, pw = shape
+    nT, nH, nW = -(-T // pt), -(-H // ph), -(-W // pw)
+    t = np.arange(nT * pt)[:, None, None]
+    h = np.arange(nH * ph)[None, :, None]
+    w = np.arange(nW * pw)[None, None, :]
+    tok = np.where((t < T) & (h < H) & (w < W), (t * H + h) * W + w, -1)
+    return tok.reshape(nT, pt, nH, ph, nW, pw).transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+
+
 def to_tiles(x, perm):
-    """Rows of the raster-ordered [N, d] array x, in tile-major order."""
-    return np.asarray(x, dtype=np.float64)[perm]
+    """Rows of the raster-ordered [N, d] array x, in tile-major order; slots marked -1
+    (padding of tile_slots) are zero rows."""
+    x = np.asarray(x, dtype=np.float64)
+    perm = np.asarray(perm)
+    out = np.zeros((len(perm),) + x.shape[1:])
+    real = perm >= 0
+    out[real] = x[perm[real]]
+    return out
 
 
-def from_tiles(xt, perm):
-    """Inverse of to_tiles."""
+def from_tiles(xt, perm, n=None):
+    """Inverse of to_tiles: the rows of the real slots back in raster order ([n, d], n =
+    the number of real slots by default)."""
     xt = np.asarray(xt, dtype=np.float64)
-    out = np.empty_like(xt)
-    out[perm] = xt
+    perm = np.asarray(perm)
+    real = perm >= 0
+    out = np.empty((int(real.sum()) if n is None else n,) + xt.shape[1:])
+    out[perm[real]] = xt[real]
     return out
 
 
 # ---------------------------------------------------------------------------
 # Distilled tile scoring  [Veda Technical Summary, §2.1 Distilled Tile Scoring]
 # ---------------------------------------------------------------------------
-def trippool(xt, P):
+def trippool(xt, P, valid=None):
     """TripPool descriptor of each tile: [mean | max | min] over the tile's P tokens, per
     channel, concatenated (§2.1, "Statistic-Aware Estimator").  [n_t, 3d].
-    Pinned: brute-force loops, hand fixture, constant tile."""
+    valid (bool per tile-major row, e.g. tile_slots(...) >= 0): only the real tokens of a
+    padded tile count.  Pinned: brute-force loops, hand fixture, constant tile."""
     xt = np.asarray(xt, dtype=np.float64)
     n_t = xt.shape[0] // P
     t = xt.reshape(n_t, P, xt.shape[1])
-    return np.concatenate([t.mean(axis=1), t.max(axis=1), t.min(axis=1)], axis=1)
+    if valid is None:
+        return np.concatenate([t.mean(axis=1), t.max(axis=1), t.min(axis=1)], axis=1)
+    v = np.asarray(valid, bool).reshape(n_t, P, 1)
+    mean = np.where(v, t, 0.0).sum(axis=1) / v.sum(axis=1)
+    return np.concatenate([mean, np.where(v, t, -np.inf).max(axis=1), np.where(v, t, np.inf).min(axis=1)], axis=1)
 
 
 def gelu(x):
@@ -140,14 +175,16 @@ def dense_attention(q, k, v, scale, return_lse=False):
     return (p @ v, lse) if return_lse else p @ v
 
 
-def sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
+def sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False, key_valid=None):
     """Tile-skipping attention on tile-major rows: query tile i attends only to the keys of
     the tiles idx[i, :], with the softmax renormalised over those keys.
 
     qt, kt, vt: [N, d]; idx: [n_t, k] (row i = kept key tiles of query tile i).
+    key_valid (bool per tile-major row): padding keys of a padded tiling take no weight.
     Returns [len(q_tiles) * P, d] for the query tiles listed (default: all), and the
-    natural-log LSE per query row if asked.  Pinned: 100%-kept equals dense attention,
-    explicit -inf mask on the full matrix, constant V, Q = 0.
+    natural-log LSE per query row if asked.  Pinned: 100%-kept equals dense attention (also
+    over the real tokens of a padded tiling), explicit -inf mask on the full matrix,
+    constant V, Q = 0.
     """
     qt, kt, vt = (np.asarray(a, np.float64) for a in (qt, kt, vt))
     n_t = qt.shape[0] // P
@@ -157,7 +194,10 @@ def sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
     off = np.arange(P)
     for a, i in enumerate(q_tiles):
         rows = (np.asarray(idx[i])[:, None] * P + off[None, :]).ravel()
-        p, lse = _softmax_rows_with_lse((qt[i * P:(i + 1) * P] @ kt[rows].T) * float(scale))
+        s = (qt[i * P:(i + 1) * P] @ kt[rows].T) * float(scale)
+        if key_valid is not None:
+            s = np.where(np.asarray(key_valid, bool)[rows][None, :], s, -np.inf)
+        p, lse = _softmax_rows_with_lse(s)
         out[a * P:(a + 1) * P] = p @ vt[rows]
         lses[a * P:(a + 1) * P] = lse
     return (out, lses) if return_lse else out
@@ -168,20 +208,28 @@ def sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False):
 # full-attention matrix over query-key tile regions; §2.3: heatmaps built in two passes on
 # random subsets of query tiles]
 # ---------------------------------------------------------------------------
-def tilemap(qt, kt, P, scale, q_tiles=None):
+def tilemap(qt, kt, P, scale, q_tiles=None, key_valid=None, query_valid=None):
     """M[a, j] = max over q in query tile q_tiles[a], key in tile j, of the full-attention
     probability softmax_row(q k^T * scale).  First the per-row log-sum-exp over all N keys,
     then the max over each region of exp(s - lse).  [len(q_tiles), n_t].
-    Pinned: Q = 0 gives 1/N, explicit dense-P max-pool, 1/N <= row max <= 1."""
+    key_valid / query_valid (bool per tile-major row): on a padded tiling, padding keys
+    take no probability and padding query rows are left out of the max.
+    Pinned: Q = 0 gives 1/N, explicit dense-P max-pool (also on a padded tiling),
+    1/N <= row max <= 1."""
     qt, kt = np.asarray(qt, np.float64), np.asarray(kt, np.float64)
     n_t = kt.shape[0] // P
     q_tiles = np.arange(qt.shape[0] // P) if q_tiles is None else np.asarray(q_tiles)
     out = np.empty((len(q_tiles), n_t))
     for a, i in enumerate(q_tiles):
         s = (qt[i * P:(i + 1) * P] @ kt.T) * float(scale)          # [P, N]
+        if key_valid is not None:
+            s = np.where(np.asarray(key_valid, bool)[None, :], s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))  # pass 1
-        out[a] = np.exp(s - lse).reshape(P, n_t, P).max(axis=(0, 2))  # pass 2
+        p = np.exp(s - lse)                                          # pass 2
+        if query_valid is not None:
+            p = np.where(np.asarray(query_valid, bool)[i * P:(i + 1) * P, None], p, -np.inf)
+        out[a] = p.reshape(P, n_t, P).max(axis=(0, 2))
     return out
 
 

@@ -221,6 +221,40 @@ def distill_grads_no_dyk(descs, w1, w2, q_tiles, targets, score_scale):
     return total / rows, g1, g2
 
 
+def slots_wraparound(grid, shape):
+    T, H, W = grid
+    pt, ph, pw = shape
+    nT, nH, nW = -(-T // pt), -(-H // ph), -(-W // pw)
+    t = np.arange(nT * pt)[:, None, None] % T
+    h = np.arange(nH * ph)[None, :, None] % H
+    w = np.arange(nW * pw)[None, None, :] % W
+    tok = (t * H + h) * W + w                                   # padding wraps to real tokens
+    return tok.reshape(nT, pt, nH, ph, nW, pw).transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+
+
+def trippool_padded_mean_over_p(xt, P, valid=None):
+    t = np.asarray(xt, np.float64).reshape(-1, P, xt.shape[1])
+    v = np.ones(t.shape[:2] + (1,), bool) if valid is None else np.asarray(valid, bool).reshape(-1, P, 1)
+    return np.concatenate([np.where(v, t, 0).sum(1) / P, np.where(v, t, -np.inf).max(1),
+                           np.where(v, t, np.inf).min(1)], 1)
+
+
+def trippool_padded_unmasked(xt, P, valid=None):
+    return O.trippool(xt, P)                                    # padding rows (zeros) counted
+
+
+def sparse_ignores_key_mask(qt, kt, vt, idx, P, scale, q_tiles=None, return_lse=False, key_valid=None):
+    return O.sparse_attention(qt, kt, vt, idx, P, scale, q_tiles, return_lse)
+
+
+def tilemap_ignores_key_mask(qt, kt, P, scale, q_tiles=None, key_valid=None, query_valid=None):
+    return O.tilemap(qt, kt, P, scale, q_tiles, None, query_valid)
+
+
+def tilemap_ignores_query_mask(qt, kt, P, scale, q_tiles=None, key_valid=None, query_valid=None):
+    return O.tilemap(qt, kt, P, scale, q_tiles, key_valid, None)
+
+
 MUTANTS = [
     ("perm: in-tile axes swapped", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_swapped_inner]),
     ("perm: tile order reversed", [pins.pin_perm_golden, pins.pin_perm_loops], [perm_tile_order_colmajor]),
@@ -249,6 +283,12 @@ MUTANTS = [
     ("distill: gradient sign", [pins.pin_distill_fd], [distill_grads_sign]),
     ("distill: key-tile path dropped", [pins.pin_distill_fd], [distill_grads_no_dyk]),
     ("search: output left tile-major", [pins.pin_search_block_local, pins.pin_search_all_kept], [search_no_untiling]),
+    ("slots: padding wraps around", [pins.pin_slots_golden, pins.pin_slots_loops], [slots_wraparound]),
+    ("trippool padded: mean over P", [pins.pin_trippool_padded_loops], [trippool_padded_mean_over_p]),
+    ("trippool padded: padding counted", [pins.pin_trippool_padded_loops], [trippool_padded_unmasked]),
+    ("sparse padded: padding keys kept", [pins.pin_sparse_padded_full_equals_dense], [sparse_ignores_key_mask]),
+    ("tilemap padded: padding keys kept", [pins.pin_tilemap_padded_bruteforce], [tilemap_ignores_key_mask]),
+    ("tilemap padded: padding queries pooled", [pins.pin_tilemap_padded_bruteforce], [tilemap_ignores_query_mask]),
 ]
 
 

@@ -374,6 +374,137 @@ def test_tilemap_zero_q_and_bounds():
     assert np.all(m <= 1.0 + 1e-15) and np.all(m.max(axis=1) >= 1.0 / (P * n_t))
 
 
+# ------------------------------------------------------------------ padded tiling (shapes that do not divide the grid)
+PADDED_CASES = [((3, 2, 3), (2, 2, 2)), ((20, 8, 12), (8, 4, 4)), ((5, 6, 7), (2, 4, 2)), ((40, 4, 8), (16, 2, 4)),
+                ((4, 8, 8), (4, 4, 4))]
+
+
+def pin_slots_golden(tile_slots):
+    tagged, rows = read_golden("slots_padded.txt")
+    grid = tuple(int(x) for x in tagged["grid"][0])
+    shape = tuple(int(x) for x in tagged["shape"][0])
+    slots = tile_slots(grid, shape)
+    assert len(slots) == len(rows)
+    for r, n in rows:
+        assert slots[int(r)] == int(n), (r, slots[int(r)], n)
+
+
+def slots_by_loops(grid, shape):
+    """Explicit construction on the padded grid: tiles row-major, rows row-major inside a
+    tile, -1 where (t, h, w) is outside the real grid."""
+    T, H, W = grid
+    pt, ph, pw = shape
+    out = []
+    for a in range(-(-T // pt)):
+        for b in range(-(-H // ph)):
+            for c in range(-(-W // pw)):
+                for i in range(pt):
+                    for j in range(ph):
+                        for l in range(pw):
+                            t, h, w = a * pt + i, b * ph + j, c * pw + l
+                            out.append((t * H + h) * W + w if (t < T and h < H and w < W) else -1)
+    return np.array(out)
+
+
+def pin_slots_loops(tile_slots):
+    for grid, shape in PADDED_CASES:
+        slots = tile_slots(grid, shape)
+        assert np.array_equal(slots, slots_by_loops(grid, shape)), (grid, shape)
+        n = grid[0] * grid[1] * grid[2]
+        assert np.array_equal(np.sort(slots[slots >= 0]), np.arange(n))     # each real token once
+        P = shape[0] * shape[1] * shape[2]
+        assert np.all((slots.reshape(-1, P) >= 0).any(axis=1))              # no all-padding tile
+
+
+def pin_trippool_padded_loops(trippool):
+    rng = np.random.default_rng(21)
+    for grid, shape in [((5, 6, 7), (2, 4, 2)), ((3, 2, 3), (2, 2, 2))]:
+        P = shape[0] * shape[1] * shape[2]
+        n, d = grid[0] * grid[1] * grid[2], 5
+        x = rng.standard_normal((n, d)) - 2.0            # all below zero: a padding zero would show in max
+        slots = O.tile_slots(grid, shape)
+        got = trippool(O.to_tiles(x, slots), P, valid=slots >= 0)
+        for j in range(len(slots) // P):
+            toks = [slots[j * P + r] for r in range(P) if slots[j * P + r] >= 0]
+            for c in range(d):
+                vals = [x[t, c] for t in toks]
+                assert math.isclose(got[j, c], sum(vals) / len(vals), rel_tol=1e-13, abs_tol=1e-13)
+                assert got[j, d + c] == max(vals)
+                assert got[j, 2 * d + c] == min(vals)
+
+
+def pin_sparse_padded_full_equals_dense(sparse_attention):
+    """All tiles kept on a padded tiling = dense attention over the real tokens."""
+    rng = np.random.default_rng(22)
+    for grid, shape in [((3, 5, 6), (2, 2, 2)), ((5, 6, 7), (2, 4, 2))]:
+        P = shape[0] * shape[1] * shape[2]
+        n, d = grid[0] * grid[1] * grid[2], 8
+        q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+        slots = O.tile_slots(grid, shape)
+        n_t = len(slots) // P
+        idx = np.tile(np.arange(n_t), (n_t, 1))
+        qt, kt, vt = (O.to_tiles(a, slots) for a in (q, k, v))
+        out_t, lse_t = sparse_attention(qt, kt, vt, idx, P, 0.3, return_lse=True, key_valid=slots >= 0)
+        ref, lse = O.dense_attention(q, k, v, 0.3, return_lse=True)
+        assert np.allclose(O.from_tiles(out_t, slots, n), ref, rtol=1e-12, atol=1e-13)
+        real = slots >= 0
+        assert np.allclose(lse_t[real], lse[slots[real]], rtol=1e-13)
+
+
+def pin_tilemap_padded_bruteforce(tilemap):
+    rng = np.random.default_rng(23)
+    grid, shape = (3, 4, 5), (2, 2, 2)
+    P, n, d = 8, 60, 8
+    q, k = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    s = (q @ k.T) * 0.5
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)                    # over the real keys only
+    slots = O.tile_slots(grid, shape)
+    n_t = len(slots) // P
+    sel = [n_t - 1, 0, 3]
+    got = tilemap(O.to_tiles(q, slots), O.to_tiles(k, slots), P, 0.5, q_tiles=sel, key_valid=slots >= 0,
+                  query_valid=slots >= 0)
+    for a, i in enumerate(sel):
+        for j in range(n_t):
+            best = max(p[slots[i * P + r], slots[j * P + c]] for r in range(P) for c in range(P)
+                       if slots[i * P + r] >= 0 and slots[j * P + c] >= 0)
+            assert math.isclose(got[a, j], best, rel_tol=1e-12)
+
+
+def test_slots_golden():
+    pin_slots_golden(O.tile_slots)
+
+
+def test_slots_loops():
+    pin_slots_loops(O.tile_slots)
+
+
+def test_slots_dividing_is_permutation():
+    for grid, shape in [((8, 16, 32), (2, 8, 8)), ((4, 8, 8), (4, 4, 4))]:
+        assert np.array_equal(O.tile_slots(grid, shape), O.tile_permutation(grid, shape))
+
+
+def test_padded_roundtrip():
+    rng = np.random.default_rng(24)
+    slots = O.tile_slots((5, 6, 7), (2, 4, 2))
+    x = rng.standard_normal((210, 3))
+    xt = O.to_tiles(x, slots)
+    assert np.all(xt[slots < 0] == 0.0)
+    assert np.array_equal(O.from_tiles(xt, slots, 210), x)
+
+
+def test_trippool_padded_loops():
+    pin_trippool_padded_loops(O.trippool)
+
+
+def test_sparse_padded_full_equals_dense():
+    pin_sparse_padded_full_equals_dense(O.sparse_attention)
+
+
+def test_tilemap_padded_bruteforce():
+    pin_tilemap_padded_bruteforce(O.tilemap)
+
+
 # ------------------------------------------------------------------ tiling search
 SEARCH_GRID, SEARCH_P, SEARCH_D = (4, 8, 8), 64, 64
 SEARCH_CANDIDATES = [(4, 4, 4), (1, 8, 8), (2, 4, 8)]
