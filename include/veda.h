@@ -23,7 +23,8 @@
  *    head_dim 128 and tile 128.  Scores, descriptors, weights, LSEs and maps are float32.
  *  - Stateless and thread-safe (apart from the per-thread last-error slot).
  *
- * Tiled layouts (per batch b and head h, N = t*h*w tokens, P = tile, n_t = N / P):
+ * Tiled layouts (per batch b and head h, N = t*h*w tokens, P = tile, n_t = N / P; for
+ * padded tilings see below):
  *  - VEDA_TILE_ROWS: [B, H, N, d]; row r holds token perm_h[r] of the raster sequence,
  *    where tile r / P is numbered row-major over the tile grid (t/p_t, h/p_h, w/p_w) and
  *    r % P row-major over (p_t, p_h, p_w).  Q, K and the attention output use it.
@@ -35,6 +36,22 @@
  *    fragments meet V in the MFMA, so every V operand is one contiguous 16-byte read.
  * The raster layout is [B, N, H, d] with any element strides for b, n, h and d contiguous;
  * raster token n = (t*H + h)*W + w.
+ *
+ * Padded tilings (bf16, tiled calls only).  A head's shape (p_t, p_h, p_w) need not divide
+ * the grid: the grid is then padded up to whole tiles on every axis for that head, giving
+ * n_t(h) = ceil(t/p_t) * ceil(h/p_h) * ceil(w/p_w) tiles, some of them partial; a row of
+ * the padded grid outside the real grid is a padding row and holds no token.  Reading of
+ * [Technical Summary §2.2 Head-Aware Tiling], whose tiles are blocks of the latent grid.
+ *  - Tiled tensors then have N = n_t * P rows per head with n_t = max_h n_t(h)
+ *    (veda_tiled_tokens); rows past a head's own tiles and padding rows are zero after
+ *    the gather and skipped by the scatter.
+ *  - TripPool pools only a tile's real rows; attention and the tile map give padding
+ *    keys no weight; padding query rows produce values that the scatter drops.
+ *  - Scores, top-k lists and maps have n_t columns per row; a head uses its first n_t(h)
+ *    (top-k and maps never pick or fill the others: scores -inf, probabilities and map
+ *    entries 0).  k must not exceed the smallest n_t(h).
+ *  - The raster-direct calls, veda_distill_step and VEDA_F32 return VEDA_ERR_UNSUPPORTED
+ *    for such a geometry; veda_oracle_tilemap needs an explicit q_tiles list.
  */
 #ifndef VEDA_H
 #define VEDA_H
@@ -51,8 +68,8 @@ typedef int32_t veda_status;
 enum {
   VEDA_OK = 0,
   VEDA_ERR_NULL = -1,        /* a required pointer is NULL */
-  VEDA_ERR_SHAPE = -2,       /* sizes inconsistent: tile shape product != tile, shape not
-                                dividing the grid, k out of range, too many heads ... */
+  VEDA_ERR_SHAPE = -2,       /* sizes inconsistent: tile shape product != tile, k out of
+                                range, too many heads ... */
   VEDA_ERR_DTYPE = -3,       /* unknown element type */
   VEDA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim/tile for this dtype) */
   VEDA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes query */
@@ -69,11 +86,19 @@ typedef enum { VEDA_TILE_ROWS = 0, VEDA_TILE_COLS = 1, VEDA_RASTER = 2 } veda_la
  * pi = (p_t, p_h, p_w) factorises the hardware tile.] */
 typedef struct {
   int32_t batch, heads, head_dim;  /* B, H (<= VEDA_MAX_HEADS), d */
-  int32_t t, h, w;                 /* latent grid; N = t*h*w, a multiple of tile */
+  int32_t t, h, w;                 /* latent grid */
   int32_t tile;                    /* P tokens per tile */
   const int32_t *tile_shapes;      /* HOST int32[heads][3] (p_t, p_h, p_w); each product
-                                      == tile and each entry divides (t, h, w) */
+                                      == tile; a shape that does not divide (t, h, w)
+                                      makes the tiling padded (see above) */
 } veda_geom;
+
+/* Tokens per head of the tiled layouts (N = n_t * P; t*h*w unless the tiling is padded),
+ * or a negative veda_status when the geometry is rejected. */
+int64_t veda_tiled_tokens(const veda_geom *g, veda_dtype dtype);
+
+/* Tiles of one head, n_t(h) (n_t unless the tiling is padded), or a negative status. */
+int32_t veda_head_tiles(const veda_geom *g, veda_dtype dtype, int32_t head);
 
 /* Head-aware tiling (permutation of tokens into per-head tiles).
  * [Technical Summary §2.2 Head-Aware Tiling]

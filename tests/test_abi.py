@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 19, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -54,6 +54,41 @@ def gather(L, g, dt=V.BF16, raster=A, tiled=B_, strides=(4096 * 2 * 128, 2 * 128
     return L.veda_tile_gather(g.ref if g is not None else None, dt, raster, *strides, tiled, layout, inverse, None)
 
 
+def test_padded_tile_counts(L):
+    """Tiles per head on the grid padded up to whole tiles, and the tiled rows per head."""
+    g = geom(grid=(20, 48, 80), shapes=((8, 4, 4), (2, 8, 8), (1, 8, 16)))
+    assert [L.veda_head_tiles(g.ref, V.BF16, h) for h in range(3)] == [3 * 12 * 20, 600, 600]
+    assert L.veda_tiled_tokens(g.ref, V.BF16) == 720 * 128
+    assert [g.head_tiles(h) for h in range(3)] == [720, 600, 600] and g.padded and g.n_tiled == 720 * 128
+    g = geom(grid=(8, 16, 31), shapes=((1, 8, 16),))          # w = 31: two tiles of 16 along w
+    assert L.veda_head_tiles(g.ref, V.BF16, 0) == 8 * 2 * 2 and L.veda_tiled_tokens(g.ref, V.BF16) == 32 * 128
+    g = geom()
+    assert L.veda_tiled_tokens(g.ref, V.BF16) == 4096 and not g.padded and g.n_tiled == g.n_tokens
+    assert L.veda_head_tiles(g.ref, V.BF16, 2) == SHAPE
+    assert L.veda_tiled_tokens(geom(d=64).ref, V.BF16) == UNSUP
+    assert L.veda_tiled_tokens(geom(d=64, tile=64, grid=(20, 8, 8), shapes=((8, 4, 2),)).ref, V.F32) == UNSUP
+
+
+def test_padded_rejected_where_unsupported(L):
+    """A padded tiling goes through the tiled calls only: the raster-direct calls, the
+    distillation step and the all-tiles tile map refuse it before launching anything."""
+    g = geom(grid=(20, 16, 32), shapes=((8, 4, 4), (2, 8, 8)))
+    n_t = g.n_tiles                                           # 3 * 4 * 8 = 96 > 80 (dividing head)
+    st = (g.n_tokens * 2 * 128, 2 * 128, 128)
+    RAS, big = V.RASTER, 1 << 40
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, 4, 0.088, A, None, None) == UNSUP
+    assert L.veda_trippool_score_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None,
+                                        None, 6, A, A, big, None) == UNSUP
+    assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, RAS, *st, 0.088, A, 4, A, None, A, big, None) == UNSUP
+    assert L.veda_distill_step(g.ref, V.BF16, A, A, A, A, 256, 64, 0.125, A, 4, A, A, A, A, 0.0, A, big,
+                               None) == UNSUP
+    assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, 0.088, None, n_t, A, None, A, big, None) == SHAPE
+    # k may not exceed the smallest per-head tile count (80 here)
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, A, 81, 0.088, A, None, None) == SHAPE
+    assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, 81, A, A,
+                                 big, None) == SHAPE
+
+
 def test_gather_validation(L):
     assert gather(L, None) == NULL
     assert gather(L, geom(), raster=None) == NULL
@@ -61,8 +96,8 @@ def test_gather_validation(L):
     assert gather(L, geom(d=64)) == UNSUP                      # bf16 needs d = 128
     assert gather(L, geom(d=128, tile=64, shapes=((1, 8, 8),) * 2), dt=V.F32) == UNSUP
     assert gather(L, geom(shapes=((2, 8, 4), (2, 8, 8)))) == SHAPE    # product != tile
-    assert gather(L, geom(grid=(20, 48, 80), shapes=((8, 4, 4),))) == SHAPE   # 8 does not divide 20
-    assert gather(L, geom(grid=(8, 16, 31), shapes=((1, 8, 16),))) == SHAPE  # N not a multiple of 128
+    # padded tilings (a shape that does not divide the grid) are bf16-only
+    assert gather(L, geom(d=64, tile=64, grid=(20, 8, 8), shapes=((8, 4, 2),)), dt=V.F32) == UNSUP
     assert gather(L, geom(), raster=MIS) == ALIGN
     assert gather(L, geom(), strides=(4096 * 256, 260, 128)) == ALIGN
     assert gather(L, geom(), layout=1, inverse=1) == UNSUP

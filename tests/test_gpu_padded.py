@@ -1,0 +1,224 @@
+"""GPU parity on padded tilings: per-head tile shapes that do not divide the latent grid,
+so that the grid is padded up to whole tiles per head (n_t(h) tiles, some of them partial).
+
+Each check compares the tiled path of the C ABI with the oracle's padded tiling
+(tile_slots, TripPool over real rows, attention and tile map with padding keys masked),
+on the workloads' own shape cycles: (8,4,4) on T = 20 (mid, large) and (16,2,4) on T = 40
+(long), plus a small grid on which every listed shape but two divides.  Tolerances as in
+test_gpu_parity: layout bit-exact; max/min bit-exact, mean 1e-6; scores 2e-5 and indices
+exact outside the 1e-5 near-tie band; attention max-abs 2e-2 and relative Frobenius 1e-2;
+tile map 1e-3 in log space.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.veda_oracle as O
+from workloads import SHAPES_128, get, make, padded_variant
+
+pytestmark = pytest.mark.gpu
+
+V = pytest.importorskip("video_dit_block_head_amd")
+from video_dit_block_head_amd.pipeline import SparseAttention  # noqa: E402
+
+CASES = {
+    # 20 x 16 x 32: (8,4,4) gives 3*4*8 = 96 tiles and (16,2,4) 2*8*8 = 128, the others 80
+    "small-padded": (padded_variant(get(1), name="small-padded", grid=(20, 16, 32), heads=5,
+                                    shape_list=tuple(SHAPES_128) + ((16, 2, 4),), topk=(16,), seed=11,
+                                    sampled_q_tiles=24), None, None),
+    "mid-padded": (padded_variant(get(2), sampled_q_tiles=32), 3, 16),
+    "large-padded": (padded_variant(get(3), topk=(60,)), 2, 8),
+    "long-padded": (padded_variant(get(4), topk=(120,)), 2, 4),
+}
+# Position -> key order inside a channel-major tile: groups of 16 ordered 0-3, 8-11, 4-7, 12-15
+COLS_KEY = np.array([16 * (p // 16) + [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15][p % 16]
+                     for p in range(128)])
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_raster(arr_hm):
+    t = torch.from_numpy(arr_hm.view(np.int16)).cuda().view(torch.bfloat16)
+    return t.permute(0, 2, 1, 3).contiguous()
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def bitwise_equal(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+class PaddedRun:
+    def __init__(self, name):
+        cfg, self.n_heads, self.n_tiles_checked = CASES[name]
+        self.cfg = cfg
+        say(f"[gpu-padded] {name}: generating")
+        wl = self.wl = make(cfg)
+        B, H, d, P = cfg.batch, cfg.heads, cfg.head_dim, cfg.tile
+        self.geom = V.Geom(B, H, d, cfg.grid, P, wl.shapes)
+        assert self.geom.padded
+        self.nt = nt = self.geom.n_tiles
+        self.kk = cfg.topk[0]
+        say(f"[gpu-padded] {name}: n_t per head {sorted(set(self.geom.head_tiles(h) for h in range(H)))}, "
+            f"k={self.kk}")
+        self.sa = SparseAttention(self.geom, torch.bfloat16, torch.from_numpy(wl.w1), torch.from_numpy(wl.w2),
+                                  score_scale=cfg.score_scale)
+        self.q, self.k, self.v = (to_dev_raster(a) for a in (wl.q, wl.k, wl.v))
+        self.sa.gather(self.q, self.k, self.v)
+        self.scores = torch.empty((B, H, nt, nt), dtype=torch.float32, device="cuda")
+        self.qd = torch.empty((B, H, nt, 3 * d), dtype=torch.float32, device="cuda")
+        self.kd = torch.empty_like(self.qd)
+        self.idx = self.sa.score(self.kk, scores=self.scores, q_desc=self.qd, k_desc=self.kd)
+        self.lse = torch.empty((B, H, self.geom.n_tiled), dtype=torch.float32, device="cuda")
+        self.sa.attend(self.idx, self.lse)
+        self.out = torch.empty_like(self.q)
+        self.sa.scatter(self.out)
+        torch.cuda.synchronize()
+        say(f"[gpu-padded] {name}: GPU path done")
+        self._oh = {}
+
+    def heads(self):
+        """The heads whose shape does not divide the grid, and head 0."""
+        T, Hh, W = self.cfg.grid
+        pad = [h for h, (pt, ph, pw) in enumerate(self.wl.shapes) if T % pt or Hh % ph or W % pw]
+        hs = sorted(set([0] + pad))
+        return hs if self.n_heads is None else [0] + pad[:self.n_heads - 1]
+
+    def oracle_head(self, b, h):
+        if (b, h) not in self._oh:
+            self._oh.clear()
+            slots = O.tile_slots(self.cfg.grid, self.wl.shapes[h])
+            self._oh[(b, h)] = tuple(O.to_tiles(self.wl.head(w, b, h), slots) for w in ("q", "k", "v")) + (slots,)
+        return self._oh[(b, h)]
+
+    def q_tiles(self, h):
+        t = self.wl.sample_tiles(h)
+        if self.n_tiles_checked is not None:
+            t = t[np.linspace(0, len(t) - 1, self.n_tiles_checked).astype(int)]
+        return t
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def r(request):
+    run = PaddedRun(request.param)
+    yield run
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_padded_gather(r):
+    cfg, P, d = r.cfg, r.cfg.tile, r.cfg.head_dim
+    for h in r.heads():
+        qt, kt, vt, slots = r.oracle_head(0, h)
+        n = len(slots)
+        gq, gk = host(r.sa.q_t[0, h]), host(r.sa.k_t[0, h])
+        assert bitwise_equal(gq[:n], qt) and bitwise_equal(gk[:n], kt), (cfg.name, h)
+        assert not gq[n:].any() and not gk[n:].any(), (cfg.name, h, "rows past the head's tiles")
+        ntile = n // P
+        vcols = host(r.sa.v_t[0, h]).reshape(r.nt, d, P).transpose(0, 2, 1)[:ntile]
+        assert bitwise_equal(vcols, vt.reshape(ntile, P, d)[:, COLS_KEY[:P], :]), (cfg.name, h, "v")
+    back = torch.empty_like(r.q)
+    V.veda_tile_gather(r.geom, back, r.sa.q_t, V.ROWS, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), r.q.view(torch.int16))
+
+
+def test_padded_descriptors(r):
+    cfg, P, d = r.cfg, r.cfg.tile, r.cfg.head_dim
+    for h in r.heads():
+        qt, kt, _, slots = r.oracle_head(0, h)
+        ntile = len(slots) // P
+        for x, gd in ((qt, r.qd), (kt, r.kd)):
+            ref = O.trippool(x, P, valid=slots >= 0)
+            got = host(gd[0, h])[:ntile]
+            assert bitwise_equal(got[:, d:], ref[:, d:]), (cfg.name, h)
+            err = np.abs(got[:, :d] - ref[:, :d]) / np.maximum(np.abs(ref[:, :d]), 1.0)
+            assert err.max() <= 1e-6, (cfg.name, h, err.max())
+
+
+def test_padded_scores_topk(r):
+    cfg, P = r.cfg, r.cfg.tile
+    worst, exempt, rows = 0.0, 0, 0
+    for h in r.heads():
+        qt, kt, _, slots = r.oracle_head(0, h)
+        valid = slots >= 0
+        ntile = len(slots) // P
+        yq = O.mlp(O.trippool(qt, P, valid=valid), r.wl.w1[h], r.wl.w2[h])
+        yk = O.mlp(O.trippool(kt, P, valid=valid), r.wl.w1[h], r.wl.w2[h])
+        s = O.tile_scores(yq, yk, cfg.score_scale)
+        gs = host(r.scores[0, h])
+        worst = max(worst, float(np.abs(gs[:ntile, :ntile] - s).max()))
+        assert np.all(np.isneginf(gs[:ntile, ntile:])), (cfg.name, h, "columns past the head's tiles")
+        idx = host(r.idx[0, h]).astype(np.int64)
+        s32 = s.astype(np.float32)
+        for i in range(ntile):
+            ok, ex = O.topk_agrees(s32[i], idx[i], r.kk)
+            assert ok, (cfg.name, h, i, idx[i])
+            exempt += ex
+            rows += 1
+    say(f"[gpu-padded] {cfg.name}: score max|err| {worst:.3g}, {exempt}/{rows} rows in the near-tie band")
+    assert worst <= 2e-5
+
+
+def test_padded_attention(r):
+    cfg, P = r.cfg, r.cfg.tile
+    scale = 1 / math.sqrt(cfg.head_dim)
+    num = den = mx = lse_err = 0.0
+    for h in r.heads():
+        qt, kt, vt, slots = r.oracle_head(0, h)
+        tiles = r.q_tiles(h)
+        idx = host(r.idx[0, h]).astype(np.int64)
+        ref, ref_lse = O.sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=tiles, return_lse=True,
+                                          key_valid=slots >= 0)
+        rows = (tiles[:, None] * P + np.arange(P)[None]).ravel()
+        real = slots[rows] >= 0                               # padding query rows carry no token
+        got = host(r.sa.o_t[0, h])[rows][real]
+        ref = ref[real]
+        num += float(((got - ref) ** 2).sum())
+        den += float((ref ** 2).sum())
+        mx = max(mx, float(np.abs(got - ref).max()))
+        lse_err = max(lse_err, float(np.abs(host(r.lse[0, h])[rows][real] - ref_lse[real]).max()))
+        # the raster output is the tiled output scattered through the slots
+        sl = slots[slots >= 0]
+        assert bitwise_equal(host(r.out[0, :, h])[sl], host(r.sa.o_t[0, h])[:len(slots)][slots >= 0]), (cfg.name, h)
+    rel = math.sqrt(num / den)
+    say(f"[gpu-padded] {cfg.name} k={r.kk}: max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
+    assert mx <= 2e-2 and rel <= 1e-2 and lse_err <= 4e-3
+
+
+def test_padded_tilemap(r):
+    cfg, P = r.cfg, r.cfg.tile
+    B, H = cfg.batch, cfg.heads
+    n_sel = cfg.sampled_q_tiles
+    qtl = torch.from_numpy(np.stack([r.wl.sample_tiles(h) for h in range(H)]).astype(np.int32)[None]
+                           .repeat(B, 0)).cuda()
+    tm = torch.empty((B, H, n_sel, r.nt), dtype=torch.float32, device="cuda")
+    say(f"[gpu-padded] {cfg.name}: tile map, {n_sel} query tiles per head")
+    r.sa.tilemap(qtl, n_sel, tm)
+    torch.cuda.synchronize()
+    tmh = host(tm)
+    worst = 0.0
+    n_check = 4 if r.n_tiles_checked is not None else n_sel
+    for h in r.heads():
+        qt, kt, _, slots = r.oracle_head(0, h)
+        ntile = len(slots) // P
+        sel = np.linspace(0, n_sel - 1, n_check).astype(int)
+        ref = O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=r.wl.sample_tiles(h)[sel],
+                        key_valid=slots >= 0, query_valid=slots >= 0)
+        got = tmh[0, h, sel]
+        assert not got[:, ntile:].any(), (cfg.name, h, "columns past the head's tiles")
+        got = got[:, :ntile]
+        keep = ref >= 1e-30
+        assert np.all(got[~keep] < 1e-25)
+        worst = max(worst, float(np.abs(np.log(got[keep]) - np.log(ref[keep])).max()))
+    say(f"[gpu-padded] {cfg.name}: tile map max|dlog M| {worst:.3g}")
+    assert worst <= 1e-3

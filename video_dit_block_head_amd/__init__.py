@@ -43,11 +43,31 @@ class Geom:
 
     @property
     def n_tokens(self):
+        """Real tokens of the latent grid (raster layout)."""
         return self.grid[0] * self.grid[1] * self.grid[2]
+
+    def head_tiles(self, h):
+        """Tiles of head h on the grid padded up to whole tiles (n_tokens / tile unless the
+        head's shape does not divide the grid)."""
+        (T, H, W), (pt, ph, pw) = self.grid, self.shapes[h]
+        return (-(-T // pt)) * (-(-H // ph)) * (-(-W // pw))
+
+    @property
+    def padded(self):
+        """Some head's tile shape does not divide the grid."""
+        T, H, W = self.grid
+        return any(T % pt or H % ph or W % pw for pt, ph, pw in self.shapes)
 
     @property
     def n_tiles(self):
-        return self.n_tokens // self.tile
+        """Tiles per head of the tiled layouts and of score / index rows (the largest
+        head_tiles; n_tokens / tile unless padded)."""
+        return max(self.head_tiles(h) for h in range(self.heads))
+
+    @property
+    def n_tiled(self):
+        """Rows per head of the tiled layouts."""
+        return self.n_tiles * self.tile
 
     @property
     def ref(self):
@@ -86,6 +106,8 @@ def lib():
                                                  vp]),
             "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
                                         vp]),
+            "veda_tiled_tokens": (i64, [G, i32]),
+            "veda_head_tiles": (i32, [G, i32, i32]),
             "veda_status_str": (ctypes.c_char_p, [i32]),
             "veda_last_hip_error": (ctypes.c_int, []),
             "veda_version": (ctypes.c_char_p, []),
@@ -189,6 +211,21 @@ def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, t
         geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), float(softmax_scale),
         _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
         ws_bytes, _stream(stream)))
+
+
+def veda_tiled_tokens(geom, dtype_code):
+    """Rows per head of the tiled layouts, as the library computes them."""
+    n = int(lib().veda_tiled_tokens(geom.ref, int(dtype_code)))
+    if n < 0:
+        _check("veda_tiled_tokens", n)
+    return n
+
+
+def veda_head_tiles(geom, dtype_code, head):
+    n = int(lib().veda_head_tiles(geom.ref, int(dtype_code), int(head)))
+    if n < 0:
+        _check("veda_head_tiles", n)
+    return n
 
 
 def veda_head_sq_error_workspace_bytes(batch, n_tokens, heads):

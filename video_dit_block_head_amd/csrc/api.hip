@@ -1,5 +1,6 @@
 // C ABI of the library: argument validation (before anything is launched), status codes,
 // and dispatch to the kernel launchers.  No exception crosses this boundary.
+#include <stdint.h>
 #include <string.h>
 
 #include "common.h"
@@ -11,8 +12,10 @@ static thread_local int g_last_hip_error = 0;
 
 namespace {
 
-constexpr int SCORE_MAX_NT = 1280;  // fused score kernel holds a row of <= 1280 scores in registers
-constexpr int TILEMAP_MAX_NT = 1280;
+constexpr int SCORE_MAX_NT = 1536;  // the score kernel holds a row of <= 1536 scores in registers
+constexpr int DISTILL_MAX_NT = 1280;
+constexpr int TILEMAP_MAX_NT_F32 = 1280;  // the fp32 tile map keeps one row of maxima in LDS
+constexpr int TILEMAP_MAX_NT = 1536;
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,15 +25,32 @@ veda_status hip_status(hipError_t e) {
   return VEDA_ERR_HIP;
 }
 
-// Validates the geometry and dtype; fills Geo and per-head shapes.
-veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *hs) {
+// Tiles of every head on the grid padded up to whole tiles: the largest and smallest count,
+// and whether some shape does not divide the grid.  Shapes are assumed valid.
+void tile_counts(const veda_geom *g, int *nt_max, int *nt_min, bool *padded) {
+  *nt_max = 0;
+  *nt_min = INT32_MAX;
+  *padded = false;
+  for (int h = 0; h < g->heads; ++h) {
+    const int pt = g->tile_shapes[3 * h], ph = g->tile_shapes[3 * h + 1], pw = g->tile_shapes[3 * h + 2];
+    const int n = head_tiles(pt, ph, pw, g->t, g->h, g->w);
+    *nt_max = n > *nt_max ? n : *nt_max;
+    *nt_min = n < *nt_min ? n : *nt_min;
+    *padded = *padded || g->t % pt || g->h % ph || g->w % pw;
+  }
+}
+
+// Validates the geometry and dtype; fills Geo and per-head shapes.  Shapes that do not
+// divide the grid pad it up to whole tiles per head (bf16 only); nt_min (optional) receives
+// the smallest per-head tile count.
+veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *hs, int *nt_min = nullptr) {
   if (g == nullptr || g->tile_shapes == nullptr) return VEDA_ERR_NULL;
   if (dt != VEDA_F32 && dt != VEDA_BF16) return VEDA_ERR_DTYPE;
   if (g->batch < 1 || g->heads < 1 || g->heads > VEDA_MAX_HEADS || g->t < 1 || g->h < 1 || g->w < 1 ||
       g->tile < 1 || g->head_dim < 1)
     return VEDA_ERR_SHAPE;
   const int64_t n = (int64_t)g->t * g->h * g->w;
-  if (n > (int64_t)1 << 30 || n % g->tile != 0) return VEDA_ERR_SHAPE;
+  if (n > (int64_t)1 << 30) return VEDA_ERR_SHAPE;
   if (dt == VEDA_BF16 && !(g->head_dim == 128 && g->tile == 128)) return VEDA_ERR_UNSUPPORTED;
   if (dt == VEDA_F32 && !(g->head_dim == 64 && g->tile == 64)) return VEDA_ERR_UNSUPPORTED;
   memset(hs, 0, sizeof(*hs));
@@ -38,11 +58,15 @@ veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *
     const int32_t pt = g->tile_shapes[3 * h], ph = g->tile_shapes[3 * h + 1], pw = g->tile_shapes[3 * h + 2];
     if (pt < 1 || ph < 1 || pw < 1) return VEDA_ERR_SHAPE;
     if ((int64_t)pt * ph * pw != g->tile) return VEDA_ERR_SHAPE;
-    if (g->t % pt || g->h % ph || g->w % pw) return VEDA_ERR_SHAPE;
     hs->s[h][0] = pt;
     hs->s[h][1] = ph;
     hs->s[h][2] = pw;
   }
+  int nt_max, nt_lo;
+  bool padded;
+  tile_counts(g, &nt_max, &nt_lo, &padded);
+  if ((int64_t)nt_max * g->tile > (int64_t)1 << 30) return VEDA_ERR_SHAPE;
+  if (padded && dt != VEDA_BF16) return VEDA_ERR_UNSUPPORTED;
   out->B = g->batch;
   out->H = g->heads;
   out->d = g->head_dim;
@@ -50,9 +74,23 @@ veda_status check_geom(const veda_geom *g, veda_dtype dt, Geo *out, HeadShapes *
   out->Hs = g->h;
   out->Ws = g->w;
   out->P = g->tile;
-  out->N = (int32_t)n;
-  out->nt = (int32_t)(n / g->tile);
+  out->N = nt_max * g->tile;  // tiled tokens per head (= t*h*w unless padded)
+  out->nt = nt_max;
+  out->padded = padded ? 1 : 0;
+  if (nt_min != nullptr) *nt_min = nt_lo;
   return VEDA_OK;
+}
+
+// Tile count used to size buffers, from the geometry alone (0 when it is unusable).
+int geom_tiles(const veda_geom *g) {
+  if (g == nullptr || g->tile < 1 || g->heads < 1 || g->heads > VEDA_MAX_HEADS) return 0;
+  if (g->tile_shapes == nullptr) return (int)((int64_t)g->t * g->h * g->w / g->tile);
+  for (int h = 0; h < g->heads; ++h)
+    if (g->tile_shapes[3 * h] < 1 || g->tile_shapes[3 * h + 1] < 1 || g->tile_shapes[3 * h + 2] < 1) return 0;
+  int nt_max, nt_min;
+  bool padded;
+  tile_counts(g, &nt_max, &nt_min, &padded);
+  return nt_max;
 }
 
 // Raster operands read through the tilings: 16-byte aligned rows and strides, and every
@@ -98,7 +136,8 @@ size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int
   geo.B = g->batch;
   geo.H = g->heads;
   geo.d = g->head_dim;
-  geo.nt = (int32_t)(n / g->tile);
+  (void)n;
+  geo.nt = geom_tiles(g);
   return score_workspace_bytes(geo, mlp_hidden, mlp_out);
 }
 
@@ -109,12 +148,13 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void
                                 size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
-  veda_status s = check_geom(g, dtype, &geo, &hs);
+  int nt_min;
+  veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
   if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
   if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
-  if (topk < 0 || topk > geo.nt) return VEDA_ERR_SHAPE;
+  if (topk < 0 || topk > nt_min) return VEDA_ERR_SHAPE;
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
@@ -123,7 +163,7 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
   return hip_status(launch_score(geo, dtype, q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
-                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream));
+                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs));
 }
 
 veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
@@ -148,6 +188,7 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
   const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
@@ -172,14 +213,15 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
                                  void *o_tiled, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
-  veda_status s = check_geom(g, dtype, &geo, &hs);
+  int nt_min;
+  veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !v_tiled || !kv_idx || !o_tiled) return VEDA_ERR_NULL;
-  if (k < 1 || k > geo.nt) return VEDA_ERR_SHAPE;
+  if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
   const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, o_tiled, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
-  return hip_status(launch_sparse_attn(geo, dtype, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse,
+  return hip_status(launch_sparse_attn(geo, hs, dtype, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse,
                                        stream));
 }
 
@@ -199,6 +241,7 @@ veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, co
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
   return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
                                               rs_h, v_cols, kv_idx, k, softmax_scale, o_raster, lse, stream));
 }
@@ -209,7 +252,7 @@ size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {
   geo.B = g->batch;
   geo.H = g->heads;
   geo.P = g->tile;
-  geo.nt = (int32_t)((int64_t)g->t * g->h * g->w / g->tile);
+  geo.nt = geom_tiles(g);
   return tilemap_workspace_bytes(geo, n_sel);
 }
 
@@ -221,14 +264,14 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void
   veda_status s = check_geom(g, dtype, &geo, &hs);
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !tilemap) return VEDA_ERR_NULL;
-  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
-  if (geo.nt > TILEMAP_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && (n_sel != geo.nt || geo.padded))) return VEDA_ERR_SHAPE;
+  if (geo.nt > (dtype == VEDA_F32 ? TILEMAP_MAX_NT_F32 : TILEMAP_MAX_NT)) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < tilemap_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
   return hip_status(
-      launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, workspace, stream));
+      launch_tilemap(geo, dtype, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse, workspace, stream, &hs));
 }
 
 size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel) {
@@ -238,7 +281,7 @@ size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel) {
   geo.H = g->heads;
   geo.d = g->head_dim;
   geo.P = g->tile;
-  geo.nt = (int32_t)((int64_t)g->t * g->h * g->w / g->tile);
+  geo.nt = geom_tiles(g);
   return distill_workspace_bytes(geo, n_sel);
 }
 
@@ -253,12 +296,13 @@ veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, con
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !tilemap) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
-  if (geo.nt > TILEMAP_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  if (geo.nt > (dtype == VEDA_F32 ? TILEMAP_MAX_NT_F32 : TILEMAP_MAX_NT)) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_raster, k_raster, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
   if (workspace == nullptr || workspace_bytes < tilemap_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
   const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
   const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
@@ -276,8 +320,9 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !w1 || !w2 || !q_tiles || !target || !loss || !dw1 || !dw2) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt) return VEDA_ERR_SHAPE;
+  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // the distillation step takes dividing shapes only
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
-  if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  if (geo.nt > DISTILL_MAX_NT) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1, dw2, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
@@ -310,6 +355,22 @@ veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, i
     return VEDA_ERR_WORKSPACE;
   return hip_status(
       launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, ref_sq, workspace, stream));
+}
+
+int64_t veda_tiled_tokens(const veda_geom *g, veda_dtype dtype) {
+  Geo geo;
+  HeadShapes hs;
+  const veda_status s = check_geom(g, dtype, &geo, &hs);
+  return s != VEDA_OK ? (int64_t)s : (int64_t)geo.N;
+}
+
+int32_t veda_head_tiles(const veda_geom *g, veda_dtype dtype, int32_t head) {
+  Geo geo;
+  HeadShapes hs;
+  const veda_status s = check_geom(g, dtype, &geo, &hs);
+  if (s != VEDA_OK) return s;
+  if (head < 0 || head >= geo.H) return VEDA_ERR_SHAPE;
+  return head_tiles(hs.s[head][0], hs.s[head][1], hs.s[head][2], geo.T, geo.Hs, geo.Ws);
 }
 
 const char *veda_status_str(veda_status s) {

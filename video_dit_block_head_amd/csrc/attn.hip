@@ -39,7 +39,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
 // the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
 // order; RK: the same for K.  Otherwise tile-major.  V is always channel-major tiled.
-template <bool RQ, bool RK>
+// PAD: padded tiling (tiled operands only): per-head tile counts and partial key tiles.
+template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
                  const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
@@ -57,7 +58,10 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead : reinterpret_cast<const char *>(k + head);
   const char *vh = reinterpret_cast<const char *>(vt + head);
   const int32_t *list = kv_idx + (bh * g.nt + i) * kk;
-  const int last = g.nt - 1;
+  // this head's tiles (fewer than nt for a head of a padded tiling with fewer tiles)
+  const int nth = PAD ? head_tiles(hs.s[hh][0], hs.s[hh][1], hs.s[hh][2], g.T, g.Hs, g.Ws) : g.nt;
+  if (i >= nth) return;  // whole workgroup, before any barrier
+  const int last = nth - 1;
   auto k_tile = [&](int j) -> const char * {
     return RK ? kh + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn : kh + (int64_t)j * 32768;
   };
@@ -98,14 +102,30 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 
   for (int tt = 0; tt < kk; ++tt) {
     const bool more = tt + 1 < kk;
+    const int jc = jn;  // this step's key tile (jn moves on to the next one below)
     // ---- S^T = K Q^T on the K tile in LDS (its loads were issued before the V loads)
     wait_vmem<8>();
     barrier();
     f32x16_t acc_s[4];
+    // A padding key of a partial tile (padded tilings only) starts at -inf: its K row is
+    // zero, so the MFMAs leave it there and it gets no weight.  Entry (kb, r) of this lane
+    // is key row 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile.
+    const TileBox bx = PAD ? tile_box(jc, pt, ph, pw, g.T, g.Hs, g.Ws) : TileBox{128, 1, 1};
+    if (box_rows(bx) < 128) {
+      uint32_t wd[4];
+      tile_row_words(bx, ph, pw, lane, wd);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_s[kb][r] = (wd[kb] >> (8 * (r >> 2) + (r & 3))) & 1u ? 0.f : -INFINITY;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
       const int row = 32 * kb + lr;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -257,18 +277,25 @@ template <bool RQ, bool RK>
 static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
                           const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
                           float *lse, hipStream_t st) {
-  if (dt == VEDA_BF16)
-    attn_bf16_kernel<RQ, RK><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
-        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs, rv);
-  else
+  if (dt == VEDA_BF16) {
+    if (!RQ && !RK && g.padded)
+      attn_bf16_kernel<false, false, true><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
+          rv);
+    else
+      attn_bf16_kernel<RQ, RK, false><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
+          rv);
+  } else
     attn_f32_kernel<RQ, RK><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
                                                                  (const float *)v, kv_idx, kk, scale, (float *)o, lse,
                                                                  g, hs, rv);
 }
 
-hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
-                              const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st) {
-  launch_attn_t<false, false>(g, HeadShapes{}, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
+                              const void *v, const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
+                              hipStream_t st) {
+  launch_attn_t<false, false>(g, hs, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 

@@ -26,8 +26,11 @@ struct HeadShapes {
 };
 
 // Geometry as the kernels see it.
+// Shapes that do not divide the grid pad it up to whole tiles per head: N and nt are then the
+// tiled per-head length and tile count of the head with the most tiles, and `padded` is 1.
 struct Geo {
   int32_t B, H, d, T, Hs, Ws, P, N, nt;
+  int32_t padded;
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -38,15 +41,56 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Raster token index of row `o` of tile `j` for tile shape (pt, ph, pw): tiles row-major
 // over the tile grid, tokens row-major inside the tile.
+// The tile grid covers the grid padded up to whole tiles (ceil per axis); the token of a
+// padding row lies outside the real grid (row_real is false) and is never accessed.
 __device__ __forceinline__ int64_t tile_row_token(int j, int o, int pt, int ph, int pw, int Hs, int Ws) {
-  const int ntw = Ws / pw, nth = Hs / ph;
+  const int ntw = (Ws + pw - 1) / pw, nth = (Hs + ph - 1) / ph;
   const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
   const int ow = o % pw, oh = (o / pw) % ph, ot = o / (pw * ph);
   return ((int64_t)(jt * pt + ot) * Hs + (jh * ph + oh)) * Ws + (jw * pw + ow);
 }
 
+// Tiles of a head on the grid padded up to whole tiles.
+__host__ __device__ __forceinline__ int head_tiles(int pt, int ph, int pw, int T, int Hs, int Ws) {
+  return ((T + pt - 1) / pt) * ((Hs + ph - 1) / ph) * ((Ws + pw - 1) / pw);
+}
+
+// Real extent of tile j along (t, h, w): the part of the tile inside the real grid (the
+// whole shape unless the tile sticks out of a padded grid).  Uniform over a tile.
+struct TileBox {
+  int vt, vh, vw;
+};
+__device__ __forceinline__ TileBox tile_box(int j, int pt, int ph, int pw, int T, int Hs, int Ws) {
+  const int ntw = (Ws + pw - 1) / pw, nth = (Hs + ph - 1) / ph;
+  const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
+  return TileBox{min(pt, T - jt * pt), min(ph, Hs - jh * ph), min(pw, Ws - jw * pw)};
+}
+__device__ __forceinline__ int box_rows(const TileBox &b) { return b.vt * b.vh * b.vw; }
+// Whether row o of a tile with extent b is real; ph and pw are powers of two (their
+// product with pt is the tile, 64 or 128 tokens), so the in-tile coordinates are shifts.
+__device__ __forceinline__ bool in_box(int o, int ph, int pw, const TileBox &b) {
+  const int lw = __builtin_ctz(pw), lh = __builtin_ctz(ph);
+  return (o >> (lw + lh)) < b.vt && ((o >> lw) & (ph - 1)) < b.vh && (o & (pw - 1)) < b.vw;
+}
+__device__ __forceinline__ bool row_real(int j, int o, int pt, int ph, int pw, int T, int Hs, int Ws) {
+  return in_box(o, ph, pw, tile_box(j, pt, ph, pw, T, Hs, Ws));
+}
+
+// Real rows of a 128-row tile as four 32-bit words (word kb: rows 32 kb .. 32 kb + 31),
+// each shifted right by 4 * (lane / 32): bit 8 (r / 4) + r % 4 of word kb is then row
+// 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4, the key of MFMA 32x32 output entry (kb, r).
+// Built from the tile's box by two ballots, so nothing per lane outlives the tile.
+__device__ __forceinline__ void tile_row_words(const TileBox &bx, int ph, int pw, int lane, uint32_t (&wd)[4]) {
+  const uint64_t m0 = __ballot(in_box(lane, ph, pw, bx)), m1 = __ballot(in_box(64 + lane, ph, pw, bx));
+  const int sh = 4 * (lane >> 5);
+  wd[0] = (uint32_t)m0 >> sh;
+  wd[1] = (uint32_t)(m0 >> 32) >> sh;
+  wd[2] = (uint32_t)m1 >> sh;
+  wd[3] = (uint32_t)(m1 >> 32) >> sh;
+}
+
 // The same token as origin(j) + intra(o): the first is uniform over a tile, the second is
-// the same for row o of every tile of a head.
+// the same for row o of every tile of a head.  Used only with shapes that divide the grid.
 __device__ __forceinline__ int64_t tile_origin(int j, int pt, int ph, int pw, int Hs, int Ws) {
   const int ntw = Ws / pw, nth = Hs / ph;
   const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);

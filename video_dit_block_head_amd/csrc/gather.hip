@@ -2,6 +2,8 @@
 // [Technical Summary: Veda, §2.2 Head-Aware Tiling]
 //
 // HBM-bound copies.  One workgroup per (tile, head, batch); every access moves 16 bytes.
+// Padded tilings (shapes that do not divide the grid): the forward copy writes zero rows for
+// padding rows and for the tiles past the head's own count; the inverse skips them.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,10 +21,15 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(uint8_t *__restrict__ 
   const int64_t row_bytes = (int64_t)g.d * eb;
   uint8_t *tbase = tiled + (((int64_t)b * g.H + h) * g.N + (int64_t)j * g.P) * row_bytes;
   const int64_t rb = (int64_t)b * rs_b * eb, rh = (int64_t)h * rs_h * eb;
+  const bool in_head = !g.padded || j < head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws);
   for (int o = r0; o < g.P; o += 16) {
+    uint4 *dst_t = reinterpret_cast<uint4 *>(tbase + o * row_bytes) + chunk;
+    if (g.padded && !(in_head && row_real(j, o, pt, ph, pw, g.T, g.Hs, g.Ws))) {
+      if (!INVERSE) *dst_t = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
     uint4 *src_r = reinterpret_cast<uint4 *>(raster + rb + n * rs_n * eb + rh) + chunk;
-    uint4 *dst_t = reinterpret_cast<uint4 *>(tbase + o * row_bytes) + chunk;
     if (INVERSE)
       *src_r = *dst_t;
     else
@@ -39,11 +46,16 @@ __global__ void __launch_bounds__(256) gather_cols_bf16_kernel(const uint16_t *_
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
   const int cb = threadIdx.x & 15, tb = threadIdx.x >> 4;  // channel block, token block
+  const bool in_head = !g.padded || j < head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws);
   uint32_t in[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t n = tile_row_token(j, cols_key(tb * 8 + i), pt, ph, pw, g.Hs, g.Ws);
-    const uint4 v = *reinterpret_cast<const uint4 *>(raster + b * rs_b + n * rs_n + h * rs_h + cb * 8);
+    const int o = cols_key(tb * 8 + i);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);  // padding rows are zero
+    if (!g.padded || (in_head && row_real(j, o, pt, ph, pw, g.T, g.Hs, g.Ws))) {
+      const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
+      v = *reinterpret_cast<const uint4 *>(raster + b * rs_b + n * rs_n + h * rs_h + cb * 8);
+    }
     in[i][0] = v.x;
     in[i][1] = v.y;
     in[i][2] = v.z;
@@ -70,9 +82,14 @@ __global__ void __launch_bounds__(256) gather_cols_f32_kernel(const float *__res
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
   float *tbase = tiled + (((int64_t)b * g.H + h) * g.nt + j) * (int64_t)g.d * g.P;
+  const bool in_head = !g.padded || j < head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws);
   for (int e = threadIdx.x; e < g.P * g.d; e += blockDim.x) {
-    const int p = e % g.P, c = e / g.P;
-    const int64_t n = tile_row_token(j, cols_key(p), pt, ph, pw, g.Hs, g.Ws);
+    const int p = e % g.P, c = e / g.P, o = cols_key(p);
+    if (g.padded && !(in_head && row_real(j, o, pt, ph, pw, g.T, g.Hs, g.Ws))) {
+      tbase[(int64_t)c * g.P + p] = 0.f;
+      continue;
+    }
+    const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
     tbase[(int64_t)c * g.P + p] = raster[b * rs_b + n * rs_n + h * rs_h + c];
   }
 }

@@ -26,8 +26,9 @@ hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const voi
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);
 
-hipError_t launch_sparse_attn(const Geo &g, veda_dtype dt, const void *q, const void *k, const void *v,
-                              const int32_t *kv_idx, int kk, float scale, void *o, float *lse, hipStream_t st);
+hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
+                              const void *v, const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
+                              hipStream_t st);
 
 // Q and O in raster layout [B, N, H, d] (element strides rs_*), K raster or tile-major,
 // V channel-major tiled.

@@ -46,7 +46,8 @@ static constexpr int PM_HST = 260;    // hidden block row stride (floats)
 
 // RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through each
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
-template <int EB, bool RQ, bool RK>
+// PAD: padded tiling (tiled operands only): per-head tile counts, partial tiles.
+template <int EB, bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
@@ -63,13 +64,15 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int r0 = (L % ngrp) * PM_ROWS, which = (L / ngrp) & 1, h = (L / (2 * ngrp)) % g.H,
             b = L / (2 * ngrp * g.H);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
   __shared__ float Ds[PM_ROWS * PM_DS];   // descriptors, then the hidden layer
 
   // ---- TripPool: lane (rg = lane/16, c = lane%16) accumulates rows rg, rg + 4, ... of its
   // 16-byte channel chunk c; the 4 row groups are combined as (g0 + g1) + (g2 + g3).
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
   const bool rast = which ? RK : RQ;  // uniform over the workgroup
+  const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;  // this head's tiles
   const uint8_t *src0 = rast ? (which ? k : q) + (int64_t)b * rv.sb + (int64_t)h * rv.sh
                              : (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
   const int rg = lane >> 4, c = lane & 15;
@@ -83,7 +86,34 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
       mx[e] = -INFINITY;
       mn[e] = INFINITY;
     }
-    if (j < g.nt) {
+    const TileBox bx = PAD ? tile_box(j, pt, ph, pw, g.T, g.Hs, g.Ws) : TileBox{P, 1, 1};
+    auto accum = [&](const uint4 &v) {
+      float x[EPC];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      if (EB == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(wd[e] << 16);
+          x[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        s[e] += x[e];
+        mx[e] = fmaxf(mx[e], x[e]);
+        mn[e] = fminf(mn[e], x[e]);
+      }
+    };
+    if (j < nth && !(RQ || RK) && PAD && box_rows(bx) < P) {
+      // a partial tile of a padded tiling (tiled operands only): its real rows, one at a time
+      const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
+#pragma unroll 1
+      for (int o = rg; o < P; o += 4)
+        if (in_box(o, ph, pw, bx)) accum(load_stream16(src + o * 256));
+    } else if (j < nth) {
       // raster rows: 32-bit offsets from the tile's origin, half a tile (16 loads) at a time
       constexpr int NL = (RQ || RK) ? P / 8 : P / 4;
 #pragma unroll 1
@@ -100,26 +130,7 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
           for (int i = 0; i < NL; ++i) v[i] = load_stream16(src + (rg + 4 * (NL * part + i)) * 256);
         }
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          float x[EPC];
-          const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-          if (EB == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[2 * e] = __uint_as_float(wd[e] << 16);
-              x[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
-          }
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            s[e] += x[e];
-            mx[e] = fmaxf(mx[e], x[e]);
-            mn[e] = fminf(mn[e], x[e]);
-          }
-        }
+        for (int i = 0; i < NL; ++i) accum(v[i]);
       }
     }
 #pragma unroll
@@ -132,10 +143,12 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
       mn[e] = fminf(mn[e], __shfl_xor(mn[e], 32));
     }
     if (rg == 0) {
-      const bool ok = j < g.nt;
+      const bool ok = j < nth;
+      // mean over the tile's real rows (all P of them unless the tiling is padded)
+      const float inv_cnt = 1.0f / (float)(PAD && ok ? box_rows(bx) : P);  // exact for P = 2^n
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        Ds[row * PM_DS + c * EPC + e] = ok ? s[e] * (1.0f / (float)P) : 0.f;  // P is a power of two
+        Ds[row * PM_DS + c * EPC + e] = ok ? s[e] * inv_cnt : 0.f;
         Ds[row * PM_DS + D + c * EPC + e] = ok ? mx[e] : 0.f;
         Ds[row * PM_DS + 2 * D + c * EPC + e] = ok ? mn[e] : 0.f;
       }
@@ -230,13 +243,15 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 template <int MAXM>
 __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict__ y, Geo g, float scale,
                                                          float *__restrict__ scores, float *__restrict__ probs,
-                                                         int topk, int32_t *__restrict__ idx) {
+                                                         int topk, int32_t *__restrict__ idx, HeadShapes hs) {
   constexpr int SW = 64 * MAXM + 1;
   __shared__ float S[16 * SW];
   const int nt = g.nt, nrb = (nt + 15) >> 4;
   const int L = xcd_tile(blockIdx.x, gridDim.x);  // each XCD walks contiguous heads
   const int i0 = (L % nrb) * 16, h = (L / nrb) % g.H, b = L / (nrb * g.H);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  // rows and columns of this head (fewer than nt for a head of a padded tiling with fewer tiles)
+  const int nth = g.padded ? head_tiles(hs.s[h][0], hs.s[h][1], hs.s[h][2], g.T, g.Hs, g.Ws) : nt;
   const float *yq = y + (((int64_t)b * g.H + h) * nt) * MLP_OUT;
   const float *yk = y + ((((int64_t)g.B + b) * g.H + h) * nt) * MLP_OUT;
   // The contraction slot kq of step s carries channel 16 kq + s, so each lane's 16 operand
@@ -291,26 +306,26 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
 #pragma unroll 1
   for (int rr = 0; rr < 4; ++rr) {
     const int row = 4 * w + rr, i = i0 + row;
-    if (i >= nt) break;  // wave-uniform
+    if (i >= nth) break;  // wave-uniform
     const int64_t grow = ((int64_t)b * g.H + h) * nt + i;
     float sc[MAXM];
 #pragma unroll
     for (int mm = 0; mm < MAXM; ++mm) sc[mm] = S[row * SW + min(64 * mm + lane, 64 * MAXM - 1)];
-    if (scores != nullptr) {
+    if (scores != nullptr) {  // columns past the head's tiles: -inf
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm)
-        if (64 * mm + lane < nt) scores[grow * nt + 64 * mm + lane] = sc[mm];
+        if (64 * mm + lane < nt) scores[grow * nt + 64 * mm + lane] = 64 * mm + lane < nth ? sc[mm] : -INFINITY;
     }
     if (probs != nullptr) {
       float mx = -INFINITY;
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm)
-        if (64 * mm + lane < nt) mx = fmaxf(mx, sc[mm]);
+        if (64 * mm + lane < nth) mx = fmaxf(mx, sc[mm]);
       mx = wave_max(mx);
       float e[MAXM], sum = 0.f;
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm) {
-        e[mm] = (64 * mm + lane < nt) ? expf(sc[mm] - mx) : 0.f;
+        e[mm] = (64 * mm + lane < nth) ? expf(sc[mm] - mx) : 0.f;
         sum += e[mm];
       }
       sum = wave_sum(sum);
@@ -322,9 +337,9 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
     if (topk > 0) {
       uint32_t key[MAXM];
 #pragma unroll
-      for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nt) ? float_key(sc[mm]) : 0u;
+      for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nth) ? float_key(sc[mm]) : 0u;
       // the row is in registers now: its LDS words serve as the wave's top-k scratch
-      wave_topk<MAXM>(key, nt, topk, lane, idx + grow * topk, nullptr, reinterpret_cast<uint32_t *>(&S[row * SW]));
+      wave_topk<MAXM>(key, nth, topk, lane, idx + grow * topk, nullptr, reinterpret_cast<uint32_t *>(&S[row * SW]));
     }
   }
 }
@@ -349,9 +364,9 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
 // ---------------------------------------------------------------------------------------
 template <int MAXM>
 static void launch_score_t(const Geo &g, const float *y, float scale, float *scores, float *probs, int topk,
-                           int32_t *idx, hipStream_t st) {
+                           int32_t *idx, const HeadShapes &hs, hipStream_t st) {
   score_topk_kernel<MAXM><<<dim3(((g.nt + 15) / 16) * g.H * g.B), 256, 0, st>>>(y, g, scale, scores, probs, topk,
-                                                                                 idx);
+                                                                                 idx, hs);
 }
 
 template <int EB, bool RQ, bool RK>
@@ -359,15 +374,19 @@ static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterVi
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
                               float *q_desc, float *k_desc, hipStream_t st) {
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
-  pool_mlp_kernel<EB, RQ, RK><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k, y,
-                                                  q_desc, k_desc, g, hs, rv);
+  if (!RQ && !RK && g.padded)
+    pool_mlp_kernel<EB, false, false, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k,
+                                                                w2k, y, q_desc, k_desc, g, hs, rv);
+  else
+    pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
+                                                           y, q_desc, k_desc, g, hs, rv);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
                            bool k_raster) {
-  const HeadShapes hs0{};
+  const HeadShapes hs0 = hs != nullptr ? *hs : HeadShapes{};  // tiled operands: shapes matter only when padded
   const RasterView rv0{0, 0, 0};
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
@@ -396,16 +415,19 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
+  const HeadShapes hsv = hs != nullptr ? *hs : HeadShapes{};
   const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster);
   if (pe != hipSuccess) return pe;
   if (g.nt <= 64)
-    launch_score_t<1>(g, y, scale, scores, probs, topk, idx, st);
+    launch_score_t<1>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else if (g.nt <= 256)
-    launch_score_t<4>(g, y, scale, scores, probs, topk, idx, st);
+    launch_score_t<4>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else if (g.nt <= 640)
-    launch_score_t<10>(g, y, scale, scores, probs, topk, idx, st);
+    launch_score_t<10>(g, y, scale, scores, probs, topk, idx, hsv, st);
+  else if (g.nt <= 1280)
+    launch_score_t<20>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else
-    launch_score_t<20>(g, y, scale, scores, probs, topk, idx, st);
+    launch_score_t<24>(g, y, scale, scores, probs, topk, idx, hsv, st);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ static constexpr int TM_QT = 2;
 
 // RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through the
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
-template <bool RQ, bool RK>
+// PAD: padded tiling (tiled operands only): per-head tile counts, partial tiles.
+template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
                     const int32_t *__restrict__ q_tiles, int n_sel, float *__restrict__ out,
@@ -45,9 +46,11 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   const int qt = w >> 1;                     // which of the workgroup's query tiles
   const int a = min(a0 + qt, n_sel - 1);     // an odd tail repeats the last tile (not written twice)
   const bool owner = a0 + qt < n_sel;
-  const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) : a;  // clamped
   const int hh = (int)(bh % g.H), bb = (int)(bh / g.H);
   const int pt = hs.s[hh][0], ph = hs.s[hh][1], pw = hs.s[hh][2];
+  // this head's tiles (fewer than nt for a head of a padded tiling with fewer tiles)
+  const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;
+  const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), nth - 1) : a;  // clamped
   const int64_t rhead = (int64_t)bb * rv.sb + (int64_t)hh * rv.sh;
   const __bf16 *qh = q + bh * (int64_t)g.N * 128;
   const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead
@@ -84,25 +87,44 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     tile_dma_offsets(w, lane, off);
   const uint32_t kb_lds[2] = {lds_addr(Kb[0]), lds_addr(Kb[1])};
   tile_to_lds(k_tile(0), kb_lds[0], w, off);
-  if (g.nt > 1) tile_to_lds(k_tile(1), kb_lds[1], w, off);
+  if (nth > 1) tile_to_lds(k_tile(1), kb_lds[1], w, off);
 
   float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
-  for (int j = 0; j < g.nt; ++j) {
+  for (int j = 0; j < nth; ++j) {
     const int buf = j & 1;
-    if (j + 1 < g.nt)
+    if (j + 1 < nth)
       wait_vmem<8>();  // tile j+1's copies may still be in flight
     else
       wait_vmem<0>();
     barrier();
     f32x16_t acc[2][4];
     const uint4 *Ks = Kb[buf];
+    // A padding key of a partial tile (padded tilings only) starts at -inf: its K row is
+    // zero, so the MFMAs leave it there and it gets no probability.  Entry (kb, r) of this
+    // lane is key row 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile.
+    const TileBox bx = PAD ? tile_box(j, pt, ph, pw, g.T, g.Hs, g.Ws) : TileBox{128, 1, 1};
+    if (box_rows(bx) < 128) {
+      uint32_t wd[4];
+      tile_row_words(bx, ph, pw, lane, wd);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = (wd[kb] >> (8 * (r >> 2) + (r & 3))) & 1u ? 0.f : -INFINITY;
+          acc[0][kb][r] = z;
+          acc[1][kb][r] = z;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[0][kb][r] = 0.f;
+          acc[1][kb][r] = 0.f;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[0][kb][r] = 0.f;
-        acc[1][kb][r] = 0.f;
-      }
       const int row = 32 * kb + lr;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -113,7 +135,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     }
     wait_lds();
     barrier();  // every wave has read this buffer
-    if (j + 2 < g.nt) tile_to_lds(k_tile(j + 2), kb_lds[buf], w, off);
+    if (j + 2 < nth) tile_to_lds(k_tile(j + 2), kb_lds[buf], w, off);
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -142,7 +164,8 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     const float lse2 = m_run[qb] + log2f(l_run[qb] + __shfl_xor(l_run[qb], 32));
     const int qi = 64 * (w & 1) + 32 * qb + lr;
     if (hi == 0) {
-      lse_s[qt][qi] = lse2;
+      // a padding query row of a padded tiling stays out of the pooled maximum
+      lse_s[qt][qi] = PAD && !row_real(i, qi, pt, ph, pw, g.T, g.Hs, g.Ws) ? INFINITY : lse2;
       if (lse_out != nullptr && owner) lse_out[(bh * n_sel + a) * 128 + qi] = lse2 * TM_LN2;
     }
   }
@@ -152,6 +175,10 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   for (int e = t; e < TM_QT * g.nt; e += 256) {
     const int qq = e / g.nt, j = e % g.nt;
     if (a0 + qq >= n_sel) continue;
+    if (j >= nth) {  // past this head's tiles
+      out[(bh * n_sel + a0 + qq) * (int64_t)g.nt + j] = 0.f;
+      continue;
+    }
     const float4 *src = reinterpret_cast<const float4 *>(rowmax + ((bh * n_sel + a0 + qq) * (int64_t)g.nt + j) * 128);
     float x = -INFINITY;
 #pragma unroll 8
@@ -224,10 +251,15 @@ template <bool RQ, bool RK>
 static void launch_tilemap_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
                              const void *k, float scale, const int32_t *q_tiles, int n_sel, float *tilemap,
                              float *lse, void *ws, hipStream_t st) {
-  if (dt == VEDA_BF16)
-    tilemap_bf16_kernel<RQ, RK><<<dim3(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B), 256, 0, st>>>(
-        (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
-  else
+  const dim3 grid(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B);
+  if (dt == VEDA_BF16) {
+    if (!RQ && !RK && g.padded)
+      tilemap_bf16_kernel<false, false, true><<<grid, 256, 0, st>>>(
+          (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
+    else
+      tilemap_bf16_kernel<RQ, RK, false><<<grid, 256, 0, st>>>(
+          (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
+  } else
     tilemap_f32_kernel<RQ, RK><<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale,
                                                                      q_tiles, n_sel, tilemap, lse, g, hs, rv);
 }
@@ -236,7 +268,7 @@ hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void
                           const int32_t *q_tiles, int n_sel, float *tilemap, float *lse, void *ws, hipStream_t st,
                           const HeadShapes *hs, const RasterView *rv, bool k_raster) {
   if (rv == nullptr)
-    launch_tilemap_t<false, false>(g, HeadShapes{}, RasterView{0, 0, 0}, dt, q, k, scale, q_tiles, n_sel, tilemap,
+    launch_tilemap_t<false, false>(g, hs != nullptr ? *hs : HeadShapes{}, RasterView{0, 0, 0}, dt, q, k, scale, q_tiles, n_sel, tilemap,
                                    lse, ws, st);
   else if (k_raster)
     launch_tilemap_t<true, true>(g, *hs, *rv, dt, q, k, scale, q_tiles, n_sel, tilemap, lse, ws, st);

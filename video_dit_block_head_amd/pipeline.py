@@ -28,7 +28,7 @@ class SparseAttention:
         self.score_scale = float(score_scale)
         self.softmax_scale = 1.0 / math.sqrt(geom.head_dim) if softmax_scale is None else float(softmax_scale)
         g = geom
-        shape = (g.batch, g.heads, g.n_tokens, g.head_dim)
+        shape = (g.batch, g.heads, g.n_tiled, g.head_dim)   # n_tiled = n_tokens unless the tiling is padded
         self.q_t = torch.empty(shape, dtype=dtype, device=device)
         self.k_t = torch.empty(shape, dtype=dtype, device=device)
         self.v_t = torch.empty(shape, dtype=dtype, device=device)   # COLS layout, same size
@@ -144,6 +144,8 @@ class SparseAttention:
 def dense_index(geom: Geom, device="cuda"):
     """Kept-tile list with every key tile (0 % skipping): the dense path."""
     g = geom
+    if g.padded:
+        raise ValueError("the dense kept-tile list needs one tile count for every head")
     return (torch.arange(g.n_tiles, dtype=torch.int32, device=device)
             .expand(g.batch, g.heads, g.n_tiles, g.n_tiles).contiguous())
 

@@ -8,7 +8,7 @@ initialised per-head estimator, and a fixed fraction of kept key tiles.
 
 This module is data only.  It holds no step of the method.
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import List, Optional, Tuple
 
 Shape3 = Tuple[int, int, int]
@@ -36,6 +36,7 @@ class Config:
     mlp_out: int = 64
     score_scale: float = 1.0 / 8.0
     unit_axis_scale: bool = False   # per-head (t,h,w) position-code scales all 1.0
+    padded: bool = False            # cycle every listed shape, also those that do not divide the grid
 
     @property
     def n_tokens(self) -> int:
@@ -55,14 +56,26 @@ class Config:
         return out
 
     def head_shapes(self) -> List[Shape3]:
-        """Tile shape of each head: the valid shapes cycled by head index."""
-        v = self.valid_shapes()
+        """Tile shape of each head: the valid shapes cycled by head index (every listed
+        shape when the workload is padded)."""
+        v = list(self.shape_list) if self.padded else self.valid_shapes()
         return [v[h % len(v)] for h in range(self.heads)]
+
+    def head_tiles(self, h: int) -> int:
+        """Tiles of head h on the grid padded up to whole tiles of its shape."""
+        (t, hh, w), (pt, ph, pw) = self.grid, self.head_shapes()[h]
+        return (-(-t // pt)) * (-(-hh // ph)) * (-(-w // pw))
 
     def kept_flops(self, k: int) -> float:
         """4 * N * N * d * (k / n_t) * heads * batch: the QK^T and PV products on kept tiles."""
         n = self.n_tokens
         return 4.0 * n * n * self.head_dim * (k / self.n_tiles) * self.heads * self.batch
+
+
+def padded_variant(cfg: Config, name: Optional[str] = None, **changes) -> Config:
+    """The same workload with the full shape list cycled over the heads, so that heads whose
+    shape does not divide the grid get a padded tiling."""
+    return replace(cfg, name=name or cfg.name + "-padded", padded=True, **changes)
 
 
 CONFIGS = [

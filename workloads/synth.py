@@ -104,7 +104,7 @@ class Workload:
 
     def sample_tiles(self, h: int) -> np.ndarray:
         if self.q_sample is None:
-            return np.arange(self.cfg.n_tiles)
+            return np.arange(self.cfg.head_tiles(h))
         return self.q_sample[h]
 
 
@@ -162,8 +162,9 @@ def make(cfg: Config, heads: Optional[List[int]] = None) -> Workload:
     q_sample = None
     if cfg.sampled_q_tiles is not None:
         r2 = np.random.default_rng(cfg.seed + 1000)
-        q_sample = np.stack([np.sort(r2.choice(cfg.n_tiles, cfg.sampled_q_tiles, replace=False))
-                             for _ in range(H)]).astype(np.int64)
+        q_sample = np.stack([np.sort(r2.choice(cfg.head_tiles(h) if cfg.padded else cfg.n_tiles,
+                                               cfg.sampled_q_tiles, replace=False))
+                             for h in range(H)]).astype(np.int64)
     return Workload(cfg, q, k, v, w1, w2, scales, sinks, cfg.head_shapes(), q_sample)
 
 
