@@ -138,7 +138,7 @@ def main():
 
     import video_dit_block_head_amd as V
     from video_dit_block_head_amd.pipeline import SparseAttention, dense_index
-    from workloads import get, make
+    from workloads import get, make, padded_variant
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -277,12 +277,59 @@ def main():
         torch.cuda.synchronize()
         herr_ms = e0.elapsed_time(e1) / reps
         herr_bytes = 2 * B * N * H * d * 2
+        # NEXT-2: the same workload with its full shape cycle, where (8,4,4) does not divide
+        # T = 20, on the padded tiled path (gather Q K V, score, attend, scatter, tile map)
+        pcfg = padded_variant(cfg)
+        pshapes = pcfg.head_shapes()
+        pgeom = V.Geom(B, H, d, cfg.grid, P, pshapes)
+        pad_row = None
+        if pgeom.padded:
+            say("[bench] padded tiling step (full shape cycle)")
+            psa = SparseAttention(pgeom, torch.bfloat16, torch.from_numpy(wl.w1), torch.from_numpy(wl.w2),
+                                  score_scale=cfg.score_scale)
+            prng = np.random.default_rng(cfg.seed + 2000)
+            pqt = torch.from_numpy(np.stack([np.sort(prng.choice(pgeom.head_tiles(h), n_sel, replace=False))
+                                             for h in range(H)]).astype(np.int32)[None].repeat(B, 0)).cuda()
+            pmap = torch.empty((B, H, n_sel, pgeom.n_tiles), dtype=torch.float32, device="cuda")
+            pout = torch.empty_like(q)
+
+            def pstep():
+                psa.gather(q, k, v)
+                pidx = psa.score(kk)
+                psa.attend(pidx)
+                psa.scatter(pout)
+                psa.tilemap(pqt, n_sel, pmap)
+                return pidx
+
+            pidx = pstep()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                pstep()
+            e1.record()
+            torch.cuda.synchronize()
+            pstep_ms = e0.elapsed_time(e1) / reps
+            e0.record()
+            for _ in range(reps):
+                psa.attend(pidx)
+            e1.record()
+            torch.cuda.synchronize()
+            pattn_ms = e0.elapsed_time(e1) / reps
+            # kept work: every (query tile, kept key tile) pair of every head, padding rows included
+            pflops = sum(4.0 * pgeom.head_tiles(h) * kk * P * P * d for h in range(H)) * B
+            pad_row = {"padded_shapes": sorted(set(map(tuple, pshapes))),
+                       "padded_tiles_per_head": sorted(set(pgeom.head_tiles(h) for h in range(H))),
+                       "padded_step_ms": round(pstep_ms, 3), "padded_attn_ms": round(pattn_ms, 3),
+                       "padded_attn_tflops": round(pflops / (pattn_ms * 1e-3) / 1e12, 1)}
+            del psa, pmap, pout
         nxt = {"distill_step_ms": round(distill_ms, 4),
                "distill_step_qk_read_gbps": round(2 * B * H * N * d * 2 / (distill_ms * 1e-3) / 1e9, 1),
                "distill_sampled_query_tiles_per_head": n_sel,
                "head_sq_error_ms": round(herr_ms, 4),
                "head_sq_error_gbps": round(herr_bytes / (herr_ms * 1e-3) / 1e9, 1),
                "head_sq_error_frac_hbm_peak": round(herr_bytes / (herr_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        if pad_row is not None:
+            nxt.update(pad_row)
 
     if args.copy_calibration:
         n = 1 << 29  # 1 GiB of bf16
