@@ -424,6 +424,10 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
     launch_score_t<4>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else if (g.nt <= 640)
     launch_score_t<10>(g, y, scale, scores, probs, topk, idx, hsv, st);
+  else if (g.nt <= 768)   // the row block in LDS grows with the bound: keep it tight
+    launch_score_t<12>(g, y, scale, scores, probs, topk, idx, hsv, st);
+  else if (g.nt <= 1024)
+    launch_score_t<16>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else if (g.nt <= 1280)
     launch_score_t<20>(g, y, scale, scores, probs, topk, idx, hsv, st);
   else
