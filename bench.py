@@ -277,7 +277,7 @@ def main():
         torch.cuda.synchronize()
         herr_ms = e0.elapsed_time(e1) / reps
         herr_bytes = 2 * B * N * H * d * 2
-        # NEXT-2: the same workload with its full shape cycle, where (8,4,4) does not divide
+        # Padded tilings: the same workload with its full shape cycle, where (8,4,4) does not divide
         # T = 20, on the padded tiled path (gather Q K V, score, attend, scatter, tile map)
         pcfg = padded_variant(cfg)
         pshapes = pcfg.head_shapes()
