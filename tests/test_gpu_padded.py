@@ -29,6 +29,10 @@ CASES = {
     "small-padded": (padded_variant(get(1), name="small-padded", grid=(20, 16, 32), heads=5,
                                     shape_list=tuple(SHAPES_128) + ((16, 2, 4),), topk=(16,), seed=11,
                                     sampled_q_tiles=24), None, None),
+    # batch 2 and k at its bound (the smallest n_t(h) = 80): every tile of the dividing heads
+    "small-padded-b2-kmax": (padded_variant(get(1), name="small-padded-b2-kmax", batch=2, grid=(20, 16, 32), heads=3,
+                                            shape_list=((8, 4, 4), (2, 8, 8), (16, 2, 4)), topk=(80,), seed=12,
+                                            sampled_q_tiles=8), None, None),
     "mid-padded": (padded_variant(get(2), sampled_q_tiles=32), 3, 16),
     "large-padded": (padded_variant(get(3), topk=(60,)), 2, 8),
     "long-padded": (padded_variant(get(4), topk=(120,)), 2, 4),
@@ -86,11 +90,15 @@ class PaddedRun:
         self._oh = {}
 
     def heads(self):
-        """The heads whose shape does not divide the grid, and head 0."""
+        """The heads whose shape does not divide the grid, and the first one whose shape does."""
         T, Hh, W = self.cfg.grid
         pad = [h for h, (pt, ph, pw) in enumerate(self.wl.shapes) if T % pt or Hh % ph or W % pw]
-        hs = sorted(set([0] + pad))
-        return hs if self.n_heads is None else [0] + pad[:self.n_heads - 1]
+        div = [h for h in range(self.cfg.heads) if h not in pad][:1]
+        return sorted(div + (pad if self.n_heads is None else pad[:self.n_heads - 1]))
+
+    def pairs(self):
+        """(batch, head) pairs checked against the oracle."""
+        return [(b, h) for b in range(self.cfg.batch) for h in self.heads()]
 
     def oracle_head(self, b, h):
         if (b, h) not in self._oh:
@@ -117,14 +125,14 @@ def r(request):
 
 def test_padded_gather(r):
     cfg, P, d = r.cfg, r.cfg.tile, r.cfg.head_dim
-    for h in r.heads():
-        qt, kt, vt, slots = r.oracle_head(0, h)
+    for b, h in r.pairs():
+        qt, kt, vt, slots = r.oracle_head(b, h)
         n = len(slots)
-        gq, gk = host(r.sa.q_t[0, h]), host(r.sa.k_t[0, h])
+        gq, gk = host(r.sa.q_t[b, h]), host(r.sa.k_t[b, h])
         assert bitwise_equal(gq[:n], qt) and bitwise_equal(gk[:n], kt), (cfg.name, h)
         assert not gq[n:].any() and not gk[n:].any(), (cfg.name, h, "rows past the head's tiles")
         ntile = n // P
-        vcols = host(r.sa.v_t[0, h]).reshape(r.nt, d, P).transpose(0, 2, 1)[:ntile]
+        vcols = host(r.sa.v_t[b, h]).reshape(r.nt, d, P).transpose(0, 2, 1)[:ntile]
         assert bitwise_equal(vcols, vt.reshape(ntile, P, d)[:, COLS_KEY[:P], :]), (cfg.name, h, "v")
     back = torch.empty_like(r.q)
     V.veda_tile_gather(r.geom, back, r.sa.q_t, V.ROWS, inverse=True)
@@ -134,12 +142,12 @@ def test_padded_gather(r):
 
 def test_padded_descriptors(r):
     cfg, P, d = r.cfg, r.cfg.tile, r.cfg.head_dim
-    for h in r.heads():
-        qt, kt, _, slots = r.oracle_head(0, h)
+    for b, h in r.pairs():
+        qt, kt, _, slots = r.oracle_head(b, h)
         ntile = len(slots) // P
         for x, gd in ((qt, r.qd), (kt, r.kd)):
             ref = O.trippool(x, P, valid=slots >= 0)
-            got = host(gd[0, h])[:ntile]
+            got = host(gd[b, h])[:ntile]
             assert bitwise_equal(got[:, d:], ref[:, d:]), (cfg.name, h)
             err = np.abs(got[:, :d] - ref[:, :d]) / np.maximum(np.abs(ref[:, :d]), 1.0)
             assert err.max() <= 1e-6, (cfg.name, h, err.max())
@@ -148,17 +156,17 @@ def test_padded_descriptors(r):
 def test_padded_scores_topk(r):
     cfg, P = r.cfg, r.cfg.tile
     worst, exempt, rows = 0.0, 0, 0
-    for h in r.heads():
-        qt, kt, _, slots = r.oracle_head(0, h)
+    for b, h in r.pairs():
+        qt, kt, _, slots = r.oracle_head(b, h)
         valid = slots >= 0
         ntile = len(slots) // P
         yq = O.mlp(O.trippool(qt, P, valid=valid), r.wl.w1[h], r.wl.w2[h])
         yk = O.mlp(O.trippool(kt, P, valid=valid), r.wl.w1[h], r.wl.w2[h])
         s = O.tile_scores(yq, yk, cfg.score_scale)
-        gs = host(r.scores[0, h])
+        gs = host(r.scores[b, h])
         worst = max(worst, float(np.abs(gs[:ntile, :ntile] - s).max()))
         assert np.all(np.isneginf(gs[:ntile, ntile:])), (cfg.name, h, "columns past the head's tiles")
-        idx = host(r.idx[0, h]).astype(np.int64)
+        idx = host(r.idx[b, h]).astype(np.int64)
         s32 = s.astype(np.float32)
         for i in range(ntile):
             ok, ex = O.topk_agrees(s32[i], idx[i], r.kk)
@@ -173,23 +181,23 @@ def test_padded_attention(r):
     cfg, P = r.cfg, r.cfg.tile
     scale = 1 / math.sqrt(cfg.head_dim)
     num = den = mx = lse_err = 0.0
-    for h in r.heads():
-        qt, kt, vt, slots = r.oracle_head(0, h)
+    for b, h in r.pairs():
+        qt, kt, vt, slots = r.oracle_head(b, h)
         tiles = r.q_tiles(h)
-        idx = host(r.idx[0, h]).astype(np.int64)
+        idx = host(r.idx[b, h]).astype(np.int64)
         ref, ref_lse = O.sparse_attention(qt, kt, vt, idx, P, scale, q_tiles=tiles, return_lse=True,
                                           key_valid=slots >= 0)
         rows = (tiles[:, None] * P + np.arange(P)[None]).ravel()
         real = slots[rows] >= 0                               # padding query rows carry no token
-        got = host(r.sa.o_t[0, h])[rows][real]
+        got = host(r.sa.o_t[b, h])[rows][real]
         ref = ref[real]
         num += float(((got - ref) ** 2).sum())
         den += float((ref ** 2).sum())
         mx = max(mx, float(np.abs(got - ref).max()))
-        lse_err = max(lse_err, float(np.abs(host(r.lse[0, h])[rows][real] - ref_lse[real]).max()))
+        lse_err = max(lse_err, float(np.abs(host(r.lse[b, h])[rows][real] - ref_lse[real]).max()))
         # the raster output is the tiled output scattered through the slots
         sl = slots[slots >= 0]
-        assert bitwise_equal(host(r.out[0, :, h])[sl], host(r.sa.o_t[0, h])[:len(slots)][slots >= 0]), (cfg.name, h)
+        assert bitwise_equal(host(r.out[b, :, h])[sl], host(r.sa.o_t[b, h])[:len(slots)][slots >= 0]), (cfg.name, h)
     rel = math.sqrt(num / den)
     say(f"[gpu-padded] {cfg.name} k={r.kk}: max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
     assert mx <= 2e-2 and rel <= 1e-2 and lse_err <= 4e-3
@@ -208,13 +216,13 @@ def test_padded_tilemap(r):
     tmh = host(tm)
     worst = 0.0
     n_check = 4 if r.n_tiles_checked is not None else n_sel
-    for h in r.heads():
-        qt, kt, _, slots = r.oracle_head(0, h)
+    for b, h in r.pairs():
+        qt, kt, _, slots = r.oracle_head(b, h)
         ntile = len(slots) // P
         sel = np.linspace(0, n_sel - 1, n_check).astype(int)
         ref = O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=r.wl.sample_tiles(h)[sel],
                         key_valid=slots >= 0, query_valid=slots >= 0)
-        got = tmh[0, h, sel]
+        got = tmh[b, h, sel]
         assert not got[:, ntile:].any(), (cfg.name, h, "columns past the head's tiles")
         got = got[:, :ntile]
         keep = ref >= 1e-30
