@@ -160,7 +160,7 @@ def test_tilemap_validation(L):
     assert f(g.ref, V.BF16, A, None, 0.088, A, 4, A, None, A, big, None) == NULL
     assert f(g.ref, V.BF16, A, A, 0.088, MIS, 4, A, None, A, big, None) == ALIGN
     need = L.veda_oracle_tilemap_workspace_bytes(g.ref, 4)
-    assert need == 1 * 2 * 4 * 32 * 128 * 4
+    assert need == 1 * 2 * 4 * 32 * 128 * 4 + 1 * 2 * 4 * 4 * 128 * 8   # row maxima, then (m, l) for <= 4 key ranges
     assert f(g.ref, V.BF16, A, A, 0.088, A, 4, A, None, None, big, None) == WS
     assert f(g.ref, V.BF16, A, A, 0.088, A, 4, A, None, A, need - 1, None) == WS
 

@@ -2,13 +2,16 @@
 // (query tile x key tile) region.  [Technical Summary: Veda, §2.1 "Target Construction";
 // §2.3: ground-truth heatmaps in two passes, on subsets of query tiles]
 //
-// bf16 path: one workgroup (4 waves x 64 queries) per two selected query tiles of a head.
-//  pass 1 (one sweep over all N keys): S^T = K Q^T per key tile (MFMA, same blocking as the
-//          attention kernel; K tiles double-buffered in LDS through direct-to-LDS copies);
-//          per query row the running log-sum-exp (log2 domain, lazy max) and the row max of
-//          each key tile, m[q][j] = max_x s(q, x) * c, written to the workspace;
-//  pass 2: M[j] = exp2(max over the tile's queries of m[q][j] - lse2[q]), from the
-//          workspace (no second Q K^T).
+// bf16 path: one workgroup (4 waves x 64 queries) per two selected query tiles of a head and
+// one of S contiguous ranges of its key tiles (S chosen so that the workgroups fill whole
+// rounds of the chip; a last round left half empty cost about a sixth of the time).
+//  pass 1 (a sweep over the range's keys): S^T = K Q^T per key tile (MFMA, same blocking as
+//          the attention kernel; K tiles double-buffered in LDS through direct-to-LDS
+//          copies); per query row the range's log-sum-exp terms (log2 domain, lazy max: the
+//          running max m and sum l) and the row max of each key tile, m[q][j] = max_x
+//          s(q, x) * c, written to the workspace;
+//  pass 2 (tilemap_pool_kernel): lse2[q] from the S (m, l) pairs, then M[j] = exp2(max over
+//          the tile's queries of m[q][j] - lse2[q]) from the workspace (no second Q K^T).
 // exp is monotone, so this is the max over the region of exp(s - lse).
 #include "common.h"
 #include "kernels.h"
@@ -20,8 +23,14 @@ static constexpr float TM_LN2 = 0.6931471805599453f;
 static constexpr float TM_SLACK = 8.0f;  // lazy running-max slack (log2 units)
 static constexpr int TM_MAX_NT = 1280;
 
+static constexpr int TM_MAX_SPLITS = 4;
+
+static inline size_t tm_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Row maxima [B, H, n_sel, nt, P] f32, then the per-range (m, l) pairs [B, H, n_sel, S, P].
 size_t tilemap_workspace_bytes(const Geo &g, int n_sel) {
-  return (size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float);
+  return tm_align256((size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float)) +
+         (size_t)g.B * g.H * n_sel * TM_MAX_SPLITS * g.P * sizeof(float2);
 }
 
 // Two selected query tiles (of one head) per workgroup: they sweep the same K tiles, so wave
@@ -35,12 +44,15 @@ static constexpr int TM_QT = 2;
 template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
-                    const int32_t *__restrict__ q_tiles, int n_sel, float *__restrict__ out,
-                    float *__restrict__ lse_out, float *__restrict__ rowmax, Geo g, HeadShapes hs, RasterView rv) {
+                    const int32_t *__restrict__ q_tiles, int n_sel, int splits, float *__restrict__ rowmax,
+                    float2 *__restrict__ part, Geo g, HeadShapes hs, RasterView rv) {
+  // items ordered (b, h, key range, query-tile pair): each XCD walks consecutive pairs that
+  // sweep the same key tiles
   const int ngrp = (n_sel + TM_QT - 1) / TM_QT;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int a0 = (L % ngrp) * TM_QT;
-  const int64_t bh = L / ngrp;
+  const int sp = (L / ngrp) % splits;
+  const int64_t bh = L / (ngrp * splits);
   const int t = threadIdx.x, lane = t & 63, lr = lane & 31, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int qt = w >> 1;                     // which of the workgroup's query tiles
@@ -51,6 +63,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   // this head's tiles (fewer than nt for a head of a padded tiling with fewer tiles)
   const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;
   const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), nth - 1) : a;  // clamped
+  const int j0 = (int)((int64_t)nth * sp / splits), j1 = (int)((int64_t)nth * (sp + 1) / splits);  // key range
   const int64_t rhead = (int64_t)bb * rv.sb + (int64_t)hh * rv.sh;
   const __bf16 *qh = q + bh * (int64_t)g.N * 128;
   const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead
@@ -61,7 +74,6 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   float *rm = rowmax + (bh * n_sel + a) * (int64_t)g.nt * 128;   // [j][128 queries]
 
   __shared__ uint4 Kb[2][128 * 16];
-  __shared__ float lse_s[TM_QT][128];
 
   bf16x8_t qf[2][8];
 #pragma unroll
@@ -86,13 +98,13 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
   else
     tile_dma_offsets(w, lane, off);
   const uint32_t kb_lds[2] = {lds_addr(Kb[0]), lds_addr(Kb[1])};
-  tile_to_lds(k_tile(0), kb_lds[0], w, off);
-  if (nth > 1) tile_to_lds(k_tile(1), kb_lds[1], w, off);
+  if (j0 < j1) tile_to_lds(k_tile(j0), kb_lds[0], w, off);
+  if (j0 + 1 < j1) tile_to_lds(k_tile(j0 + 1), kb_lds[1], w, off);
 
   float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
-  for (int j = 0; j < nth; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nth)
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+    if (j + 1 < j1)
       wait_vmem<8>();  // tile j+1's copies may still be in flight
     else
       wait_vmem<0>();
@@ -135,7 +147,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
     }
     wait_lds();
     barrier();  // every wave has read this buffer
-    if (j + 2 < nth) tile_to_lds(k_tile(j + 2), kb_lds[buf], w, off);
+    if (j + 2 < j1) tile_to_lds(k_tile(j + 2), kb_lds[buf], w, off);
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -159,35 +171,60 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
       l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
   }
+  // this range's (m, l) per query row: l summed over both halves of the lane pair
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lse2 = m_run[qb] + log2f(l_run[qb] + __shfl_xor(l_run[qb], 32));
+    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const int qi = 64 * (w & 1) + 32 * qb + lr;
-    if (hi == 0) {
-      // a padding query row of a padded tiling stays out of the pooled maximum
-      lse_s[qt][qi] = PAD && !row_real(i, qi, pt, ph, pw, g.T, g.Hs, g.Ws) ? INFINITY : lse2;
-      if (lse_out != nullptr && owner) lse_out[(bh * n_sel + a) * 128 + qi] = lse2 * TM_LN2;
-    }
+    if (hi == 0 && owner) part[((bh * n_sel + a) * splits + sp) * 128 + qi] = make_float2(m_run[qb], l);
   }
-  __syncthreads();  // row maxima (global) and lse_s (LDS) visible to the workgroup
+}
 
-  // pass 2: M[j] = exp2(max over the tile's queries of rowmax - lse)
-  for (int e = t; e < TM_QT * g.nt; e += 256) {
-    const int qq = e / g.nt, j = e % g.nt;
-    if (a0 + qq >= n_sel) continue;
+// Pass 2, one workgroup per selected query tile: lse2[q] = log2 of the sum over the ranges of
+// l * 2^m, then M[j] = exp2(max over the tile's queries of rowmax[j][q] - lse2[q]).
+template <bool PAD>
+__global__ void __launch_bounds__(256) tilemap_pool_kernel(const float *__restrict__ rowmax,
+                                                           const float2 *__restrict__ part, int splits,
+                                                           const int32_t *__restrict__ q_tiles, int n_sel,
+                                                           float *__restrict__ out, float *__restrict__ lse_out,
+                                                           Geo g, HeadShapes hs) {
+  const int64_t bh = blockIdx.x;
+  const int a = blockIdx.y;
+  const int t = threadIdx.x, hh = (int)(bh % g.H);
+  const int pt = hs.s[hh][0], ph = hs.s[hh][1], pw = hs.s[hh][2];
+  const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;
+  __shared__ float lse_s[128];
+  if (t < 128) {
+    const float2 *pp = part + (bh * n_sel + a) * splits * 128 + t;
+    float m = -1e30f;
+    for (int s = 0; s < splits; ++s) m = fmaxf(m, pp[s * 128].x);
+    float l = 0.f;
+    for (int s = 0; s < splits; ++s) l += pp[s * 128].y * __builtin_amdgcn_exp2f(pp[s * 128].x - m);
+    const float lse2 = m + log2f(l);
+    if (lse_out != nullptr) lse_out[(bh * n_sel + a) * 128 + t] = lse2 * TM_LN2;
+    bool real = true;
+    if (PAD) {  // a padding query row of a padded tiling stays out of the pooled maximum
+      const int i = q_tiles ? min(max(q_tiles[bh * n_sel + a], 0), nth - 1) : a;
+      real = row_real(i, t, pt, ph, pw, g.T, g.Hs, g.Ws);
+    }
+    lse_s[t] = real ? lse2 : INFINITY;
+  }
+  __syncthreads();
+  for (int j = t; j < g.nt; j += 256) {
+    float *o = out + (bh * n_sel + a) * (int64_t)g.nt + j;
     if (j >= nth) {  // past this head's tiles
-      out[(bh * n_sel + a0 + qq) * (int64_t)g.nt + j] = 0.f;
+      *o = 0.f;
       continue;
     }
-    const float4 *src = reinterpret_cast<const float4 *>(rowmax + ((bh * n_sel + a0 + qq) * (int64_t)g.nt + j) * 128);
+    const float4 *src = reinterpret_cast<const float4 *>(rowmax + ((bh * n_sel + a) * (int64_t)g.nt + j) * 128);
     float x = -INFINITY;
 #pragma unroll 8
     for (int c = 0; c < 32; ++c) {
       const float4 v = src[c];
-      x = fmaxf(x, fmaxf(fmaxf(v.x - lse_s[qq][4 * c], v.y - lse_s[qq][4 * c + 1]),
-                         fmaxf(v.z - lse_s[qq][4 * c + 2], v.w - lse_s[qq][4 * c + 3])));
+      x = fmaxf(x, fmaxf(fmaxf(v.x - lse_s[4 * c], v.y - lse_s[4 * c + 1]),
+                         fmaxf(v.z - lse_s[4 * c + 2], v.w - lse_s[4 * c + 3])));
     }
-    out[(bh * n_sel + a0 + qq) * (int64_t)g.nt + j] = __builtin_amdgcn_exp2f(x);
+    *o = __builtin_amdgcn_exp2f(x);
   }
 }
 
@@ -247,18 +284,54 @@ __global__ void __launch_bounds__(64) tilemap_f32_kernel(const float *__restrict
   for (int j = t; j < g.nt; j += 64) out[(bh * n_sel + a) * (int64_t)g.nt + j] = expf(wm[j]);
 }
 
+// Key ranges per query-tile pair: the S in 1..TM_MAX_SPLITS for which the workgroups
+// (two per CU) fill their last round best; at most the smallest per-head tile count.
+static int tilemap_splits(int groups, const Geo &g, const HeadShapes &hs) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  const int64_t slots = 2 * (int64_t)cus[dev];
+  int nt_min = g.nt;
+  if (g.padded)
+    for (int h = 0; h < g.H; ++h) nt_min = std::min(nt_min, head_tiles(hs.s[h][0], hs.s[h][1], hs.s[h][2], g.T, g.Hs, g.Ws));
+  int best = 1;
+  double best_cost = (double)((groups + slots - 1) / slots);
+  for (int s = 2; s <= TM_MAX_SPLITS && s <= nt_min; ++s) {
+    const double cost = (double)(((int64_t)groups * s + slots - 1) / slots) / s;  // rounds, in whole-sweep units
+    if (cost < best_cost - 1e-9) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <bool RQ, bool RK>
 static void launch_tilemap_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
                              const void *k, float scale, const int32_t *q_tiles, int n_sel, float *tilemap,
                              float *lse, void *ws, hipStream_t st) {
-  const dim3 grid(((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B);
   if (dt == VEDA_BF16) {
-    if (!RQ && !RK && g.padded)
-      tilemap_bf16_kernel<false, false, true><<<grid, 256, 0, st>>>(
-          (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
-    else
-      tilemap_bf16_kernel<RQ, RK, false><<<grid, 256, 0, st>>>(
-          (const __bf16 *)q, (const __bf16 *)k, scale * TM_LOG2E, q_tiles, n_sel, tilemap, lse, (float *)ws, g, hs, rv);
+    const int groups = ((n_sel + TM_QT - 1) / TM_QT) * g.H * g.B;
+    const int splits = tilemap_splits(groups, g, hs);
+    float *rowmax = static_cast<float *>(ws);
+    float2 *part = reinterpret_cast<float2 *>(static_cast<char *>(ws) +
+                                              tm_align256((size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float)));
+    const dim3 grid(groups * splits), pgrid(g.H * g.B, n_sel);
+    const __bf16 *qq = (const __bf16 *)q, *kk = (const __bf16 *)k;
+    if (!RQ && !RK && g.padded) {
+      tilemap_bf16_kernel<false, false, true><<<grid, 256, 0, st>>>(qq, kk, scale * TM_LOG2E, q_tiles, n_sel, splits,
+                                                                    rowmax, part, g, hs, rv);
+      tilemap_pool_kernel<true><<<pgrid, 256, 0, st>>>(rowmax, part, splits, q_tiles, n_sel, tilemap, lse, g, hs);
+    } else {
+      tilemap_bf16_kernel<RQ, RK, false><<<grid, 256, 0, st>>>(qq, kk, scale * TM_LOG2E, q_tiles, n_sel, splits,
+                                                               rowmax, part, g, hs, rv);
+      tilemap_pool_kernel<false><<<pgrid, 256, 0, st>>>(rowmax, part, splits, q_tiles, n_sel, tilemap, lse, g, hs);
+    }
   } else
     tilemap_f32_kernel<RQ, RK><<<dim3(n_sel, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k, scale,
                                                                      q_tiles, n_sel, tilemap, lse, g, hs, rv);
