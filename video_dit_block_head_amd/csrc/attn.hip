@@ -36,6 +36,17 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t &a, const bf16x8_t &b,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine lanes l and l ^ 32 with v_permlane32_swap (a VALU op, no LDS round trip): with both
+// operands = v, the two results hold v[l % 32] and v[32 + l % 32] in every lane.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
 // the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
 // order; RK: the same for K.  Otherwise tile-major.  V is always channel-major tiled.
@@ -89,7 +100,10 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 #pragma unroll
     for (int e = 0; e < 8; ++e) koff[e] = off[e];
   const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
-  int jn = min(max(list[0], 0), last);  // out-of-range entries are clamped
+  // The kept list is read 64 entries at a time into one register (lane l holds entry 64c + l)
+  // and each step takes its entry with a readlane: no scalar load waits inside the loop.
+  int lchunk = list[min(lane, kk - 1)];
+  int jn = min(max(__builtin_amdgcn_readlane(lchunk, 0), 0), last);  // out-of-range entries are clamped
   tile_to_lds(k_tile(jn), ks_lds, w, koff);
   tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
 
@@ -124,19 +138,33 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[kb][r] = 0.f;
     }
+    // the four key blocks' accumulations in rotation, so that consecutive MFMAs are
+    // independent; operand reads run four MFMAs ahead
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = 32 * kb + lr;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (row & 15))]);
-        acc_s[kb] = mfma32(a, qf[s], acc_s[kb]);
-      }
+    for (int f = 0; f < 32; ++f) {
+      const int kb = f & 3, s = f >> 2, row = 32 * kb + lr;
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (lr & 15))]);
+      acc_s[kb] = mfma32(a, qf[s], acc_s[kb]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int f = 0; f < 28; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     wait_lds();
     barrier();  // every wave has its K operands: the buffer may be refilled
     if (more) {
-      jn = min(max(list[tt + 1], 0), last);
+      const int tn = tt + 1;
+      int e;
+      if ((tn & 63) == 0) {  // uniform, once per 64 steps (the load is waited for only here)
+        lchunk = list[min(tn + lane, kk - 1)];
+        e = __builtin_amdgcn_readlane(lchunk, 0);
+      } else {
+        e = __builtin_amdgcn_readlane(lchunk, tn & 63);
+      }
+      jn = min(max(e, 0), last);
       tile_to_lds(k_tile(jn), ks_lds, w, koff);
     }
 
@@ -146,7 +174,7 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    mx = half_max(mx) * c2;
     if (__ballot(mx > m_run + RESCALE_SLACK)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
@@ -191,12 +219,19 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
         acc_o[db] = mfma32(a, pb[s], acc_o[db]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // operand reads four MFMAs ahead
+#pragma unroll
+    for (int f = 0; f < 28; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     wait_lds();
     barrier();  // every wave has its V operands
     if (more) tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
   __bf16 *orow = RQ ? reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(o) + rhead + qtok * rv.sn)
                     : o + head + (int64_t)qrow * 128;
