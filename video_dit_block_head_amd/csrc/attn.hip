@@ -8,7 +8,9 @@
 //    straight into LDS (global_load_lds, no register staging) with the XOR swizzle
 //    "16-byte chunk c of row r at slot c ^ (r & 15)", which makes every MFMA operand read
 //    a conflict-free 16-byte LDS read.  K and V have their own buffers: the next K tile
-//    streams in during softmax + P V, the next V tile during the next Q K^T;
+//    streams in during softmax + P V, the next V tile during the next Q K^T.  Three
+//    barriers per key tile: K(t) read (K buffer free), V(t) complete, and V(t) read with
+//    K(t+1) complete;
 //  - S^T = K Q^T (32 keys x 32 queries per MFMA block) puts one query per lane column, so
 //    the row max needs one exchange between lane halves; O^T = V^T P^T keeps each lane's
 //    accumulators on its own query, so the online-softmax rescale is lane-local;
@@ -106,6 +108,8 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   int jn = min(max(__builtin_amdgcn_readlane(lchunk, 0), 0), last);  // out-of-range entries are clamped
   tile_to_lds(k_tile(jn), ks_lds, w, koff);
   tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
+  wait_vmem<8>();
+  barrier();  // K(0) is complete
 
   f32x16_t acc_o[4];
 #pragma unroll
@@ -118,8 +122,6 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
     const bool more = tt + 1 < kk;
     const int jc = jn;  // this step's key tile (jn moves on to the next one below)
     // ---- S^T = K Q^T on the K tile in LDS (its loads were issued before the V loads)
-    wait_vmem<8>();
-    barrier();
     f32x16_t acc_s[4];
     // A padding key of a partial tile (padded tilings only) starts at -inf: its K row is
     // zero, so the MFMAs leave it there and it gets no weight.  Entry (kb, r) of this lane
@@ -227,7 +229,8 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     wait_lds();
-    barrier();  // every wave has its V operands
+    wait_vmem<0>();  // this wave's part of K(t+1) has landed
+    barrier();       // every wave is done with V(t), and K(t+1) is complete
     if (more) tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
   }
 
