@@ -226,6 +226,16 @@ def main():
     score_ms = float(np.mean(per_stage["score_topk"]))
     say(f"[bench] step {ms_step:.2f} ms; stages (median ms) {json.dumps({s: round(x, 3) for s, x in med.items()})}")
 
+    # tile recall of the last step: the estimator's kept list against the oracle mask (the k
+    # largest entries of each sampled row of the max-pooled attention map), averaged over rows
+    est = sa.idx_buffer(kk).long()
+    est = torch.gather(est, 2, qtl.long()[..., None].expand(B, H, n_sel, kk)).reshape(-1, kk)
+    oidx = torch.empty((B, H, n_sel, kk), dtype=torch.int32, device="cuda")
+    V.veda_topk_mask(tmap, kk, oidx)
+    hit = torch.zeros((est.shape[0], nt), dtype=torch.float32, device="cuda").scatter_(1, est, 1.0)
+    recall = float(hit.gather(1, oidx.reshape(-1, kk).long()).sum()) / (est.shape[0] * kk)
+    torch.cuda.synchronize()
+
     # this library's own dense path (k = n_t, 0 % skipping), for the speedup
     dense = None
     if not args.no_dense:
@@ -372,6 +382,9 @@ def main():
         "scoring_gbps": round(score_bytes / (score_ms * 1e-3) / 1e9, 1),
         "scoring_frac_hbm_peak": round(score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "stages_median_ms": {s: round(x, 4) for s, x in med.items()},
+        "tile_recall": {"value": round(recall, 4), "k": kk, "sampled_query_tiles_per_head": n_sel,
+                        "chance": round(kk / nt, 4),
+                        "note": "estimator with the synthetic (untrained) MLP weights against the oracle mask"},
         "dense": dense,
         "next_rows": nxt,
         "roofline": roof,

@@ -152,13 +152,14 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ?
 // The k-th largest key is found bit by bit (largest T with count(key >= T) >= k), starting
 // below the bits that every valid key of the row shares, and stopping as soon as exactly k
 // keys are >= the candidate (that set is then the answer, whatever lies below).  Every later
-// candidate exceeds T, so only keys >= T can still be counted: once at most 128 of them are
-// left they are compacted (through `scratch`, 128 words of the wave's own LDS) into two
-// registers per lane, and the remaining bits cost two ballots instead of MAXM.
-template <int MAXM>
+// candidate exceeds T, so only keys >= T can still be counted: once at most 64 NC of them
+// are left they are compacted (through `scratch`, 64 NC words of the wave's own LDS) into NC
+// registers per lane, and the remaining bits cost NC ballots instead of MAXM.
+template <int MAXM, int NC = 2>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_cols, int k, int lane,
                                           int32_t *__restrict__ idx, uint8_t *__restrict__ mask,
                                           uint32_t *scratch) {
+  static_assert(NC >= 1 && NC <= 8, "compaction registers");
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) {
@@ -182,7 +183,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_col
     int alive = T != 0u ? n_cols : 64 * MAXM;
     bool done = false;
     int b = b0;
-    for (; b >= 0 && (MAXM <= 2 || alive > 128); --b) {
+    for (; b >= 0 && (MAXM <= NC || alive > 64 * NC); --b) {
       const uint32_t cand = T | (1u << b);
       int cnt = 0;
 #pragma unroll
@@ -196,20 +197,24 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[MAXM], int n_col
         break;
       }
     }
-    if (MAXM > 2 && !done && b >= 0) {
+    if (MAXM > NC && !done && b >= 0) {
       int base = 0;
 #pragma unroll
       for (int m = 0; m < MAXM; ++m) {
         const bool a = key[m] >= T;
         const uint64_t am = __ballot(a);
-        if (a) scratch[base + __popcll(am & lt)] = key[m];  // base + rank < alive <= 128
+        if (a) scratch[base + __popcll(am & lt)] = key[m];  // base + rank < alive <= 64 NC
         base += __popcll(am);
       }
       // padding 0 is never counted: every candidate is >= 1
-      const uint32_t c0 = lane < base ? scratch[lane] : 0u, c1 = 64 + lane < base ? scratch[64 + lane] : 0u;
+      uint32_t c[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) c[j] = 64 * j + lane < base ? scratch[64 * j + lane] : 0u;
       for (; b >= 0; --b) {
         const uint32_t cand = T | (1u << b);
-        const int cnt = __popcll(__ballot(c0 >= cand)) + __popcll(__ballot(c1 >= cand));
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) cnt += __popcll(__ballot(c[j] >= cand));
         if (cnt >= k) T = cand;
         if (cnt == k) break;
       }

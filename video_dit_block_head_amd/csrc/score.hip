@@ -239,17 +239,20 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 // ---------------------------------------------------------------------------------------
 // Scores for 16 query-tile rows: S = scale * y_q y_k^T on 16x16x4 fp32 MFMA (A[m = lane%16]
 // [k = lane/16], B[k = lane/16][n = lane%16], D[m = 4*(lane/16) + r][n = lane%16]); two
-// accumulation chains (even / odd k steps) summed at the end.  Then one wave per row.
-template <int MAXM>
-__global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict__ y, Geo g, float scale,
-                                                         float *__restrict__ scores, float *__restrict__ probs,
-                                                         int topk, int32_t *__restrict__ idx, HeadShapes hs) {
+// accumulation chains (even / odd k steps) summed at the end.  Then one wave per row: NW
+// waves take 16 / NW rows each.  Long rows (large MAXM) make the row block big enough that
+// only one workgroup fits a CU, so they use 16 waves, one row each, to keep every SIMD busy
+// through the latency-bound top-k.
+template <int MAXM, int NW>
+__global__ void __launch_bounds__(64 * NW) score_topk_kernel(const float *__restrict__ y, Geo g, float scale,
+                                                             float *__restrict__ scores, float *__restrict__ probs,
+                                                             int topk, int32_t *__restrict__ idx, HeadShapes hs) {
   constexpr int SW = 64 * MAXM + 1;
   __shared__ float S[16 * SW];
   const int nt = g.nt, nrb = (nt + 15) >> 4;
   const int L = xcd_tile(blockIdx.x, gridDim.x);  // each XCD walks contiguous heads
   const int i0 = (L % nrb) * 16, h = (L / nrb) % g.H, b = L / (nrb * g.H);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   // rows and columns of this head (fewer than nt for a head of a padded tiling with fewer tiles)
   const int nth = g.padded ? head_tiles(hs.s[h][0], hs.s[h][1], hs.s[h][2], g.T, g.Hs, g.Ws) : nt;
   const float *yq = y + (((int64_t)b * g.H + h) * nt) * MLP_OUT;
@@ -264,22 +267,22 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
     for (int e = 0; e < 4; ++e) qa[e] = qr[e];
   }
   const int nblk = (nt + 15) >> 4;
-  // Key blocks w, w + 4, w + 8, ... of this wave, loaded SD blocks ahead (a ring of SD
+  // Key blocks w, w + NW, w + 2 NW, ... of this wave, loaded SD blocks ahead (a ring of SD
   // register buffers indexed by constants: the loop is unrolled SD times).
   constexpr int SD = 3;
   float4 kv[SD][4];
 #pragma unroll
   for (int u = 0; u < SD; ++u) {
-    const int kb = w + 4 * u;
+    const int kb = w + NW * u;
     const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)min(16 * kb + m, nt - 1) * MLP_OUT + 16 * kq);
 #pragma unroll
     for (int e = 0; e < 4; ++e) kv[u][e] = kr[e];   // clamped rows: always in bounds
   }
 #pragma unroll 1
-  for (int kb0 = w; kb0 < nblk; kb0 += 4 * SD) {
+  for (int kb0 = w; kb0 < nblk; kb0 += NW * SD) {
 #pragma unroll
     for (int u = 0; u < SD; ++u) {
-      const int kb = kb0 + 4 * u;
+      const int kb = kb0 + NW * u;
       if (kb < nblk) {  // wave-uniform
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -292,7 +295,7 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
         const int key = 16 * kb + m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[(4 * kq + r) * SW + key] = (a0[r] + a1[r]) * scale;
-        const int kn = kb + 4 * SD;
+        const int kn = kb + NW * SD;
         if (kn < nblk) {
           const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)(16 * kn + m < nt ? 16 * kn + m : nt - 1) *
                                                                        MLP_OUT + 16 * kq);
@@ -304,8 +307,8 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
   }
   __syncthreads();
 #pragma unroll 1
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * w + rr, i = i0 + row;
+  for (int rr = 0; rr < 16 / NW; ++rr) {
+    const int row = (16 / NW) * w + rr, i = i0 + row;
     if (i >= nth) break;  // wave-uniform
     const int64_t grow = ((int64_t)b * g.H + h) * nt + i;
     float sc[MAXM];
@@ -339,7 +342,9 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const float *__restrict
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nth) ? float_key(sc[mm]) : 0u;
       // the row is in registers now: its LDS words serve as the wave's top-k scratch
-      wave_topk<MAXM>(key, nth, topk, lane, idx + grow * topk, nullptr, reinterpret_cast<uint32_t *>(&S[row * SW]));
+      // long rows compact up to 512 candidates (so that k up to 512 reaches the cheap phase)
+      wave_topk<MAXM, (MAXM >= 16 ? 8 : 2)>(key, nth, topk, lane, idx + grow * topk, nullptr,
+                                             reinterpret_cast<uint32_t *>(&S[row * SW]));
     }
   }
 }
@@ -365,8 +370,9 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
 template <int MAXM>
 static void launch_score_t(const Geo &g, const float *y, float scale, float *scores, float *probs, int topk,
                            int32_t *idx, const HeadShapes &hs, hipStream_t st) {
-  score_topk_kernel<MAXM><<<dim3(((g.nt + 15) / 16) * g.H * g.B), 256, 0, st>>>(y, g, scale, scores, probs, topk,
-                                                                                 idx, hs);
+  constexpr int NW = MAXM >= 16 ? 16 : (MAXM >= 10 ? 8 : 4);
+  score_topk_kernel<MAXM, NW><<<dim3(((g.nt + 15) / 16) * g.H * g.B), 64 * NW, 0, st>>>(y, g, scale, scores, probs,
+                                                                                       topk, idx, hs);
 }
 
 template <int EB, bool RQ, bool RK>
