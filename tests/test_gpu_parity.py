@@ -241,8 +241,17 @@ def test_sparsity_sweep(r):
     cfg = r.cfg
     if len(cfg.topk) < 3:
         pytest.skip("no sparsity sweep for this workload")
+    # the selections themselves, on one head: every row against the oracle's fp32 scores
+    # (k up to 240 exercises the compacted search over up to 512 candidates on long rows)
+    h = int(r.heads(1)[0])
+    qt, kt, _, _ = r.oracle_head(0, h)
+    s32 = O.tile_scores(O.mlp(O.trippool(qt, cfg.tile), r.wl.w1[h], r.wl.w2[h]),
+                        O.mlp(O.trippool(kt, cfg.tile), r.wl.w1[h], r.wl.w2[h]), cfg.score_scale).astype(np.float32)
     for kk in cfg.topk[1:-1]:
         idx = r.sa.score(kk)
+        got = host(idx[0, h]).astype(np.int64)
+        for i in range(cfg.n_tiles):
+            assert O.topk_agrees(s32[i], got[i], kk)[0], (cfg.name, kk, h, i)
         o_t = torch.empty_like(r.sa.o_t)
         say(f"[gpu-parity] {cfg.name}: k={kk}")
         V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, kk, 1 / math.sqrt(cfg.head_dim), o_t)
