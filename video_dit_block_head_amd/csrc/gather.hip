@@ -37,25 +37,49 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(uint8_t *__restrict__ 
   }
 }
 
-// Column layout, bf16: each thread moves one 8-position x 8-channel block, transposing it
-// in registers, so that each tile is written channel-major ([d][P]) with the key order of
-// cols_key().  Reads of a token row are coalesced across the 16 lanes that share the row.
+// Column layout, bf16, through LDS so that both sides are coalesced: the 256 threads first
+// copy the tile's 128 token rows into LDS (16 lanes per 256-byte row, chunk c of row o at slot
+// c ^ cols_slot(o)); then each thread gathers one 8-position x 8-channel block (eight 16-byte
+// LDS reads), transposes it in registers and writes 8 channel rows; the 16 lanes that share a
+// channel row write it whole (256 contiguous bytes).  The swizzle gives the 16 rows that one
+// read instruction touches per channel block 16 different slots, so neither the copy in nor
+// the reads out have bank conflicts.  Each tile is written channel-major ([d][P]) with the
+// key order of cols_key().
+__device__ __forceinline__ int cols_slot(int o) { return (((o >> 4) << 1) | ((o >> 2) & 1)) & 15; }
+
 __global__ void __launch_bounds__(256) gather_cols_bf16_kernel(const uint16_t *__restrict__ raster, int64_t rs_b,
                                                                int64_t rs_n, int64_t rs_h,
                                                                uint16_t *__restrict__ tiled, Geo g, HeadShapes hs) {
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
-  const int cb = threadIdx.x & 15, tb = threadIdx.x >> 4;  // channel block, token block
+  const int t = threadIdx.x;
   const bool in_head = !g.padded || j < head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws);
+  __shared__ uint4 tile[128 * 16];
+  {
+    const int c = t & 15, r0 = t >> 4;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = r0 + 16 * i;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);  // padding rows are zero
+      if (!g.padded || (in_head && row_real(j, o, pt, ph, pw, g.T, g.Hs, g.Ws))) {
+        const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
+        v[i] = *reinterpret_cast<const uint4 *>(raster + b * rs_b + n * rs_n + h * rs_h + c * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = r0 + 16 * i;
+      tile[o * 16 + (c ^ cols_slot(o))] = v[i];
+    }
+  }
+  __syncthreads();
+  const int tb = t & 15, cb = t >> 4;  // position block (8 keys), channel block (8 channels)
   uint32_t in[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int o = cols_key(tb * 8 + i);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);  // padding rows are zero
-    if (!g.padded || (in_head && row_real(j, o, pt, ph, pw, g.T, g.Hs, g.Ws))) {
-      const int64_t n = tile_row_token(j, o, pt, ph, pw, g.Hs, g.Ws);
-      v = *reinterpret_cast<const uint4 *>(raster + b * rs_b + n * rs_n + h * rs_h + cb * 8);
-    }
+    const uint4 v = tile[o * 16 + (cb ^ cols_slot(o))];
     in[i][0] = v.x;
     in[i][1] = v.y;
     in[i][2] = v.z;
