@@ -19,10 +19,12 @@
 //                         row's contribution g_a = score_scale * dL/ds_a . y_k
 //   dyq_kernel            dy_q[i] = sum of g_a over the rows a sampling tile i
 //   dyk_kernel            dy_k[j] (one wave per key tile)
-//   mlp_bwd_rows_kernel   per 32 rows: Z1 = D W1, H1 = GELU(Z1), dZ1 = (dy W2^T) GELU'(Z1)
-//   atb_kernel            dW1 = D^T dZ1 and dW2 = H1^T dy per head, 64 x 64 output tiles
+//   mlp_bwd_rows_kernel   per 32 rows: H1 = GELU(Z1), dZ1 = (dy W2^T) GELU'(Z1), with the
+//                         pre-activation Z1 = D W1 kept by the forward pooling kernel
+//   atb_mfma_kernel       dW1 = D^T dZ1 and dW2 = H1^T dy per head on fp32 MFMA, 64 x 64
+//                         tiles, four waves per tile over quarters of the rows
 //   loss_kernel, sgd_kernel
-// The step is small next to the forward path (a few GFLOP); plain fp32 VALU arithmetic.
+// The step is small next to the forward path (a few GFLOP); fp32 throughout.
 #include "common.h"
 #include "kernels.h"
 
@@ -160,39 +162,27 @@ __global__ void __launch_bounds__(64) dyk_kernel(const int32_t *__restrict__ q_t
   dy[((kbase + bh) * g.nt + j) * DS_OUT + c] = acc * scale;
 }
 
-// 32 rows of one (Q|K, b, h): Z1 = D W1 (thread u = hidden unit u), H1 = GELU(Z1),
+// 32 rows of one (Q|K, b, h), thread u = hidden unit u: the forward pass left the
+// pre-activation Z1 = D W1 in h1; this replaces it by H1 = GELU(Z1) and writes
 // dZ1 = (dy W2^T) * GELU'(Z1).
-__global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restrict__ desc, const float *__restrict__ dy,
-                                                           const float *__restrict__ w1, const float *__restrict__ w2,
+__global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restrict__ dy, const float *__restrict__ w2,
                                                            float *__restrict__ h1, float *__restrict__ dz1, Geo g) {
-  const int d3 = 3 * g.d;
-  extern __shared__ float sm[];  // [32][3d] descriptors, then [32][64] dy
-  float *Dl = sm, *Yl = sm + 32 * d3;
+  __shared__ float Yl[32 * DS_OUT];  // dy of the 32 rows
   const int ngrp = (g.nt + 31) / 32;
   const int grp = blockIdx.x % ngrp;
-  const int64_t wbh = blockIdx.x / ngrp;         // (which*B + b)*H + h
+  const int64_t wbh = blockIdx.x / ngrp;  // (which*B + b)*H + h
   const int h = (int)(wbh % g.H);
   const int r0 = grp * 32, nr = min(32, g.nt - r0);
   const int u = threadIdx.x;
-  for (int e = u; e < 32 * d3; e += 256) {
-    const int r = e / d3;
-    Dl[e] = r < nr ? desc[(wbh * g.nt + r0 + r) * d3 + e % d3] : 0.f;
-  }
   for (int e = u; e < 32 * DS_OUT; e += 256) {
     const int r = e / DS_OUT;
     Yl[e] = r < nr ? dy[(wbh * g.nt + r0 + r) * DS_OUT + e % DS_OUT] : 0.f;
   }
-  __syncthreads();
-  const float *W1 = w1 + (int64_t)h * d3 * DS_HID + u;
-  const float *W2 = w2 + ((int64_t)h * DS_HID + u) * DS_OUT;
   float z[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) z[r] = 0.f;
-  for (int f = 0; f < d3; ++f) {
-    const float wv = W1[(int64_t)f * DS_HID];
-#pragma unroll
-    for (int r = 0; r < 32; ++r) z[r] = fmaf(Dl[r * d3 + f], wv, z[r]);
-  }
+  for (int r = 0; r < 32; ++r) z[r] = r < nr ? h1[(wbh * g.nt + r0 + r) * DS_HID + u] : 0.f;
+  __syncthreads();
+  const float *W2 = w2 + ((int64_t)h * DS_HID + u) * DS_OUT;
   float dh[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) dh[r] = 0.f;
@@ -211,55 +201,78 @@ __global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restri
   }
 }
 
-// C[h] (M x N) = sum over rows of A[row][m] * B[row][n], rows = the 2*B segments (Q|K, b)
-// of n_t rows of head h; A has row stride lda, B row stride ldb (floats); 64 x 64 tiles,
-// 4 x 4 outputs per thread, rows staged 16 at a time in LDS.
-__global__ void __launch_bounds__(256) atb_kernel(const float *__restrict__ A, int lda, const float *__restrict__ Bm,
-                                                  int ldb, int M, int N, float *__restrict__ C, Geo g) {
-  __shared__ float As[16][64 + 4], Bs[16][64 + 4];
+// C[h] (M x N) = sum over rows of A[row][m] * B[row][n], rows = the 2*B segments (Q|K, b) of
+// n_t rows of head h (A row stride lda, B row stride ldb, floats), on fp32 MFMA 32x32x2
+// (A[m = lane%32][k = lane/32], B[k = lane/32][n = lane%32], D[m = 8*(r/4) + 4*(lane/32) + r%4]
+// [n = lane%32]).  One workgroup per 64 x 64 output tile (2 x 2 blocks): each of its four
+// waves sums a contiguous quarter of the rows, two rows per step, with the operands loaded
+// PF steps ahead in register rings; wave 0 then adds the four partial tiles in wave order.
+// Every sum runs in a fixed order, so the result is deterministic.  M and N are multiples
+// of 64.
+__global__ void __launch_bounds__(256) atb_mfma_kernel(const float *__restrict__ A, int lda,
+                                                       const float *__restrict__ Bm, int ldb, int M, int N,
+                                                       float *__restrict__ C, Geo g) {
+  constexpr int PF = 8;
+  __shared__ float red[3][4][16][64];  // partial tiles of waves 1..3: [wave][block][r][lane]
   const int tm = blockIdx.x, tn = blockIdx.y, h = blockIdx.z;
-  const int t = threadIdx.x, ti = t >> 4, tj = t & 15;
-  float acc[4][4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, lr = lane & 31, kh = lane >> 5;
+  const int half = (g.nt + 1) >> 1, nsteps = 2 * g.B * half;
+  const int q4 = (nsteps + 3) / 4, s_begin = wv * q4, s_end = min(nsteps, s_begin + q4);  // this wave's steps
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-  const int nseg = 2 * g.B;
-  for (int sgm = 0; sgm < nseg; ++sgm) {
-    const int64_t rbase = ((int64_t)sgm * g.H + h) * g.nt;  // (which*B + b)*H + h
-    for (int r0 = 0; r0 < g.nt; r0 += 16) {
-      __syncthreads();
-      for (int e = t; e < 16 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        const bool ok = r0 + r < g.nt;
-        const int m = 64 * tm + c, n = 64 * tn + c;
-        As[r][c] = ok && m < M ? A[(rbase + r0 + r) * lda + m] : 0.f;
-        Bs[r][c] = ok && n < N ? Bm[(rbase + r0 + r) * ldb + n] : 0.f;
-      }
-      __syncthreads();
-#pragma unroll 4
-      for (int r = 0; r < 16; ++r) {
-        float av[4], bv[4];
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) av[a] = As[r][4 * ti + a];
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+  const float *Ab = A + 64 * tm + lr, *Bb = Bm + 64 * tn + lr;
+  auto load = [&](int s, float (&av)[2], float (&bv)[2]) {
+    const int sg = s / half, row = 2 * (s - sg * half) + kh;  // segment (Q|K, b) and row of step s
+    const bool ok = s < s_end && row < g.nt;
+    const int64_t rr = ok ? ((int64_t)sg * g.H + h) * g.nt + row : 0;  // clamped: always in bounds
+    av[0] = Ab[rr * lda];
+    av[1] = Ab[rr * lda + 32];
+    bv[0] = Bb[rr * ldb];
+    bv[1] = Bb[rr * ldb + 32];
+    if (!ok) av[0] = av[1] = 0.f;
+  };
+  float ar[PF][2], br[PF][2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bv[b] = Bs[r][4 * tj + b];
+  for (int p = 0; p < PF; ++p) load(s_begin + p, ar[p], br[p]);
+#pragma unroll 1
+  for (int s0 = s_begin; s0 < s_end; s0 += PF) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
-      }
+    for (int p = 0; p < PF; ++p) {
+      const float a0 = ar[p][0], a1 = ar[p][1], b0 = br[p][0], b1 = br[p][1];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      load(s0 + p + PF, ar[p], br[p]);
+      __builtin_amdgcn_sched_barrier(0);  // keep each load a full ring ahead of its use
     }
   }
+  // the four waves' partial sums, added in wave order by wave 0
+  if (wv > 0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int m = 64 * tm + 4 * ti + a;
-    if (m >= M) continue;
+    for (int bk = 0; bk < 4; ++bk)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int n = 64 * tn + 4 * tj + b;
-      if (n < N) C[((int64_t)h * M + m) * N + n] = acc[a][b];
-    }
+      for (int r = 0; r < 16; ++r) red[wv - 1][bk][r][lane] = acc[bk >> 1][bk & 1][r];
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[mb][nb][r];
+#pragma unroll
+          for (int o = 0; o < 3; ++o) v += red[o][2 * mb + nb][r][lane];
+          const int m = 64 * tm + 32 * mb + 8 * (r >> 2) + 4 * kh + (r & 3), n = 64 * tn + 32 * nb + lr;
+          C[((int64_t)h * M + m) * N + n] = v;
+        }
   }
 }
 
@@ -302,7 +315,9 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
   const int d3 = 3 * g.d;
   const size_t desc_half = (size_t)g.B * g.H * g.nt * d3;
   // forward: descriptors and MLP outputs of every Q and K tile (shared weights)
-  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st);
+  // (the pre-activation hidden layer goes to h1, which the backward rows kernel turns into GELU)
+  const hipError_t pe =
+      launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st, nullptr, nullptr, false, w.h1);
   if (pe != hipSuccess) return pe;
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
   const float inv_rows = 1.0f / (float)rows;
@@ -318,10 +333,11 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
   dyq_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.gq, w.dy, g);
   dyk_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.ds, w.y, score_scale, w.dy, g);
   const int ngrp = (g.nt + 31) / 32;
-  const size_t smem = (size_t)(32 * d3 + 32 * DS_OUT) * sizeof(float);
-  mlp_bwd_rows_kernel<<<dim3(ngrp * 2 * g.B * g.H), 256, smem, st>>>(w.desc, w.dy, w1, w2, w.h1, w.dz1, g);
-  atb_kernel<<<dim3((d3 + 63) / 64, DS_HID / 64, g.H), 256, 0, st>>>(w.desc, d3, w.dz1, DS_HID, d3, DS_HID, dw1, g);
-  atb_kernel<<<dim3(DS_HID / 64, 1, g.H), 256, 0, st>>>(w.h1, DS_HID, w.dy, DS_OUT, DS_HID, DS_OUT, dw2, g);
+  mlp_bwd_rows_kernel<<<dim3(ngrp * 2 * g.B * g.H), 256, 0, st>>>(w.dy, w2, w.h1, w.dz1, g);
+  // 3d is 384 (bf16) or 192 (fp32): both multiples of the 64-wide output tile
+  atb_mfma_kernel<<<dim3(d3 / 64, DS_HID / 64, g.H), 256, 0, st>>>(w.desc, d3, w.dz1, DS_HID, d3, DS_HID, dw1, g);
+  atb_mfma_kernel<<<dim3(DS_HID / 64, DS_OUT / 64, g.H), 256, 0, st>>>(w.h1, DS_HID, w.dy, DS_OUT, DS_HID, DS_OUT, dw2,
+                                                                       g);
   loss_kernel<<<1, 256, 0, st>>>(w.loss, rows, loss);
   if (lr != 0.f) {
     const int64_t n1 = (int64_t)g.H * d3 * DS_HID, n2 = (int64_t)g.H * DS_HID * DS_OUT;

@@ -17,11 +17,12 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
                         void *ws, hipStream_t st, const HeadShapes *hs = nullptr, const RasterView *rv = nullptr,
                         bool k_raster = false);
 
-// TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL.
+// TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL;
+// the pre-activation hidden layer z [Q|K][B][H][n_t][256] if non-NULL.
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs = nullptr,
-                           const RasterView *rv = nullptr, bool k_raster = false);
+                           const RasterView *rv = nullptr, bool k_raster = false, float *z = nullptr);
 
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);

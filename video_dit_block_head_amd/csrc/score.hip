@@ -51,8 +51,8 @@ template <int EB, bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
-                float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, Geo g, HeadShapes hs,
-                RasterView rv) {
+                float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, float *__restrict__ zout,
+                Geo g, HeadShapes hs, RasterView rv) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
@@ -201,6 +201,17 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
       const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
       Ds[row * PM_HST + 64 * w + m] = gelu_erf(acc0[r]);
       Ds[row * PM_HST + 64 * w + 32 + m] = gelu_erf(acc1[r]);
+    }
+    if (zout != nullptr) {  // the pre-activation layer, for the estimator's backward pass
+      float *zo = zout + ((((int64_t)which * g.B + b) * g.H + h) * g.nt + r0) * MLP_HIDDEN + 64 * w + m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (r0 + row < g.nt) {
+          zo[(int64_t)row * MLP_HIDDEN] = acc0[r];
+          zo[(int64_t)row * MLP_HIDDEN + 32] = acc1[r];
+        }
+      }
     }
   }
   __syncthreads();
@@ -378,38 +389,38 @@ static void launch_score_t(const Geo &g, const float *y, float scale, float *sco
 template <int EB, bool RQ, bool RK>
 static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
-                              float *q_desc, float *k_desc, hipStream_t st) {
+                              float *q_desc, float *k_desc, float *z, hipStream_t st) {
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
   if (!RQ && !RK && g.padded)
     pool_mlp_kernel<EB, false, false, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k,
-                                                                w2k, y, q_desc, k_desc, g, hs, rv);
+                                                                w2k, y, q_desc, k_desc, z, g, hs, rv);
   else
     pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
-                                                           y, q_desc, k_desc, g, hs, rv);
+                                                           y, q_desc, k_desc, z, g, hs, rv);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
-                           bool k_raster) {
+                           bool k_raster, float *z) {
   const HeadShapes hs0 = hs != nullptr ? *hs : HeadShapes{};  // tiled operands: shapes matter only when padded
   const RasterView rv0{0, 0, 0};
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
     if (bf)
-      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
     else
-      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
   } else if (k_raster) {
     if (bf)
-      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
     else
-      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
   } else {
     if (bf)
-      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
     else
-      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st);
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
   }
   return hipGetLastError();
 }
