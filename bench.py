@@ -236,6 +236,21 @@ def main():
     recall = float(hit.gather(1, oidx.reshape(-1, kk).long()).sum()) / (est.shape[0] * kk)
     torch.cuda.synchronize()
 
+    # the scoring pass with the probability matrix written too (B*H*n_t^2 floats more)
+    probs = torch.empty((B, H, nt, nt), dtype=torch.float32, device="cuda")
+    score_p = (lambda: sa.score(kk, probs=probs)) if args.path == "tiled" else (lambda: sa.score_raster(q, kk, probs=probs))
+    score_p()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        score_p()
+    e1.record()
+    torch.cuda.synchronize()
+    score_p_ms = e0.elapsed_time(e1) / 10
+    score_p_bytes = score_bytes + B * H * nt * nt * 4
+    del probs
+
     # this library's own dense path (k = n_t, 0 % skipping), for the speedup
     dense = None
     if not args.no_dense:
@@ -381,6 +396,9 @@ def main():
         "scoring_ms": round(score_ms, 4),
         "scoring_gbps": round(score_bytes / (score_ms * 1e-3) / 1e9, 1),
         "scoring_frac_hbm_peak": round(score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "scoring_with_probs": {"ms": round(score_p_ms, 4), "gbps": round(score_p_bytes / (score_p_ms * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(score_p_bytes / (score_p_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                               "bytes": score_p_bytes},
         "stages_median_ms": {s: round(x, 4) for s, x in med.items()},
         "tile_recall": {"value": round(recall, 4), "k": kk, "sampled_query_tiles_per_head": n_sel,
                         "chance": round(kk / nt, 4),
