@@ -214,7 +214,7 @@ veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, con
                                        float *lse, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
- * gradients of every Q and K tile, per-row KL terms). */
+ * gradients of the sampled Q tiles and of every K tile, per-row KL terms). */
 size_t veda_distill_workspace_bytes(const veda_geom *g, int32_t n_sel);
 
 /* One distillation step of the per-head tile-score estimator.  [Technical Summary §2.1

@@ -32,10 +32,12 @@ def to_dev_raster(arr_hm, bf16):
     return t.permute(0, 2, 1, 3).contiguous()
 
 
-CASES = [("tiny", 2, "map"), ("small", 8, "map"), ("mid", 16, "random")]
+# "dup": sampled with replacement and with a repeated tile in every (b, h) list (a tile
+# sampled twice counts twice: two KL rows, two gradient contributions)
+CASES = [("tiny", 2, "map"), ("small", 8, "map"), ("mid", 16, "random"), ("small", 8, "dup")]
 
 
-@pytest.mark.parametrize("name,n_sel,target_kind", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("name,n_sel,target_kind", CASES, ids=[f"{c[0]}-{c[2]}" for c in CASES])
 def test_distill_step_vs_oracle(name, n_sel, target_kind):
     cfg = get(name)
     say(f"[gpu-distill] {name}: generating")
@@ -48,7 +50,15 @@ def test_distill_step_vs_oracle(name, n_sel, target_kind):
     q, k, v = (to_dev_raster(a, bf16) for a in (wl.q, wl.k, wl.v))
     sa.gather(q, k, v)
     rng = np.random.default_rng(cfg.seed + 500)
-    sel = np.stack([np.stack([np.sort(rng.choice(nt, n_sel, replace=False)) for _ in range(H)]) for _ in range(B)])
+    if target_kind == "dup":
+        def pick():
+            x = rng.choice(nt, n_sel, replace=True)
+            x[-1] = x[0]  # at least one repeat
+            return np.sort(x)
+    else:
+        def pick():
+            return np.sort(rng.choice(nt, n_sel, replace=False))
+    sel = np.stack([np.stack([pick() for _ in range(H)]) for _ in range(B)])
     # oracle side: descriptors of the tiled inputs, targets
     descs, q_tiles, targets = {}, {}, {}
     for b in range(B):

@@ -5,19 +5,20 @@
 //
 // For every sampled query tile a (tile i = q_tiles[b, h, a]) of every head:
 //   p_a = M[b, h, a, :] / sum_j M[b, h, a, j]        (max-pooled map, normalised per row)
-//   s_a = score_scale * y_q[i] . y_k[:]              (estimator logits of that row)
+//   s_a = score_scale * y_q[a] . y_k[:]              (estimator logits; y_q[a] is tile i's)
 //   L   = mean over all B*H*n_sel rows of KL(p_a || softmax(s_a))
 // and the gradients of L with respect to W1 [H, 3d, 256] and W2 [H, 256, 64] (one MLP per
 // head, shared by the Q-tile and K-tile descriptors), y = GELU(D W1) W2.
 //   dL/ds_a = (softmax(s_a) - p_a) / R
-//   dy_q[i] = score_scale * sum over the rows a of tile i of dL/ds_a . y_k
-//   dy_k[j] = score_scale * sum_a dL/ds_a[j] y_q[i_a]
-//   dW2 = sum over Q and K rows of H1^T dy,  dZ1 = (dy W2^T) * GELU'(Z1),  dW1 = sum D^T dZ1
+//   dy of Q row a (one row per list entry; an unlisted Q tile gets no gradient, and a tile
+//            listed twice has two rows) = score_scale * dL/ds_a . y_k
+//   dy_k[j] = score_scale * sum_a dL/ds_a[j] y_q[a]
+//   dW2 = sum over the Q and K rows of H1^T dy,  dZ1 = (dy W2^T) * GELU'(Z1),  dW1 = sum D^T dZ1
 // Kernels (all deterministic: fixed-order reductions, no atomics):
-//   pool_mlp (score.hip)  descriptors D and outputs y of every Q and K tile
+//   pool_mlp (score.hip)  descriptors D, pre-activations Z1 and outputs y of the listed Q
+//                         tiles and of every K tile
 //   kl_grad_kernel        one wave per sampled row: logits, softmax, KL, dL/ds, and that
-//                         row's contribution g_a = score_scale * dL/ds_a . y_k
-//   dyq_kernel            dy_q[i] = sum of g_a over the rows a sampling tile i
+//                         row's dy = score_scale * dL/ds_a . y_k
 //   dyk_kernel            dy_k[j] (one wave per key tile)
 //   mlp_bwd_rows_kernel   per 32 rows: H1 = GELU(Z1), dZ1 = (dy W2^T) GELU'(Z1), with the
 //                         pre-activation Z1 = D W1 kept by the forward pooling kernel
@@ -35,17 +36,17 @@ static constexpr int DS_HID = 256, DS_OUT = 64;
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout (floats): y [2][B][H][n_t][64] | D [2][B][H][n_t][3d] | dS [B][H][n_sel][n_t]
-// | G [B][H][n_sel][64] | dY [2][B][H][n_t][64] | H1 [2][B][H][n_t][256] | dZ1 (same) | loss [B*H*n_sel]
+// | dY [2][B][H][n_t][64] | H1 [2][B][H][n_t][256] | dZ1 (same) | loss [B*H*n_sel].  In the Q
+// half of y, D, dY, H1 and dZ1, row a of a (b, h) block is list entry a (n_sel <= n_t rows).
 struct DistillWs {
-  float *y, *desc, *ds, *gq, *dy, *h1, *dz1, *loss;
+  float *y, *desc, *ds, *dy, *h1, *dz1, *loss;
 };
 
 static size_t ws_parts(const Geo &g, int n_sel, size_t *off) {
   const size_t rows = 2 * (size_t)g.B * g.H * g.nt, sel = (size_t)g.B * g.H * n_sel;
-  const size_t sz[8] = {rows * DS_OUT, rows * 3 * g.d, sel * g.nt, sel * DS_OUT,
-                        rows * DS_OUT, rows * DS_HID, rows * DS_HID, sel};
+  const size_t sz[7] = {rows * DS_OUT, rows * 3 * g.d, sel * g.nt, rows * DS_OUT, rows * DS_HID, rows * DS_HID, sel};
   size_t o = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 7; ++i) {
     off[i] = o;
     o += al256(sz[i] * sizeof(float));
   }
@@ -53,7 +54,7 @@ static size_t ws_parts(const Geo &g, int n_sel, size_t *off) {
 }
 
 size_t distill_workspace_bytes(const Geo &g, int n_sel) {
-  size_t off[8];
+  size_t off[7];
   return ws_parts(g, n_sel, off);
 }
 
@@ -65,9 +66,9 @@ __device__ __forceinline__ float gelu_grad(float x) {
 
 // One wave per sampled row (b, h, a); 4 rows per workgroup.
 template <int MAXM>
-__global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ y, const int32_t *__restrict__ q_tiles,
-                                                      int n_sel, const float *__restrict__ target, float scale,
-                                                      float inv_rows, float *__restrict__ ds, float *__restrict__ gq,
+__global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ y, int n_sel,
+                                                      const float *__restrict__ target, float scale,
+                                                      float inv_rows, float *__restrict__ ds, float *__restrict__ dyq,
                                                       float *__restrict__ loss_rows, Geo g) {
   __shared__ float dsl[4][64 * MAXM];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -75,8 +76,8 @@ __global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ 
   if (row >= (int64_t)g.B * g.H * n_sel) return;      // whole wave; no barrier follows
   const int64_t bh = row / n_sel;
   const int nt = g.nt;
-  const int i = min(max(q_tiles[row], 0), nt - 1);
-  const float *yq = y + (bh * nt + i) * DS_OUT;
+  const int64_t a = row - bh * n_sel;       // list position: the Q rows are the listed tiles
+  const float *yq = y + (bh * nt + a) * DS_OUT;
   const float *yk = y + (((int64_t)g.B * g.H + bh) * nt) * DS_OUT;
   const float *m = target + row * nt;
   float s[MAXM], mt[MAXM];
@@ -131,48 +132,33 @@ __global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ 
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   float acc = 0.f;
   for (int j = 0; j < nt; ++j) acc = fmaf(dsl[wv][j], yk[(int64_t)j * DS_OUT + lane], acc);
-  gq[row * DS_OUT + lane] = acc * scale;
+  dyq[(bh * nt + a) * DS_OUT + lane] = acc * scale;  // dy of Q row a (one row per list entry)
 }
 
-// dy_q[b, h, i][c] = sum over the sampled rows a with tile i of g_a[c], in order of a.
-__global__ void __launch_bounds__(64) dyq_kernel(const int32_t *__restrict__ q_tiles, int n_sel,
-                                                 const float *__restrict__ gq, float *__restrict__ dy, Geo g) {
-  const int i = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int c = threadIdx.x;
-  float acc = 0.f;
-  for (int a = 0; a < n_sel; ++a)
-    if (min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1) == i) acc += gq[(bh * n_sel + a) * DS_OUT + c];
-  dy[(bh * g.nt + i) * DS_OUT + c] = acc;
-}
-
-// dy_k[b, h, j][c] = scale * sum_a dS[a][j] y_q[i_a][c], in order of a.
-__global__ void __launch_bounds__(64) dyk_kernel(const int32_t *__restrict__ q_tiles, int n_sel,
-                                                 const float *__restrict__ ds, const float *__restrict__ y,
+// dy_k[b, h, j][c] = scale * sum_a dS[a][j] y_q[a][c] (Q row a is list entry a), in order of a.
+__global__ void __launch_bounds__(64) dyk_kernel(int n_sel, const float *__restrict__ ds, const float *__restrict__ y,
                                                  float scale, float *__restrict__ dy, Geo g) {
   const int j = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int c = threadIdx.x;
   const int64_t kbase = (int64_t)g.B * g.H;
   float acc = 0.f;
-  for (int a = 0; a < n_sel; ++a) {
-    const int i = min(max(q_tiles[bh * n_sel + a], 0), g.nt - 1);
-    acc = fmaf(ds[(bh * n_sel + a) * g.nt + j], y[(bh * g.nt + i) * DS_OUT + c], acc);
-  }
+  for (int a = 0; a < n_sel; ++a) acc = fmaf(ds[(bh * n_sel + a) * g.nt + j], y[(bh * g.nt + a) * DS_OUT + c], acc);
   dy[((kbase + bh) * g.nt + j) * DS_OUT + c] = acc * scale;
 }
 
-// 32 rows of one (Q|K, b, h), thread u = hidden unit u: the forward pass left the
-// pre-activation Z1 = D W1 in h1; this replaces it by H1 = GELU(Z1) and writes
-// dZ1 = (dy W2^T) * GELU'(Z1).
+// 32 rows of one (Q|K, b, h) block of nrows rows (Q: the list entries, K: every tile),
+// thread u = hidden unit u: the forward pass left the pre-activation Z1 = D W1 in h1; this
+// replaces it by H1 = GELU(Z1) and writes dZ1 = (dy W2^T) * GELU'(Z1).
 __global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restrict__ dy, const float *__restrict__ w2,
-                                                           float *__restrict__ h1, float *__restrict__ dz1, Geo g) {
+                                                           float *__restrict__ h1, float *__restrict__ dz1, int which,
+                                                           int nrows, Geo g) {
   __shared__ float Yl[32 * DS_OUT];  // dy of the 32 rows
-  const int ngrp = (g.nt + 31) / 32;
+  const int ngrp = (nrows + 31) / 32;
   const int grp = blockIdx.x % ngrp;
-  const int64_t wbh = blockIdx.x / ngrp;  // (which*B + b)*H + h
+  const int64_t wbh = (int64_t)which * g.B * g.H + blockIdx.x / ngrp;  // (which*B + b)*H + h
   const int h = (int)(wbh % g.H);
-  const int r0 = grp * 32, nr = min(32, g.nt - r0);
+  const int r0 = grp * 32, nr = min(32, nrows - r0);
   const int u = threadIdx.x;
   for (int e = u; e < 32 * DS_OUT; e += 256) {
     const int r = e / DS_OUT;
@@ -211,12 +197,13 @@ __global__ void __launch_bounds__(256) mlp_bwd_rows_kernel(const float *__restri
 // of 64.
 __global__ void __launch_bounds__(256) atb_mfma_kernel(const float *__restrict__ A, int lda,
                                                        const float *__restrict__ Bm, int ldb, int M, int N,
-                                                       float *__restrict__ C, Geo g) {
+                                                       float *__restrict__ C, int nq, Geo g) {
   constexpr int PF = 8;
   __shared__ float red[3][4][16][64];  // partial tiles of waves 1..3: [wave][block][r][lane]
   const int tm = blockIdx.x, tn = blockIdx.y, h = blockIdx.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, lr = lane & 31, kh = lane >> 5;
-  const int half = (g.nt + 1) >> 1, nsteps = 2 * g.B * half;
+  // steps of two rows: first the B Q segments (nq rows each), then the B K segments (n_t rows)
+  const int hq = (nq + 1) >> 1, hk = (g.nt + 1) >> 1, nsq = g.B * hq, nsteps = nsq + g.B * hk;
   const int q4 = (nsteps + 3) / 4, s_begin = wv * q4, s_end = min(nsteps, s_begin + q4);  // this wave's steps
   f32x16_t acc[2][2];
 #pragma unroll
@@ -227,9 +214,11 @@ __global__ void __launch_bounds__(256) atb_mfma_kernel(const float *__restrict__
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
   const float *Ab = A + 64 * tm + lr, *Bb = Bm + 64 * tn + lr;
   auto load = [&](int s, float (&av)[2], float (&bv)[2]) {
-    const int sg = s / half, row = 2 * (s - sg * half) + kh;  // segment (Q|K, b) and row of step s
-    const bool ok = s < s_end && row < g.nt;
-    const int64_t rr = ok ? ((int64_t)sg * g.H + h) * g.nt + row : 0;  // clamped: always in bounds
+    const bool qs = s < nsq;
+    const int hs = qs ? hq : hk, s2 = qs ? s : s - nsq;
+    const int sg = s2 / hs, row = 2 * (s2 - sg * hs) + kh;  // segment (b) within Q or K, and its row
+    const bool ok = s < s_end && row < (qs ? nq : g.nt);
+    const int64_t rr = ok ? (((int64_t)(qs ? 0 : g.B) + sg) * g.H + h) * g.nt + row : 0;  // clamped: in bounds
     av[0] = Ab[rr * lda];
     av[1] = Ab[rr * lda + 32];
     bv[0] = Bb[rr * ldb];
@@ -297,47 +286,50 @@ __global__ void __launch_bounds__(256) sgd_kernel(float *__restrict__ w, const f
 }
 
 template <int MAXM>
-static void launch_kl(const Geo &g, const float *y, const int32_t *q_tiles, int n_sel, const float *target,
+static void launch_kl(const Geo &g, const float *y, int n_sel, const float *target,
                       float scale, float inv_rows, const DistillWs &w, hipStream_t st) {
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
-  kl_grad_kernel<MAXM><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(y, q_tiles, n_sel, target, scale, inv_rows,
-                                                                       w.ds, w.gq, w.loss, g);
+  kl_grad_kernel<MAXM><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(y, n_sel, target, scale, inv_rows, w.ds,
+                                                                       w.dy, w.loss, g);
 }
 
 hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void *k, float *w1, float *w2,
                           float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
                           float *dw1, float *dw2, float lr, void *ws, hipStream_t st) {
-  size_t off[8];
+  size_t off[7];
   ws_parts(g, n_sel, off);
   char *base = static_cast<char *>(ws);
   DistillWs w{(float *)(base + off[0]), (float *)(base + off[1]), (float *)(base + off[2]), (float *)(base + off[3]),
-              (float *)(base + off[4]), (float *)(base + off[5]), (float *)(base + off[6]), (float *)(base + off[7])};
+              (float *)(base + off[4]), (float *)(base + off[5]), (float *)(base + off[6])};
   const int d3 = 3 * g.d;
   const size_t desc_half = (size_t)g.B * g.H * g.nt * d3;
   // forward: descriptors and MLP outputs of every Q and K tile (shared weights)
-  // (the pre-activation hidden layer goes to h1, which the backward rows kernel turns into GELU)
-  const hipError_t pe =
-      launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st, nullptr, nullptr, false, w.h1);
+  // Q rows: the listed tiles only (an unlisted Q tile gets no gradient); the pre-activation
+  // hidden layer goes to h1, which the backward rows kernel turns into GELU
+  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st, nullptr,
+                                        nullptr, false, w.h1, q_tiles, n_sel);
   if (pe != hipSuccess) return pe;
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
   const float inv_rows = 1.0f / (float)rows;
   if (g.nt <= 64)
-    launch_kl<1>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<1>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
   else if (g.nt <= 256)
-    launch_kl<4>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<4>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
   else if (g.nt <= 640)
-    launch_kl<10>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<10>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
   else
-    launch_kl<20>(g, w.y, q_tiles, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<20>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
   const dim3 gi(g.nt, g.B * g.H);
-  dyq_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.gq, w.dy, g);
-  dyk_kernel<<<gi, 64, 0, st>>>(q_tiles, n_sel, w.ds, w.y, score_scale, w.dy, g);
+  dyk_kernel<<<gi, 64, 0, st>>>(n_sel, w.ds, w.y, score_scale, w.dy, g);
   const int ngrp = (g.nt + 31) / 32;
-  mlp_bwd_rows_kernel<<<dim3(ngrp * 2 * g.B * g.H), 256, 0, st>>>(w.dy, w2, w.h1, w.dz1, g);
+  const int ngrp_q = (n_sel + 31) / 32;
+  mlp_bwd_rows_kernel<<<dim3(ngrp_q * g.B * g.H), 256, 0, st>>>(w.dy, w2, w.h1, w.dz1, 0, n_sel, g);
+  mlp_bwd_rows_kernel<<<dim3(ngrp * g.B * g.H), 256, 0, st>>>(w.dy, w2, w.h1, w.dz1, 1, g.nt, g);
   // 3d is 384 (bf16) or 192 (fp32): both multiples of the 64-wide output tile
-  atb_mfma_kernel<<<dim3(d3 / 64, DS_HID / 64, g.H), 256, 0, st>>>(w.desc, d3, w.dz1, DS_HID, d3, DS_HID, dw1, g);
+  atb_mfma_kernel<<<dim3(d3 / 64, DS_HID / 64, g.H), 256, 0, st>>>(w.desc, d3, w.dz1, DS_HID, d3, DS_HID, dw1,
+                                                                     n_sel, g);
   atb_mfma_kernel<<<dim3(DS_HID / 64, DS_OUT / 64, g.H), 256, 0, st>>>(w.h1, DS_HID, w.dy, DS_OUT, DS_HID, DS_OUT, dw2,
-                                                                       g);
+                                                                        n_sel, g);
   loss_kernel<<<1, 256, 0, st>>>(w.loss, rows, loss);
   if (lr != 0.f) {
     const int64_t n1 = (int64_t)g.H * d3 * DS_HID, n2 = (int64_t)g.H * DS_HID * DS_OUT;

@@ -18,11 +18,14 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
                         bool k_raster = false);
 
 // TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL;
-// the pre-activation hidden layer z [Q|K][B][H][n_t][256] if non-NULL.
+// the pre-activation hidden layer z [Q|K][B][H][n_t][256] if non-NULL.  With qlist
+// ([B][H][nlist] tile indices), the Q rows are the listed tiles, rows 0 .. nlist-1 of each
+// (b, h) block, instead of every tile.
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs = nullptr,
-                           const RasterView *rv = nullptr, bool k_raster = false, float *z = nullptr);
+                           const RasterView *rv = nullptr, bool k_raster = false, float *z = nullptr,
+                           const int32_t *qlist = nullptr, int nlist = 0);
 
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);

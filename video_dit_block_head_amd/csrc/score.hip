@@ -52,7 +52,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
                 float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, float *__restrict__ zout,
-                Geo g, HeadShapes hs, RasterView rv) {
+                const int32_t *__restrict__ qlist, int nlist, Geo g, HeadShapes hs, RasterView rv) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
@@ -73,12 +73,19 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
   const bool rast = which ? RK : RQ;  // uniform over the workgroup
   const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;  // this head's tiles
+  // With a query-tile list, the Q rows are its entries (row r pools tile qlist[b, h, r]) and
+  // there are nlist of them; groups past the list have nothing to do.
+  const bool listed = qlist != nullptr && which == 0;
+  if (listed && r0 >= nlist) return;  // whole workgroup, before any barrier
+  const int32_t *qrow = listed ? qlist + ((int64_t)b * g.H + h) * nlist : nullptr;
   const uint8_t *src0 = rast ? (which ? k : q) + (int64_t)b * rv.sb + (int64_t)h * rv.sh
                              : (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
   const int rg = lane >> 4, c = lane & 15;
 #pragma unroll 1
   for (int tt = 0; tt < 8; ++tt) {
-    const int row = 8 * w + tt, j = r0 + row;
+    const int row = 8 * w + tt;
+    // the tile this row pools; nth (no tile) past the end
+    const int j = listed ? (r0 + row < nlist ? min(max(qrow[r0 + row], 0), nth - 1) : nth) : r0 + row;
     float s[EPC], mx[EPC], mn[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
@@ -389,38 +396,39 @@ static void launch_score_t(const Geo &g, const float *y, float scale, float *sco
 template <int EB, bool RQ, bool RK>
 static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
-                              float *q_desc, float *k_desc, float *z, hipStream_t st) {
+                              float *q_desc, float *k_desc, float *z, const int32_t *qlist, int nlist,
+                              hipStream_t st) {
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
   if (!RQ && !RK && g.padded)
     pool_mlp_kernel<EB, false, false, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k,
-                                                                w2k, y, q_desc, k_desc, z, g, hs, rv);
+                                                                w2k, y, q_desc, k_desc, z, qlist, nlist, g, hs, rv);
   else
     pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
-                                                           y, q_desc, k_desc, z, g, hs, rv);
+                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
-                           bool k_raster, float *z) {
+                           bool k_raster, float *z, const int32_t *qlist, int nlist) {
   const HeadShapes hs0 = hs != nullptr ? *hs : HeadShapes{};  // tiled operands: shapes matter only when padded
   const RasterView rv0{0, 0, 0};
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
     if (bf)
-      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
     else
-      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
   } else if (k_raster) {
     if (bf)
-      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
     else
-      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
   } else {
     if (bf)
-      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
     else
-      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, st);
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
   }
   return hipGetLastError();
 }
