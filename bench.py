@@ -348,7 +348,8 @@ def main():
                        "padded_attn_tflops": round(pflops / (pattn_ms * 1e-3) / 1e12, 1)}
             del psa, pmap, pout
         nxt = {"distill_step_ms": round(distill_ms, 4),
-               "distill_step_qk_read_gbps": round(2 * B * H * N * d * 2 / (distill_ms * 1e-3) / 1e9, 1),
+               # the step reads every K tile and the sampled Q tiles once
+               "distill_step_qk_read_gbps": round(B * H * (nt + n_sel) * P * d * 2 / (distill_ms * 1e-3) / 1e9, 1),
                "distill_sampled_query_tiles_per_head": n_sel,
                "head_sq_error_ms": round(herr_ms, 4),
                "head_sq_error_gbps": round(herr_bytes / (herr_ms * 1e-3) / 1e9, 1),
