@@ -7,10 +7,11 @@
 //  - the kept K tile ([key][d]) and V tile ([d][key], channel-major in HBM) are copied
 //    straight into LDS (global_load_lds, no register staging) with the XOR swizzle
 //    "16-byte chunk c of row r at slot c ^ (r & 15)", which makes every MFMA operand read
-//    a conflict-free 16-byte LDS read.  K and V have their own buffers: the next K tile
-//    streams in during softmax + P V, the next V tile during the next Q K^T.  Three
-//    barriers per key tile: K(t) read (K buffer free), V(t) complete, and V(t) read with
-//    K(t+1) complete;
+//    a conflict-free 16-byte LDS read, issued four MFMAs ahead of its use (scheduling
+//    groups: the default schedule read one ahead).  K and V have their own buffers: the
+//    next K tile streams in during softmax + P V, the next V tile during the next Q K^T.
+//    Three barriers per key tile: K(t) read (K buffer free), V(t) complete, and V(t) read
+//    with K(t+1) complete;
 //  - S^T = K Q^T (32 keys x 32 queries per MFMA block) puts one query per lane column, so
 //    the row max needs one exchange between lane halves; O^T = V^T P^T keeps each lane's
 //    accumulators on its own query, so the online-softmax rescale is lane-local;

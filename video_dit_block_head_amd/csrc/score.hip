@@ -8,10 +8,13 @@
 //                    MFMA: layer 1 32x3d @ 3d x256 (v_mfma_f32_32x32x2f32, 64 hidden units
 //                    per wave), exact-erf GELU, layer 2 32x256 @ 256x64
 //                    (v_mfma_f32_16x16x4f32, 16 outputs per wave).  Three workgroups per
-//                    CU, so other workgroups' streaming overlaps one's MFMA work.
+//                    CU, so other workgroups' streaming overlaps one's MFMA work.  For the
+//                    distillation step it can take a list of Q tiles and also keep the
+//                    pre-activation hidden layer.
 //  score_topk_kernel 16 query-tile rows per workgroup: S = y_q y_k^T on fp32 MFMA
 //                    (v_mfma_f32_16x16x4f32) into an LDS row block, then one wave per row
-//                    for softmax and top-k (ballot/popcount; deterministic).
+//                    for softmax and top-k (ballot/popcount; deterministic); 4, 8 or 16
+//                    waves per workgroup by row length.
 //  topk_kernel       standalone top-k, one wave per row.
 #include "common.h"
 #include "kernels.h"
