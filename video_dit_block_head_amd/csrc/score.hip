@@ -264,7 +264,7 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 // waves take 16 / NW rows each.  Long rows (large MAXM) make the row block big enough that
 // only one workgroup fits a CU, so they use 16 waves, one row each, to keep every SIMD busy
 // through the latency-bound top-k.
-template <int MAXM, int NW>
+template <int MAXM, int NW, int NC>
 __global__ void __launch_bounds__(64 * NW) score_topk_kernel(const float *__restrict__ y, Geo g, float scale,
                                                              float *__restrict__ scores, float *__restrict__ probs,
                                                              int topk, int32_t *__restrict__ idx, HeadShapes hs) {
@@ -363,8 +363,7 @@ __global__ void __launch_bounds__(64 * NW) score_topk_kernel(const float *__rest
 #pragma unroll
       for (int mm = 0; mm < MAXM; ++mm) key[mm] = (64 * mm + lane < nth) ? float_key(sc[mm]) : 0u;
       // the row is in registers now: its LDS words serve as the wave's top-k scratch
-      // long rows compact up to 512 candidates (so that k up to 512 reaches the cheap phase)
-      wave_topk<MAXM, (MAXM >= 16 ? 8 : 2)>(key, nth, topk, lane, idx + grow * topk, nullptr,
+      wave_topk<MAXM, NC>(key, nth, topk, lane, idx + grow * topk, nullptr,
                                              reinterpret_cast<uint32_t *>(&S[row * SW]));
     }
   }
@@ -392,8 +391,24 @@ template <int MAXM>
 static void launch_score_t(const Geo &g, const float *y, float scale, float *scores, float *probs, int topk,
                            int32_t *idx, const HeadShapes &hs, hipStream_t st) {
   constexpr int NW = MAXM >= 16 ? 16 : (MAXM >= 10 ? 8 : 4);
-  score_topk_kernel<MAXM, NW><<<dim3(((g.nt + 15) / 16) * g.H * g.B), 64 * NW, 0, st>>>(y, g, scale, scores, probs,
-                                                                                       topk, idx, hs);
+  // Top-k compaction width (candidates kept in NC registers per lane once at most 64 NC
+  // remain): wide enough that the search reaches the compacted phase soon, narrow enough
+  // that each later bit costs few ballots.  The bounds on k come from counting the ballots
+  // of the search on normally distributed rows; the selection does not depend on NC.
+  const dim3 grid(((g.nt + 15) / 16) * g.H * g.B), block(64 * NW);
+  if constexpr (MAXM >= 16) {
+    if (topk > 160)
+      score_topk_kernel<MAXM, NW, 8><<<grid, block, 0, st>>>(y, g, scale, scores, probs, topk, idx, hs);
+    else
+      score_topk_kernel<MAXM, NW, 4><<<grid, block, 0, st>>>(y, g, scale, scores, probs, topk, idx, hs);
+  } else if constexpr (MAXM >= 10) {
+    if (topk > 100)
+      score_topk_kernel<MAXM, NW, 6><<<grid, block, 0, st>>>(y, g, scale, scores, probs, topk, idx, hs);
+    else
+      score_topk_kernel<MAXM, NW, 2><<<grid, block, 0, st>>>(y, g, scale, scores, probs, topk, idx, hs);
+  } else {
+    score_topk_kernel<MAXM, NW, 2><<<grid, block, 0, st>>>(y, g, scale, scores, probs, topk, idx, hs);
+  }
 }
 
 template <int EB, bool RQ, bool RK>
