@@ -172,6 +172,17 @@ def test_binding_fails_loudly_without_gpu_tensors():
         V.veda_topk_mask(torch.zeros(4, 10), 3, torch.zeros(4, 3, dtype=torch.int32))
 
 
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No fallback: with libveda.so absent, the first call raises instead of computing."""
+    monkeypatch.setattr(V, "_lib", None)
+    monkeypatch.setattr(V, "LIB_PATH", str(tmp_path / "libveda.so"))
+    with pytest.raises(V.VedaError, match="missing"):
+        V.lib()
+    import torch
+    with pytest.raises(V.VedaError):
+        V.veda_topk_mask(torch.zeros(4, 10), 3, torch.zeros(4, 3, dtype=torch.int32))
+
+
 def test_head_error_validation(L):
     f = L.veda_head_sq_error
     wsb = L.veda_head_sq_error_workspace_bytes(1, 16, 2)
