@@ -41,7 +41,8 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 // workgroups fit a CU, so other workgroups stream while one runs its MLP).
 //   pooling: wave w pools tiles 8w .. 8w + 7, 32 16-byte loads per lane in flight;
 //   layer 1: fp32 MFMA 32x32x2 (A[m = lane%32][k = lane/32], B[k = lane/32][n = lane%32]),
-//            64 hidden units per wave, weights prefetched PF steps ahead in registers;
+//            64 hidden units per wave (two per lane column, so one 8-byte weight load per
+//            lane and step), weights prefetched PF steps ahead in registers;
 //   GELU (exact erf) into the hidden block, in place of the descriptors;
 //   layer 2: fp32 MFMA 16x16x4, 16 outputs per wave for all 32 rows (no cross-wave sum).
 // EB: element bytes (2: bf16 with d = P = 128; 4: f32 with d = P = 64).  Rows are 256 bytes.
@@ -173,35 +174,33 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
     }
   }
 
-  // ---- layer 1: hidden units 64 w .. 64 w + 63
+  // ---- layer 1: hidden units 64 w .. 64 w + 63; column m of the two accumulator blocks is
+  // hidden unit 64 w + 2 m (acc0) and 64 w + 2 m + 1 (acc1), so that each lane takes both of
+  // its weights of a step with one 8-byte load
   {
     const int m = lane & 31, kh = lane >> 5;
-    const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * MLP_HIDDEN + 64 * w + m;
+    const float *W1 = (which ? w1k : w1q) + (int64_t)h * D3 * MLP_HIDDEN + 64 * w + 2 * m;
     f32x16_t acc0, acc1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc0[r] = 0.f;
       acc1[r] = 0.f;
     }
-    float wr[PF][2];
+    float2 wr[PF];
 #pragma unroll
-    for (int pp = 0; pp < PF; ++pp) {
-      wr[pp][0] = W1[(2 * pp + kh) * MLP_HIDDEN];
-      wr[pp][1] = W1[(2 * pp + kh) * MLP_HIDDEN + 32];
-    }
+    for (int pp = 0; pp < PF; ++pp) wr[pp] = *reinterpret_cast<const float2 *>(W1 + (2 * pp + kh) * MLP_HIDDEN);
 #pragma unroll 1
     for (int sb = 0; sb < D3 / 2; sb += PF) {
 #pragma unroll
       for (int pp = 0; pp < PF; ++pp) {
         const int kk = 2 * (sb + pp) + kh;
-        const float b0 = wr[pp][0], b1 = wr[pp][1];
+        const float2 bw = wr[pp];
         // unconditional prefetch (row clamped in range): no branch, so the waits stay exact
         const int kn = min(kk + 2 * PF, D3 - 2 + kh);
         const float av = Ds[m * PM_DS + kk];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc1, 0, 0, 0);
-        wr[pp][0] = W1[kn * MLP_HIDDEN];
-        wr[pp][1] = W1[kn * MLP_HIDDEN + 32];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bw.x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bw.y, acc1, 0, 0, 0);
+        wr[pp] = *reinterpret_cast<const float2 *>(W1 + kn * MLP_HIDDEN);
         __builtin_amdgcn_sched_barrier(0);  // keep each step's prefetch a full ring ahead of its use
       }
     }
@@ -209,18 +208,14 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-      Ds[row * PM_HST + 64 * w + m] = gelu_erf(acc0[r]);
-      Ds[row * PM_HST + 64 * w + 32 + m] = gelu_erf(acc1[r]);
+      *reinterpret_cast<float2 *>(&Ds[row * PM_HST + 64 * w + 2 * m]) = make_float2(gelu_erf(acc0[r]), gelu_erf(acc1[r]));
     }
     if (zout != nullptr) {  // the pre-activation layer, for the estimator's backward pass
-      float *zo = zout + ((((int64_t)which * g.B + b) * g.H + h) * g.nt + r0) * MLP_HIDDEN + 64 * w + m;
+      float *zo = zout + ((((int64_t)which * g.B + b) * g.H + h) * g.nt + r0) * MLP_HIDDEN + 64 * w + 2 * m;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (r0 + row < g.nt) {
-          zo[(int64_t)row * MLP_HIDDEN] = acc0[r];
-          zo[(int64_t)row * MLP_HIDDEN + 32] = acc1[r];
-        }
+        if (r0 + row < g.nt) *reinterpret_cast<float2 *>(&zo[(int64_t)row * MLP_HIDDEN]) = make_float2(acc0[r], acc1[r]);
       }
     }
   }
