@@ -261,6 +261,26 @@ def test_sparsity_sweep(r):
         assert mx <= 2e-2 and rel <= 1e-2
 
 
+# Rows longer than 256 tiles pick the top-k compaction width from k (2 or 6 up to 768 tiles,
+# 4 or 8 beyond); these k straddle each switch.
+WIDTH_KS = {"large": (100, 101, 300), "long": (160, 161)}
+
+
+def test_topk_compaction_widths(r):
+    cfg = r.cfg
+    if cfg.name not in WIDTH_KS:
+        pytest.skip("rows of at most 256 tiles use one width")
+    h = int(r.heads(1)[0])
+    qt, kt, _, _ = r.oracle_head(0, h)
+    s32 = O.tile_scores(O.mlp(O.trippool(qt, cfg.tile), r.wl.w1[h], r.wl.w2[h]),
+                        O.mlp(O.trippool(kt, cfg.tile), r.wl.w1[h], r.wl.w2[h]), cfg.score_scale).astype(np.float32)
+    for kk in WIDTH_KS[cfg.name]:
+        say(f"[gpu-parity] {cfg.name}: top-k widths, k={kk}")
+        got = host(r.sa.score(kk)[0, h]).astype(np.int64)
+        for i in range(cfg.n_tiles):
+            assert O.topk_agrees(s32[i], got[i], kk)[0], (cfg.name, kk, h, i)
+
+
 # ----------------------------------------------------------------------------- tile map
 def test_tilemap_and_recall(r):
     cfg, ci = r.cfg, r.cfg.index
