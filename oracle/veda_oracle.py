@@ -262,7 +262,8 @@ def search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, 
     ties to the lower index; err [C, B, H]; ref [B, H] = squared norm of the full output).
     Pinned: a head whose attention is block-local on one candidate's tiles, with an
     estimator that keeps exactly those tiles, selects that candidate with zero error;
-    with every tile kept, all errors vanish."""
+    with every tile kept, all errors vanish; two calibration batches whose block-local
+    tilings disagree (per head) are decided by the error summed over the batch."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     B, N, H, _ = q.shape
     err = np.zeros((len(candidates), B, H))
@@ -308,9 +309,11 @@ def kl_rows(p, s):
 
 def distill_loss(descs, w1, w2, q_tiles, targets, score_scale):
     """Mean over every sampled row of KL(target row normalised to sum 1 || softmax of the
-    estimator's logits).  descs: list over (b, h) of (D_q [n_t, 3d], D_k [n_t, 3d]) with
-    head index h_of[k]; w1 [H, 3d, hid], w2 [H, hid, out]; q_tiles[(b, h)]: [n_sel];
-    targets[(b, h)]: [n_sel, n_t]."""
+    estimator's logits).  descs: dict {(block, h): (D_q [n_t, 3d], D_k [n_t, 3d])}, one
+    entry per (batch, head) block with its head index h; w1 [H, 3d, hid], w2 [H, hid, out];
+    q_tiles[block]: [n_sel] (blocks may sample different numbers of tiles);
+    targets[block]: [n_sel, n_t].  Pinned: the hand-worked two-block case of
+    tests/golden/distill_hand.txt (1 and 3 sampled rows, unnormalised targets)."""
     total, rows = 0.0, 0
     for (bh, h), (dq, dk) in descs.items():
         yq = mlp(dq, w1[h], w2[h])

@@ -13,7 +13,7 @@ import torch
 
 import oracle.veda_oracle as O
 from workloads import bf16_bits_to_f32, get, make
-from workloads.synth import block_local_case
+from cases import block_local_case
 
 pytestmark = pytest.mark.gpu
 

@@ -177,6 +177,53 @@ def search_no_untiling(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, 
     return err.sum(axis=1).argmin(axis=0), err, ref
 
 
+def search_batch0_only(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """Chooses from the first calibration batch alone."""
+    _, err, ref = O.search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale)
+    return err[:, 0, :].argmin(axis=0), err, ref
+
+
+def search_last_batch_only(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """Chooses from the last calibration batch alone."""
+    _, err, ref = O.search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale)
+    return err[:, -1, :].argmin(axis=0), err, ref
+
+
+def search_sum_over_heads(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale):
+    """Sums the errors over heads too, so every head gets the same tiling."""
+    _, err, ref = O.search_tile_shapes(q, k, v, grid, P, candidates, w1, w2, topk, score_scale, scale)
+    best = int(err.sum(axis=(1, 2)).argmin())
+    return np.full(err.shape[2], best), err, ref
+
+
+def _rows_and_blocks(descs, q_tiles):
+    return sum(len(np.asarray(q_tiles[bh])) for bh, _ in descs), len(descs)
+
+
+def distill_loss_mean_blocks(descs, w1, w2, q_tiles, targets, score_scale):
+    """Divides the summed KL by the number of (batch, head) blocks instead of the rows."""
+    rows, blocks = _rows_and_blocks(descs, q_tiles)
+    return O.distill_loss(descs, w1, w2, q_tiles, targets, score_scale) * rows / blocks
+
+
+def distill_grads_mean_blocks(descs, w1, w2, q_tiles, targets, score_scale):
+    """The same divisor in the gradients (so they stay consistent with that loss)."""
+    rows, blocks = _rows_and_blocks(descs, q_tiles)
+    loss, g1, g2 = O.distill_grads(descs, w1, w2, q_tiles, targets, score_scale)
+    return loss * rows / blocks, g1 * rows / blocks, g2 * rows / blocks
+
+
+def distill_loss_unnormalised(descs, w1, w2, q_tiles, targets, score_scale):
+    """Takes the target rows as they come, without dividing by their sums."""
+    total, rows = 0.0, 0
+    for (bh, h), (dq, dk) in descs.items():
+        sel = np.asarray(q_tiles[bh])
+        s = O.tile_scores(O.mlp(dq, w1[h], w2[h])[sel], O.mlp(dk, w1[h], w2[h]), score_scale)
+        total += O.kl_rows(np.asarray(targets[bh], np.float64), s).sum()
+        rows += len(sel)
+    return total / rows
+
+
 def gelu_grad_no_density(x):
     """Drops the x phi(x) term."""
     x = np.asarray(x, np.float64)
@@ -282,6 +329,12 @@ MUTANTS = [
     ("kl: direction reversed", [pins.pin_kl_rows], [kl_reversed]),
     ("distill: gradient sign", [pins.pin_distill_fd], [distill_grads_sign]),
     ("distill: key-tile path dropped", [pins.pin_distill_fd], [distill_grads_no_dyk]),
+    ("search: first batch only", [pins.pin_search_batch_sum], [search_batch0_only]),
+    ("search: last batch only", [pins.pin_search_batch_sum], [search_last_batch_only]),
+    ("search: errors summed over heads", [pins.pin_search_batch_sum], [search_sum_over_heads]),
+    ("distill: mean over blocks (loss and gradients)", [pins.pin_distill_hand],
+     [distill_loss_mean_blocks, distill_grads_mean_blocks]),
+    ("distill: target rows not normalised", [pins.pin_distill_hand], [distill_loss_unnormalised]),
     ("search: output left tile-major", [pins.pin_search_block_local, pins.pin_search_all_kept], [search_no_untiling]),
     ("slots: padding wraps around", [pins.pin_slots_golden, pins.pin_slots_loops], [slots_wraparound]),
     ("trippool padded: mean over P", [pins.pin_trippool_padded_loops], [trippool_padded_mean_over_p]),

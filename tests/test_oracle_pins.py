@@ -514,7 +514,7 @@ def pin_search_block_local(search_tile_shapes):
     """Attention confined to the (1, 8, 8) tiles and an estimator that keeps each query
     tile's own tile (top-1): that candidate reproduces full attention up to e^-50 weights,
     the others miss most of each query's keys."""
-    from workloads.synth import block_local_case
+    from cases import block_local_case
     q, k, v, w1, w2 = block_local_case(SEARCH_GRID, SEARCH_CANDIDATES[1], SEARCH_D, heads=2, batch=1)
     choice, err, ref = search_tile_shapes(q, k, v, SEARCH_GRID, SEARCH_P, SEARCH_CANDIDATES, w1, w2, 1, 0.125,
                                           1 / math.sqrt(SEARCH_D))
@@ -535,8 +535,31 @@ def pin_search_all_kept(search_tile_shapes):
     assert np.all(err / ref[None] < 1e-24)
 
 
+def pin_search_batch_sum(search_tile_shapes):
+    """Two calibration batches that disagree: head 0 is block-local on candidate 0 in batch 0
+    (V x 8) and on candidate 1 in batch 1; head 1 on candidate 1 in batch 0 and on
+    candidate 2 in batch 1 (V x 8).  The error summed over the batch picks 0 for head 0 and
+    2 for head 1.  Batch 0 alone would pick (0, 1), the last batch alone (1, 2), and one
+    choice from errors summed over heads would be the same for both heads."""
+    from cases import block_local_inputs
+    c = SEARCH_CANDIDATES
+    q, k, v, w1, w2 = block_local_inputs(SEARCH_GRID, [[c[0], c[1]], [c[1], c[2]]], SEARCH_D,
+                                         v_scale=[[8.0, 1.0], [1.0, 8.0]])
+    choice, err, ref = search_tile_shapes(q, k, v, SEARCH_GRID, SEARCH_P, c, w1, w2, 1, 0.125,
+                                          1 / math.sqrt(SEARCH_D))
+    assert list(choice) == [0, 2], (list(choice), err.sum(axis=1))
+    assert err.shape == (3, 2, 2) and ref.shape == (2, 2)
+    # each block's own tiling reproduces full attention
+    assert err[0, 0, 0] < 1e-12 * ref[0, 0] and err[1, 1, 0] < 1e-12 * ref[1, 0]
+    assert err[1, 0, 1] < 1e-12 * ref[0, 1] and err[2, 1, 1] < 1e-12 * ref[1, 1]
+
+
 def test_search_block_local():
     pin_search_block_local(O.search_tile_shapes)
+
+
+def test_search_batch_sum():
+    pin_search_batch_sum(O.search_tile_shapes)
 
 
 def test_search_all_kept():
@@ -585,11 +608,40 @@ def _distill_case(seed=22, H=2, B=2, nt=6, d3=12, hid=5, out=4, n_sel=3):
     return descs, w1, w2, q_tiles, targets
 
 
-def pin_distill_fd(distill_grads):
+def distill_hand_case():
+    """The blocks, sampled tiles, targets and hand-worked loss of tests/golden/distill_hand.txt,
+    with seeded Q-tile descriptors and weights (the loss does not depend on them: every
+    K-tile descriptor is zero, so every logit is 0)."""
+    tagged, _ = read_golden("distill_hand.txt")
+    nt = int(tagged["n_t"][0][0])
+    rng = np.random.default_rng(31)
+    d3, hid, out, H = 6, 5, 3, 2
+    descs, q_tiles, targets = {}, {}, {}
+    for row in tagged["block"]:
+        bh, h = int(row[0]), int(row[1])
+        descs[(bh, h)] = (rng.standard_normal((nt, d3)), np.zeros((nt, d3)))
+        q_tiles[bh] = np.array([int(x) for x in row[2:]])
+        targets[bh] = np.array([r[1:] for r in tagged["target"] if int(r[0]) == bh])
+    w1 = rng.standard_normal((H, d3, hid))
+    w2 = rng.standard_normal((H, hid, out))
+    return descs, w1, w2, q_tiles, targets, tagged["loss"][0][0]
+
+
+def pin_distill_hand(distill_loss, distill_grads=None):
+    """The hand-worked loss: the mean over all four sampled rows of two blocks (1 and 3 rows)
+    of KL(normalised target || uniform)."""
+    descs, w1, w2, q_tiles, targets, want = distill_hand_case()
+    assert math.isclose(distill_loss(descs, w1, w2, q_tiles, targets, 0.7), want, rel_tol=1e-13)
+    if distill_grads is not None:
+        assert math.isclose(distill_grads(descs, w1, w2, q_tiles, targets, 0.7)[0], want, rel_tol=1e-13)
+
+
+def pin_distill_fd(distill_grads, distill_loss=None):
     """Central differences of the loss in every weight (one head's query tile sampled twice)."""
+    distill_loss = O.distill_loss if distill_loss is None else distill_loss
     descs, w1, w2, q_tiles, targets = _distill_case()
     loss, g1, g2 = distill_grads(descs, w1, w2, q_tiles, targets, 0.3)
-    assert math.isclose(loss, O.distill_loss(descs, w1, w2, q_tiles, targets, 0.3), rel_tol=1e-12)
+    assert math.isclose(loss, distill_loss(descs, w1, w2, q_tiles, targets, 0.3), rel_tol=1e-12)
     h = 1e-6
     for w, g in ((w1, g1), (w2, g2)):
         fd = np.zeros_like(w)
@@ -597,8 +649,8 @@ def pin_distill_fd(distill_grads):
             wp, wm = w.copy(), w.copy()
             wp[idx] += h
             wm[idx] -= h
-            lp = O.distill_loss(descs, wp if w is w1 else w1, wp if w is w2 else w2, q_tiles, targets, 0.3)
-            lm = O.distill_loss(descs, wm if w is w1 else w1, wm if w is w2 else w2, q_tiles, targets, 0.3)
+            lp = distill_loss(descs, wp if w is w1 else w1, wp if w is w2 else w2, q_tiles, targets, 0.3)
+            lm = distill_loss(descs, wm if w is w1 else w1, wm if w is w2 else w2, q_tiles, targets, 0.3)
             fd[idx] = (lp - lm) / (2 * h)
         assert np.allclose(g, fd, rtol=1e-5, atol=1e-9), np.abs(g - fd).max()
 
@@ -613,6 +665,10 @@ def test_kl_rows():
 
 def test_distill_grads_fd():
     pin_distill_fd(O.distill_grads)
+
+
+def test_distill_hand():
+    pin_distill_hand(O.distill_loss, O.distill_grads)
 
 
 def test_distill_zero_at_match():

@@ -167,37 +167,3 @@ def make(cfg: Config, heads: Optional[List[int]] = None) -> Workload:
                              for h in range(H)]).astype(np.int64)
     return Workload(cfg, q, k, v, w1, w2, scales, sinks, cfg.head_shapes(), q_sample)
 
-
-def block_id(grid, shape):
-    """Tile index of every raster token under tiling `shape` (row-major tile numbering)."""
-    T, Hs, Ws = grid
-    pt, ph, pw = shape
-    t, h, w = np.meshgrid(np.arange(T), np.arange(Hs), np.arange(Ws), indexing="ij")
-    return (((t // pt) * (Hs // ph) + h // ph) * (Ws // pw) + w // pw).reshape(-1)
-
-
-def block_local_case(grid, shape, d, heads=1, batch=1, c=20.0, hidden=256, out=64, seed=0):
-    """Inputs whose attention is confined to the tiles of one tiling: Q = K = c * one-hot of
-    the token's tile under `shape` (so q.k is c^2 inside a tile, 0 across tiles), V ~ N(0,1)
-    (bf16-exact values), and estimator weights that pass the tile mean straight through
-    (W1, W2 = identity on the leading channels), so a tile's score is largest against
-    itself.  Every value is exact in bfloat16.  Returns raster [B, N, H, d] float32 q, k, v
-    and float32 w1 [H, 3d, hidden], w2 [H, hidden, out]."""
-    ids = block_id(grid, shape)
-    n_blocks = int(ids.max()) + 1
-    if n_blocks > min(d, out):
-        raise ValueError("one-hot code needs d and the MLP width >= number of tiles")
-    N = ids.size
-    code = np.zeros((N, d), np.float32)
-    code[np.arange(N), ids] = np.float32(c)
-    q = np.broadcast_to(code[None, :, None, :], (batch, N, heads, d)).astype(np.float32)
-    k = q.copy()
-    rng = np.random.default_rng(seed)
-    v = bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal((batch, N, heads, d), dtype=np.float32)))
-    w1 = np.zeros((heads, 3 * d, hidden), np.float32)
-    w2 = np.zeros((heads, hidden, out), np.float32)
-    for i in range(min(d, hidden)):
-        w1[:, i, i] = 1.0
-    for i in range(min(hidden, out)):
-        w2[:, i, i] = 1.0
-    return q, k, v, w1, w2
