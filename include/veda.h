@@ -149,7 +149,11 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  * selected, non-contiguous key/value tiles]  For every query tile i of every (b, h):
  * O = softmax(Q_i K_sel^T * softmax_scale) V_sel over the keys of the tiles
  * kv_idx[b, h, i, 0..k-1], the softmax renormalised over those keys.
- *   q_tiled, k_tiled: VEDA_TILE_ROWS; v_tiled: VEDA_TILE_COLS
+ *   q_tiled, k_tiled: VEDA_TILE_ROWS
+ *   v_tiled, v_layout: V and the layout the caller holds it in.  Only VEDA_TILE_COLS
+ *           (channel-major tiles, as veda_tile_gather writes them with that layout) is
+ *           read; any other layout returns VEDA_ERR_UNSUPPORTED with nothing launched (a
+ *           VEDA_TILE_ROWS V must first go through veda_tile_gather with VEDA_TILE_COLS)
  *   kv_idx: [B, H, n_t, k] int32, each entry in [0, n_t), no repeats within a row
  *           (k == n_t with every tile listed is dense attention).  Entries outside
  *           [0, n_t) are clamped into it (no out-of-bounds access; the result is then
@@ -158,7 +162,7 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  *   lse:     out [B, H, N] f32 natural-log log-sum-exp of each query row, nullable */
 veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype,
                                  const void *q_tiled, const void *k_tiled, const void *v_tiled,
-                                 const int32_t *kv_idx, int32_t k, float softmax_scale,
+                                 veda_layout v_layout, const int32_t *kv_idx, int32_t k, float softmax_scale,
                                  void *o_tiled, float *lse, hipStream_t stream);
 
 /* Workspace (bytes) that veda_oracle_tilemap needs: B*H*n_sel*n_t*P floats. */
@@ -193,7 +197,8 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
  * is raster token origin_h(j) + intra_h(r).  k_layout says where K is: VEDA_RASTER (with
  * the same strides as Q) or VEDA_TILE_ROWS (tile-major [B, H, N, d], from
  * veda_tile_gather; K tiles are then contiguous 32 KB copies, which the attention and
- * tile-map kernels prefer).  V stays VEDA_TILE_COLS.  The output of
+ * tile-map kernels prefer).  V stays VEDA_TILE_COLS (v_layout, checked as in
+ * veda_sparse_attn_fwd).  The output of
  * veda_sparse_attn_fwd_raster is raster (same strides) and its lse is [B, H, N] in raster
  * token order; the tile-map lse keeps its [B, H, n_sel * P] tile-row order.  Extra status:
  * VEDA_ERR_UNSUPPORTED if an in-tile token offset times the token stride reaches 2^31
@@ -206,7 +211,8 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                         veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
-                                        const void *v_cols, const int32_t *kv_idx, int32_t k_kept,
+                                        const void *v_cols, veda_layout v_layout, const int32_t *kv_idx,
+                                        int32_t k_kept,
                                         float softmax_scale, void *o_raster, float *lse, hipStream_t stream);
 veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
@@ -243,6 +249,8 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
  *   a, b: raster [B, N, H, d] contiguous tensors of `dtype` (d = head_dim; d * element
  *         size a multiple of 16 bytes), e.g. a sparse output and the dense output
  *   err:    out [B, H] f32, err[b, h] = sum over tokens n and channels c of (a - b)^2
+ *   err_batch_sum: out [H] f32, sum over b of err[b, h] (the search objective summed
+ *         over the calibration batch, added in ascending b), nullable
  *   ref_sq: out [B, H] f32, sum of b^2 (for relative errors), nullable
  *   workspace: device scratch of >= veda_head_sq_error_workspace_bytes(B, N, H) bytes,
  *         8-byte aligned, caller-owned (one partial pair per head and token chunk)
@@ -253,7 +261,7 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
 size_t veda_head_sq_error_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t heads);
 veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim,
                                veda_dtype dtype, const void *a, const void *b, float *err,
-                               float *ref_sq, void *workspace, size_t workspace_bytes,
+                               float *err_batch_sum, float *ref_sq, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
 const char *veda_status_str(veda_status s);

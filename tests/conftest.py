@@ -15,6 +15,15 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
 
 
+def gpu_visible():
+    """Whether this process can see a GPU (counting devices initialises no HIP context)."""
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
 def read_golden(name):
     """Parse a tests/golden fixture: '#' lines are comments, other lines are
     'tag v1 v2 ...' or plain number rows.  Returns (tagged: dict[str, list[list[float]]],

@@ -2,7 +2,8 @@
 declares, and rejects bad arguments with the documented status before touching the GPU.
 
 No call here has arguments that pass validation, so nothing is ever launched (the fake
-device addresses below are never dereferenced)."""
+device addresses below are never dereferenced).  The module skips itself wherever a GPU
+is visible, so that a regression in a check could never launch a kernel on a fake address."""
 import ctypes
 import os
 import re
@@ -10,7 +11,9 @@ import re
 import pytest
 
 import video_dit_block_head_amd as V
-from conftest import ROOT
+from conftest import ROOT, gpu_visible
+
+pytestmark = pytest.mark.skipif(gpu_visible(), reason="fake device addresses: CPU-only (no GPU visible)")
 
 HEADER = os.path.join(ROOT, "include", "veda.h")
 OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN = 0, -1, -2, -3, -4, -5, -6
@@ -76,7 +79,8 @@ def test_padded_rejected_where_unsupported(L):
     n_t = g.n_tiles                                           # 3 * 4 * 8 = 96 > 80 (dividing head)
     st = (g.n_tokens * 2 * 128, 2 * 128, 128)
     RAS, big = V.RASTER, 1 << 40
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, 4, 0.088, A, None, None) == UNSUP
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, 4, 0.088, A, None,
+                                         None) == UNSUP
     assert L.veda_trippool_score_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None,
                                         None, 6, A, A, big, None) == UNSUP
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, RAS, *st, 0.088, A, 4, A, None, A, big, None) == UNSUP
@@ -84,7 +88,7 @@ def test_padded_rejected_where_unsupported(L):
                                None) == UNSUP
     assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, 0.088, None, n_t, A, None, A, big, None) == SHAPE
     # k may not exceed the smallest per-head tile count (80 here)
-    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, A, 81, 0.088, A, None, None) == SHAPE
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.COLS, A, 81, 0.088, A, None, None) == SHAPE
     assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, 81, A, A,
                                  big, None) == SHAPE
 
@@ -142,12 +146,24 @@ def test_topk_validation(L):
 def test_attn_validation(L):
     g = geom()
     f = L.veda_sparse_attn_fwd
-    assert f(g.ref, V.BF16, A, A, None, A, 4, 0.088, A, None, None) == NULL
-    assert f(g.ref, V.BF16, A, A, A, A, 0, 0.088, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, A, A, A, 33, 0.088, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, A, A, A, 4, 0.088, MIS, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, A, A, 4, 0.088, A, MIS, None) == ALIGN
-    assert f(geom(d=64).ref, V.BF16, A, A, A, A, 4, 0.088, A, None, None) == UNSUP
+    C = V.COLS
+    assert f(g.ref, V.BF16, A, A, None, C, A, 4, 0.088, A, None, None) == NULL
+    assert f(g.ref, V.BF16, A, A, A, C, A, 0, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, C, A, 33, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, C, A, 4, 0.088, MIS, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, A, C, A, 4, 0.088, A, MIS, None) == ALIGN
+    assert f(geom(d=64).ref, V.BF16, A, A, A, C, A, 4, 0.088, A, None, None) == UNSUP
+
+
+def test_attn_refuses_v_not_channel_major(L):
+    """V is read channel-major (VEDA_TILE_COLS) only: a tile-major or raster V is refused
+    with a status, never computed as if it were channel-major."""
+    g = geom()
+    for lay in (V.ROWS, V.RASTER, 7):
+        assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, lay, A, 4, 0.088, A, None, None) == UNSUP
+        st = (4096 * 2 * 128, 2 * 128, 128)
+        assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, lay, A, 4, 0.088, A, None,
+                                             None) == UNSUP
 
 
 def test_tilemap_validation(L):
@@ -190,14 +206,15 @@ def test_head_error_validation(L):
     assert L.veda_head_sq_error_workspace_bytes(2, 76800, 40) == 2 * 40 * 256 * 8
     assert L.veda_head_sq_error_workspace_bytes(0, 16, 2) == 0
     W = (A, wsb)
-    assert f(1, 16, 2, 128, 7, A, B_, A, None, *W, None) == DTYPE
-    assert f(0, 16, 2, 128, V.BF16, A, B_, A, None, *W, None) == SHAPE
-    assert f(1, 16, 2, 12, V.BF16, A, B_, A, None, *W, None) == SHAPE     # 24-byte rows
-    assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, *W, None) == NULL
-    assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, *W, None) == NULL
-    assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, *W, None) == ALIGN
-    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, None, wsb, None) == WS
-    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, A, wsb - 1, None) == WS
+    assert f(1, 16, 2, 128, 7, A, B_, A, None, None, *W, None) == DTYPE
+    assert f(0, 16, 2, 128, V.BF16, A, B_, A, None, None, *W, None) == SHAPE
+    assert f(1, 16, 2, 12, V.BF16, A, B_, A, None, None, *W, None) == SHAPE     # 24-byte rows
+    assert f(1, 16, 2, 128, V.BF16, None, B_, A, None, None, *W, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, A, B_, None, None, None, *W, None) == NULL
+    assert f(1, 16, 2, 128, V.BF16, MIS, B_, A, None, None, *W, None) == ALIGN
+    assert f(1, 16, 2, 128, V.BF16, A, B_, A, ctypes.c_void_p(0x10002), None, *W, None) == ALIGN   # batch sum
+    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, None, None, wsb, None) == WS
+    assert f(1, 16, 2, 128, V.BF16, A, B_, A, None, None, A, wsb - 1, None) == WS
 
 
 def test_raster_validation(L):
@@ -205,15 +222,56 @@ def test_raster_validation(L):
     f = L.veda_sparse_attn_fwd_raster
     st = (4096 * 2 * 128, 2 * 128, 128)
     RAS = V.RASTER
-    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, A, 4, 0.088, A, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, None, RAS, *st, A, A, 4, 0.088, A, None, None) == NULL
-    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, A, 4, 0.088, A, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, A, 4, 0.088, A, None, None) == SHAPE   # K layout
+    C = V.COLS
+    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, C, A, 4, 0.088, A, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, None, RAS, *st, A, C, A, 4, 0.088, A, None, None) == NULL
+    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, C, A, 4, 0.088, A, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, C, A, 4, 0.088, A, None, None) == SHAPE   # K layout
     # in-tile token offset x token stride beyond 2^31 bytes
-    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, A, 4, 0.088,
-             A, None, None) == UNSUP
+    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, C, A, 4,
+             0.088, A, None, None) == UNSUP
     s = L.veda_trippool_score_raster
     assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, A, 1 << 30,
              None) == NULL
     t = L.veda_oracle_tilemap_raster
     assert t(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, A, 0, A, None, A, 1 << 40, None) == SHAPE
+
+
+def test_binding_checks_sizes_before_taking_pointers():
+    """The C ABI cannot see buffer sizes, so the binding checks dtype and size of every
+    tensor against the geometry first: short, mistyped or misshapen CPU tensors raise with
+    the size message, before the GPU check and before any pointer is taken."""
+    import torch
+    g = geom()                                    # B 1, H 2, N 4096, d 128, n_t 32
+    n = 2 * 4096 * 128
+    bf = lambda m: torch.zeros(m, dtype=torch.bfloat16)
+    i32 = lambda m: torch.zeros(m, dtype=torch.int32)
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(2 * 32 * 4).view(1, 2, 32, 4), 4, 0.088, bf(n - 8))
+    with pytest.raises(V.VedaError, match="does not match k"):
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(2 * 32 * 5).view(1, 2, 32, 5), 4, 0.088, bf(n))
+    with pytest.raises(V.VedaError, match="dtype"):
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), torch.zeros(1, 2, 32, 4, dtype=torch.int64), 4, 0.088, bf(n))
+    with pytest.raises(V.VedaError, match="at least"):     # list of one head only
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(32 * 4).view(1, 1, 32, 4), 4, 0.088, bf(n))
+    with pytest.raises(V.VedaError, match="shape"):
+        V.veda_tile_gather(g, torch.zeros(1, 4096, 3, 128, dtype=torch.bfloat16), bf(n))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_tile_gather(g, torch.zeros(1, 4096, 2, 128, dtype=torch.bfloat16), bf(n - 1))
+    w1, w2 = torch.zeros(2, 384, 256), torch.zeros(2, 256, 64)
+    with pytest.raises(V.VedaError, match="shape"):
+        V.veda_trippool_score(g, bf(n), bf(n), torch.zeros(3, 384, 256), w2, topk=6, idx=i32(2 * 32 * 6))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_trippool_score(g, bf(n), bf(n), w1, w2, topk=6, idx=i32(2 * 32 * 6 - 1))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_trippool_score(g, bf(n), bf(n), w1, w2, scores=torch.zeros(2 * 32 * 31))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_oracle_tilemap(g, bf(n), bf(n), 0.088, i32(2 * 4), 4, torch.zeros(2 * 4 * 32 - 1))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_topk_mask(torch.zeros(4, 10), 3, i32(11))
+    with pytest.raises(V.VedaError, match="at least"):
+        V.veda_head_sq_error(bf(2 * 16 * 128).view(1, 16, 2, 128), bf(2 * 16 * 128).view(1, 16, 2, 128),
+                             torch.zeros(1))
+    # well-formed CPU tensors get as far as the device check
+    with pytest.raises(V.VedaError, match="GPU tensor"):
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(2 * 32 * 4).view(1, 2, 32, 4), 4, 0.088, bf(n))

@@ -92,16 +92,16 @@ def lib():
             "veda_trippool_score": (i32, [G, i32, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp,
                                           vp, sz, vp]),
             "veda_topk_mask": (i32, [i64, i32, vp, i32, vp, vp, vp]),
-            "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]),
+            "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, i32, vp, i32, f32, vp, vp, vp]),
             "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
             "veda_head_sq_error_workspace_bytes": (sz, [i32, i32, i32]),
-            "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
                                                  vp, vp, vp, vp, i32, vp, vp, sz, vp]),
-            "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, i32, f32, vp, vp,
-                                                  vp]),
+            "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
+                                                  vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
                                                  vp]),
             "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
@@ -136,20 +136,85 @@ def _dtype_code(t):
     raise VedaError(f"unsupported tensor dtype {t.dtype}")
 
 
-def _p(t, name, need_contig=True):
+class _Arg:
+    """A tensor argument whose dtype and size have been checked; its device pointer is taken
+    by _call once every argument of the call has passed those checks."""
+    __slots__ = ("t", "name", "contig")
+
+    def __init__(self, t, name, contig):
+        self.t, self.name, self.contig = t, name, contig
+
+    def ptr(self):
+        if not self.t.is_cuda:
+            raise VedaError(f"{self.name} must be a GPU tensor")
+        if self.contig and not self.t.is_contiguous():
+            raise VedaError(f"{self.name} must be contiguous")
+        return ctypes.c_void_p(self.t.data_ptr())
+
+
+def _p(t, name, need_contig=True, dtype=None, numel=None, shape=None):
+    """Tensor argument t (None stays None) after checking its dtype and its size (at least
+    `numel` elements, or exactly `shape`).  The C ABI cannot see buffer sizes: a short
+    buffer would be read or written out of bounds, so every size is checked here, for every
+    argument, before _call checks devices and takes any pointer."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise VedaError(f"{name} must be a GPU tensor")
-    if need_contig and not t.is_contiguous():
-        raise VedaError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    if dtype is not None and t.dtype != dtype:
+        raise VedaError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise VedaError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise VedaError(f"{name}: {t.numel()} elements, at least {numel} needed")
+    return _Arg(t, name, need_contig)
+
+
+def _call(name, *args):
+    """Call entry point `name` of the library: tensor arguments must be GPU tensors (and
+    contiguous where required); any non-zero status raises VedaError."""
+    conv = [a.ptr() if isinstance(a, _Arg) else a for a in args]
+    conv = [a.handle() if isinstance(a, _Stream) else a for a in conv]
+    _check(name, getattr(lib(), name)(*conv))
+
+
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _elem_dtype(t):
+    """The element type of a Q/K/V operand (bf16 or fp32), as a torch dtype."""
+    _dtype_code(t)
+    return t.dtype
+
+
+def _tiled_numel(geom):
+    return geom.batch * geom.heads * geom.n_tiled * geom.head_dim
+
+
+def _raster_shape(geom):
+    return (geom.batch, geom.n_tokens, geom.heads, geom.head_dim)
+
+
+class _Stream:
+    """The HIP stream of a call (torch's current stream by default), resolved by _call after
+    the tensor arguments have been checked."""
+    __slots__ = ("s",)
+
+    def __init__(self, s):
+        self.s = s
+
+    def handle(self):
+        import torch
+        s = torch.cuda.current_stream() if self.s is None else self.s
+        return ctypes.c_void_p(s.cuda_stream)
 
 
 def _stream(stream):
-    import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return _Stream(stream)
 
 
 def version():
@@ -159,15 +224,39 @@ def version():
 def veda_tile_gather(geom, raster, tiled, layout=ROWS, inverse=False, stream=None):
     """raster: [B, N, H, d] tensor (any strides, last dim contiguous); tiled: contiguous
     tensor of B*H*N*d elements in `layout`.  inverse=True scatters tiled -> raster."""
+    dt = _elem_dtype(raster)
     if raster.stride(-1) != 1:
         raise VedaError("raster: last dimension must be contiguous")
-    _check("veda_tile_gather", lib().veda_tile_gather(
-        geom.ref, _dtype_code(raster), _p(raster, "raster", False), raster.stride(0), raster.stride(1),
-        raster.stride(2), _p(tiled, "tiled"), int(layout), int(bool(inverse)), _stream(stream)))
+    _call("veda_tile_gather",
+        geom.ref, _dtype_code(raster), _p(raster, "raster", False, dt, shape=_raster_shape(geom)),
+        raster.stride(0), raster.stride(1), raster.stride(2), _p(tiled, "tiled", True, dt, _tiled_numel(geom)),
+        int(layout), int(bool(inverse)), _stream(stream))
 
 
 def veda_trippool_workspace_bytes(geom, mlp_hidden, mlp_out):
     return int(lib().veda_trippool_workspace_bytes(geom.ref, int(mlp_hidden), int(mlp_out)))
+
+
+def _weights(geom, w1_q, w2_q, w1_k, w2_k):
+    """Checked pointers of the estimator weights and the MLP widths (hidden, out)."""
+    f32 = _torch().float32
+    H, d3 = geom.heads, 3 * geom.head_dim
+    if w1_q.dim() != 3 or w2_q.dim() != 3:
+        raise VedaError("w1 [H, 3d, hidden] and w2 [H, hidden, out] expected")
+    hidden, mout = int(w1_q.shape[-1]), int(w2_q.shape[-1])
+    ws = (_p(w1_q, "w1_q", True, f32, shape=(H, d3, hidden)), _p(w2_q, "w2_q", True, f32, shape=(H, hidden, mout)),
+          _p(w1_k, "w1_k", True, f32, shape=(H, d3, hidden)), _p(w2_k, "w2_k", True, f32, shape=(H, hidden, mout)))
+    return ws, hidden, mout
+
+
+def _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx):
+    torch = _torch()
+    B, H, nt = geom.batch, geom.heads, geom.n_tiles
+    rows = B * H * nt
+    return (_p(scores, "scores", True, torch.float32, rows * nt), _p(probs, "probs", True, torch.float32, rows * nt),
+            _p(q_desc, "q_desc", True, torch.float32, rows * 3 * geom.head_dim),
+            _p(k_desc, "k_desc", True, torch.float32, rows * 3 * geom.head_dim),
+            _p(idx, "idx", True, torch.int32, rows * max(int(topk), 0)))
 
 
 def veda_trippool_score(geom, q_tiled, k_tiled, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
@@ -175,42 +264,68 @@ def veda_trippool_score(geom, q_tiled, k_tiled, w1_q, w2_q, w1_k=None, w2_k=None
                         stream=None):
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
-    hidden, mout = int(w1_q.shape[-1]), int(w2_q.shape[-1])
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("veda_trippool_score", lib().veda_trippool_score(
-        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), _p(w1_q, "w1_q"),
-        _p(w2_q, "w2_q"), _p(w1_k, "w1_k"), _p(w2_k, "w2_k"), hidden, mout, float(score_scale),
-        _p(scores, "scores"), _p(probs, "probs"), _p(q_desc, "q_desc"), _p(k_desc, "k_desc"), int(topk),
-        _p(idx, "idx"), _p(workspace, "workspace"), ws_bytes, _stream(stream)))
+    dt = _elem_dtype(q_tiled)
+    n = _tiled_numel(geom)
+    qp, kp = _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n)
+    (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    _call("veda_trippool_score",
+        geom.ref, _dtype_code(q_tiled), qp, kp, a, b, c, e, hidden, mout, float(score_scale), *outs[:4], int(topk),
+        outs[4], _p(workspace, "workspace"), _ws(workspace), _stream(stream))
 
 
 def veda_topk_mask(scores, k, idx, mask=None, stream=None):
     """scores: [..., n_cols] float32 contiguous; idx: [..., k] int32; mask: [..., n_cols] uint8."""
+    torch = _torch()
     n_cols = int(scores.shape[-1])
-    rows = scores.numel() // n_cols
-    _check("veda_topk_mask", lib().veda_topk_mask(rows, n_cols, _p(scores, "scores"), int(k), _p(idx, "idx"),
-                                                   _p(mask, "mask"), _stream(stream)))
+    rows = scores.numel() // max(n_cols, 1)
+    sp = _p(scores, "scores", True, torch.float32)
+    _call("veda_topk_mask", rows, n_cols, sp, int(k),
+                                                   _p(idx, "idx", True, torch.int32, rows * int(k)),
+                                                   _p(mask, "mask", True, torch.uint8, rows * n_cols), _stream(stream))
+
+
+def _kv_idx(geom, kv_idx, k):
+    """Checked pointer of a kept-tile list [B, H, n_t, k]: its last dimension must be k."""
+    if kv_idx is None:
+        return None
+    if kv_idx.dim() < 1 or int(kv_idx.shape[-1]) != int(k):
+        raise VedaError(f"kv_idx: last dimension {tuple(kv_idx.shape)[-1:]} does not match k = {k}")
+    return _p(kv_idx, "kv_idx", True, _torch().int32, geom.batch * geom.heads * geom.n_tiles * int(k))
 
 
 def veda_sparse_attn_fwd(geom, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse=None,
-                         stream=None):
-    _check("veda_sparse_attn_fwd", lib().veda_sparse_attn_fwd(
-        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), _p(v_tiled, "v_tiled"),
-        _p(kv_idx, "kv_idx"), int(k), float(softmax_scale), _p(o_tiled, "o_tiled"), _p(lse, "lse"),
-        _stream(stream)))
+                         v_layout=COLS, stream=None):
+    """v_tiled holds V in v_layout; the library reads COLS only (anything else is refused)."""
+    dt = _elem_dtype(q_tiled)
+    n = _tiled_numel(geom)
+    _call("veda_sparse_attn_fwd",
+        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n),
+        _p(v_tiled, "v_tiled", True, dt, n), int(v_layout), _kv_idx(geom, kv_idx, k), int(k), float(softmax_scale),
+        _p(o_tiled, "o_tiled", True, dt, n),
+        _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tiled), _stream(stream))
 
 
 def veda_oracle_tilemap_workspace_bytes(geom, n_sel):
     return int(lib().veda_oracle_tilemap_workspace_bytes(geom.ref, int(n_sel)))
 
 
+def _tilemap_io(geom, q_tiles, n_sel, tilemap, lse):
+    torch = _torch()
+    bh = geom.batch * geom.heads
+    return (_p(q_tiles, "q_tiles", True, torch.int32, bh * int(n_sel)),
+            _p(tilemap, "tilemap", True, torch.float32, bh * int(n_sel) * geom.n_tiles),
+            _p(lse, "lse", True, torch.float32, bh * int(n_sel) * geom.tile))
+
+
 def veda_oracle_tilemap(geom, q_tiled, k_tiled, softmax_scale, q_tiles, n_sel, tilemap, lse=None, workspace=None,
                         stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("veda_oracle_tilemap", lib().veda_oracle_tilemap(
-        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), float(softmax_scale),
-        _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
-        ws_bytes, _stream(stream)))
+    dt = _elem_dtype(q_tiled)
+    n = _tiled_numel(geom)
+    qt, tm, lp = _tilemap_io(geom, q_tiles, n_sel, tilemap, lse)
+    _call("veda_oracle_tilemap",
+        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n),
+        float(softmax_scale), qt, int(n_sel), tm, lp, _p(workspace, "workspace"), _ws(workspace), _stream(stream))
 
 
 def veda_tiled_tokens(geom, dtype_code):
@@ -232,22 +347,24 @@ def veda_head_sq_error_workspace_bytes(batch, n_tokens, heads):
     return int(lib().veda_head_sq_error_workspace_bytes(int(batch), int(n_tokens), int(heads)))
 
 
-def veda_head_sq_error(a, b, err, ref_sq=None, workspace=None, stream=None):
+def veda_head_sq_error(a, b, err, ref_sq=None, workspace=None, err_batch_sum=None, stream=None):
     """a, b: contiguous raster [B, N, H, d] tensors of one dtype; err (and ref_sq): [B, H]
-    float32, written with sum (a - b)^2 (and sum b^2) per (batch, head).  workspace: a device
-    buffer of at least veda_head_sq_error_workspace_bytes(B, N, H) bytes; allocated on a's
-    device when None."""
+    float32, written with sum (a - b)^2 (and sum b^2) per (batch, head); err_batch_sum: [H]
+    float32, written with the sum of err over the batch.  workspace: a device buffer of at
+    least veda_head_sq_error_workspace_bytes(B, N, H) bytes; allocated on a's device when
+    None."""
+    torch = _torch()
     if a.shape != b.shape or a.dtype != b.dtype or a.dim() != 4:
         raise VedaError("a and b must be [B, N, H, d] tensors of one shape and dtype")
     B, N, H, d = (int(x) for x in a.shape)
+    outs = (_p(err, "err", True, torch.float32, B * H), _p(err_batch_sum, "err_batch_sum", True, torch.float32, H),
+            _p(ref_sq, "ref_sq", True, torch.float32, B * H))
     if workspace is None:
-        import torch
         workspace = torch.empty(max(1, veda_head_sq_error_workspace_bytes(B, N, H)), dtype=torch.uint8,
                                 device=a.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check("veda_head_sq_error", lib().veda_head_sq_error(
-        B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), _p(err, "err"), _p(ref_sq, "ref_sq"),
-        _p(workspace, "workspace"), ws_bytes, _stream(stream)))
+    _call("veda_head_sq_error",
+        B, N, H, d, _dtype_code(a), _p(a, "a"), _p(b, "b"), *outs, _p(workspace, "workspace"), _ws(workspace),
+        _stream(stream))
 
 
 def veda_distill_workspace_bytes(geom, n_sel):
@@ -258,12 +375,19 @@ def veda_distill_step(geom, q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1
                       workspace=None, stream=None):
     """One KL distillation step of the per-head estimator (shared Q/K MLP).  w1, w2 are
     updated in place when lr != 0; loss [1], dw1, dw2 are outputs."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("veda_distill_step", lib().veda_distill_step(
-        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled"), _p(k_tiled, "k_tiled"), _p(w1, "w1"), _p(w2, "w2"),
-        int(w1.shape[-1]), int(w2.shape[-1]), float(score_scale), _p(q_tiles, "q_tiles"), int(q_tiles.shape[-1]),
-        _p(target, "target"), _p(loss, "loss"), _p(dw1, "dw1"), _p(dw2, "dw2"), float(lr), _p(workspace, "workspace"),
-        ws_bytes, _stream(stream)))
+    torch = _torch()
+    dt = _elem_dtype(q_tiled)
+    n = _tiled_numel(geom)
+    (a, b, _, _), hidden, mout = _weights(geom, w1, w2, w1, w2)
+    n_sel = int(q_tiles.shape[-1])
+    bh = geom.batch * geom.heads
+    _call("veda_distill_step",
+        geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n), a,
+        b, hidden, mout, float(score_scale), _p(q_tiles, "q_tiles", True, torch.int32, bh * n_sel), n_sel,
+        _p(target, "target", True, torch.float32, bh * n_sel * geom.n_tiles),
+        _p(loss, "loss", True, torch.float32, 1), _p(dw1, "dw1", True, torch.float32, shape=tuple(w1.shape)),
+        _p(dw2, "dw2", True, torch.float32, shape=tuple(w2.shape)), float(lr), _p(workspace, "workspace"),
+        _ws(workspace), _stream(stream))
 
 
 def _raster_strides(*ts):
@@ -275,13 +399,19 @@ def _raster_strides(*ts):
     return st
 
 
-def _k_operand(q, k, k_layout, *others):
+def _raster(geom, t, name, dt):
+    """Checked pointer of a raster [B, N, H, d] operand (strided; last dim contiguous)."""
+    return _p(t, name, False, dt, shape=_raster_shape(geom))
+
+
+def _k_operand(geom, q, k, k_layout, *others):
     """Strides shared by the raster operands, and the checked K pointer."""
+    dt = _elem_dtype(q)
     if k_layout == RASTER:
-        return _raster_strides(q, k, *others), _p(k, "k", False)
+        return _raster_strides(q, k, *others), _raster(geom, k, "k", dt)
     if k_layout != ROWS:
         raise VedaError("k_layout must be RASTER or ROWS")
-    return _raster_strides(q, *others), _p(k, "k")
+    return _raster_strides(q, *others), _p(k, "k", True, dt, _tiled_numel(geom))
 
 
 def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125, scores=None,
@@ -291,31 +421,33 @@ def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, sco
     raster too, or tile-major with k_layout=ROWS."""
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
-    rs, kp = _k_operand(q, k, k_layout)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("veda_trippool_score_raster", lib().veda_trippool_score_raster(
-        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, _p(w1_q, "w1_q"), _p(w2_q, "w2_q"),
-        _p(w1_k, "w1_k"), _p(w2_k, "w2_k"), int(w1_q.shape[-1]), int(w2_q.shape[-1]), float(score_scale),
-        _p(scores, "scores"), _p(probs, "probs"), _p(q_desc, "q_desc"), _p(k_desc, "k_desc"), int(topk),
-        _p(idx, "idx"), _p(workspace, "workspace"), ws_bytes, _stream(stream)))
+    rs, kp = _k_operand(geom, q, k, k_layout)
+    qp = _raster(geom, q, "q", _elem_dtype(q))
+    (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    _call("veda_trippool_score_raster",
+        geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e, hidden, mout, float(score_scale),
+        *outs[:4], int(topk), outs[4], _p(workspace, "workspace"), _ws(workspace), _stream(stream))
 
 
 def veda_sparse_attn_fwd_raster(geom, q, k, v_cols, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
-                                stream=None):
+                                v_layout=COLS, stream=None):
     """veda_sparse_attn_fwd with raster Q and output O [B, N, H, d]; K raster or tile-major
     (k_layout=ROWS); V channel-major tiled; lse [B, H, N] in raster token order."""
-    rs, kp = _k_operand(q, k, k_layout, o)
-    _check("veda_sparse_attn_fwd_raster", lib().veda_sparse_attn_fwd_raster(
-        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, _p(v_cols, "v_cols"),
-        _p(kv_idx, "kv_idx"), int(kk), float(softmax_scale), _p(o, "o", False), _p(lse, "lse"), _stream(stream)))
+    dt = _elem_dtype(q)
+    rs, kp = _k_operand(geom, q, k, k_layout, o)
+    _call("veda_sparse_attn_fwd_raster",
+        geom.ref, _dtype_code(q), _raster(geom, q, "q", dt), kp, int(k_layout), *rs,
+        _p(v_cols, "v_cols", True, dt, _tiled_numel(geom)), int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
+        float(softmax_scale), _raster(geom, o, "o", dt),
+        _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tiled), _stream(stream))
 
 
 def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilemap, lse=None, workspace=None,
                                k_layout=RASTER, stream=None):
     """veda_oracle_tilemap on raster Q [B, N, H, d]; K raster or tile-major (k_layout=ROWS)."""
-    rs, kp = _k_operand(q, k, k_layout)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("veda_oracle_tilemap_raster", lib().veda_oracle_tilemap_raster(
-        geom.ref, _dtype_code(q), _p(q, "q", False), kp, int(k_layout), *rs, float(softmax_scale),
-        _p(q_tiles, "q_tiles"), int(n_sel), _p(tilemap, "tilemap"), _p(lse, "lse"), _p(workspace, "workspace"),
-        ws_bytes, _stream(stream)))
+    rs, kp = _k_operand(geom, q, k, k_layout)
+    qt, tm, lp = _tilemap_io(geom, q_tiles, n_sel, tilemap, lse)
+    _call("veda_oracle_tilemap_raster",
+        geom.ref, _dtype_code(q), _raster(geom, q, "q", _elem_dtype(q)), kp, int(k_layout), *rs,
+        float(softmax_scale), qt, int(n_sel), tm, lp, _p(workspace, "workspace"), _ws(workspace), _stream(stream))

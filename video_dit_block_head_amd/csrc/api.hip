@@ -209,14 +209,15 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
 }
 
 veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
-                                 const void *v_tiled, const int32_t *kv_idx, int32_t k, float softmax_scale,
-                                 void *o_tiled, float *lse, hipStream_t stream) {
+                                 const void *v_tiled, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
+                                 float softmax_scale, void *o_tiled, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
   veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !v_tiled || !kv_idx || !o_tiled) return VEDA_ERR_NULL;
+  if (v_layout != VEDA_TILE_COLS) return VEDA_ERR_UNSUPPORTED;  // V is read channel-major only
   if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
   const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, o_tiled, lse};
   for (const void *p : ptrs)
@@ -228,13 +229,14 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
                                         const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
                                         int64_t rs_h,
-                                        const void *v_cols, const int32_t *kv_idx, int32_t k, float softmax_scale,
-                                        void *o_raster, float *lse, hipStream_t stream) {
+                                        const void *v_cols, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
+                                        float softmax_scale, void *o_raster, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   veda_status s = check_geom(g, dtype, &geo, &hs);
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !v_cols || !kv_idx || !o_raster) return VEDA_ERR_NULL;
+  if (v_layout != VEDA_TILE_COLS) return VEDA_ERR_UNSUPPORTED;
   if (k < 1 || k > geo.nt) return VEDA_ERR_SHAPE;
   const void *ptrs[] = {q_raster, k_raster, v_cols, kv_idx, o_raster, lse};
   for (const void *p : ptrs)
@@ -337,8 +339,8 @@ size_t veda_head_sq_error_workspace_bytes(int32_t batch, int32_t n_tokens, int32
 }
 
 veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, int32_t head_dim, veda_dtype dtype,
-                               const void *a, const void *b, float *err, float *ref_sq, void *workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               const void *a, const void *b, float *err, float *err_batch_sum, float *ref_sq,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != VEDA_F32 && dtype != VEDA_BF16) return VEDA_ERR_DTYPE;
   if (batch < 1 || n_tokens < 1 || heads < 1 || head_dim < 1 || batch > 65535 || heads > 65535)
     return VEDA_ERR_SHAPE;
@@ -346,7 +348,8 @@ veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, i
   if (((int64_t)head_dim * eb) % 16 != 0) return VEDA_ERR_SHAPE;
   if (!a || !b || !err) return VEDA_ERR_NULL;
   if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(err) & 3u) ||
-      (reinterpret_cast<uintptr_t>(ref_sq) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+      (reinterpret_cast<uintptr_t>(ref_sq) & 3u) || (reinterpret_cast<uintptr_t>(err_batch_sum) & 3u) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 7u))
     return VEDA_ERR_ALIGN;
   // one chunk's 16-byte pieces are counted in 32 bits
   const int64_t chunk_rows = ((int64_t)n_tokens + head_sq_error_chunks(n_tokens) - 1) / head_sq_error_chunks(n_tokens);
@@ -354,7 +357,8 @@ veda_status veda_head_sq_error(int32_t batch, int32_t n_tokens, int32_t heads, i
   if (workspace == nullptr || workspace_bytes < veda_head_sq_error_workspace_bytes(batch, n_tokens, heads))
     return VEDA_ERR_WORKSPACE;
   return hip_status(
-      launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, ref_sq, workspace, stream));
+      launch_head_sq_error(batch, n_tokens, heads, head_dim, dtype, a, b, err, err_batch_sum, ref_sq, workspace,
+                           stream));
 }
 
 int64_t veda_tiled_tokens(const veda_geom *g, veda_dtype dtype) {

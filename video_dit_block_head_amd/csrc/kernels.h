@@ -54,6 +54,7 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
 
 int head_sq_error_chunks(int n_tokens);  // token chunks per head (one partial pair each)
 hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,
-                                const void *b, float *err, float *ref_sq, void *ws, hipStream_t st);
+                                const void *b, float *err, float *err_batch_sum, float *ref_sq, void *ws,
+                                hipStream_t st);
 
 }  // namespace veda

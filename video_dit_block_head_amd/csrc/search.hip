@@ -7,8 +7,9 @@
 // (head, chunk, batch) streams the chunk's d-element rows of both raster tensors in 16-byte
 // pieces (8 pieces of each tensor in flight per thread), accumulates sum (a - b)^2 and
 // sum b^2 in fp32 and writes one partial pair.  A second kernel adds each head's C partials
-// in a fixed order, so the result is deterministic.  HBM-bound; B*H*C workgroups (C up to
-// 256) keep every CU streaming, where one workgroup per head would leave most of them idle.
+// in a fixed order, and then the batches in ascending order, so the result is
+// deterministic.  HBM-bound; B*H*C workgroups (C up to 256) keep every CU streaming, where
+// one workgroup per head would leave most of them idle.
 #include "common.h"
 #include "kernels.h"
 
@@ -88,29 +89,38 @@ __global__ void __launch_bounds__(SE_THREADS) head_sq_error_kernel(const uint8_t
   }
 }
 
-// One wave per (batch, head): lane l adds partials l, l + 64, ... in order, then a fixed
-// butterfly adds the lanes.
+// One wave per head: for b = 0, 1, ... in turn, lane l adds that (batch, head)'s partials
+// l, l + 64, ... in order and a fixed butterfly adds the lanes (err[b, h]); the batch sum
+// adds those per-batch results in ascending b.
 __global__ void __launch_bounds__(256) head_sq_error_sum_kernel(const float2 *__restrict__ part, int chunks,
-                                                                int rows, float *__restrict__ err,
+                                                                int batch, int heads, float *__restrict__ err,
+                                                                float *__restrict__ err_batch_sum,
                                                                 float *__restrict__ ref_sq) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= rows) return;  // whole wave
-  float se = 0.f, sr = 0.f;
-  for (int c = lane; c < chunks; c += 64) {
-    const float2 p = part[(int64_t)row * chunks + c];
-    se += p.x;
-    sr += p.y;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= heads) return;  // whole wave
+  float total = 0.f;
+  for (int bb = 0; bb < batch; ++bb) {
+    const int64_t row = (int64_t)bb * heads + h;
+    float se = 0.f, sr = 0.f;
+    for (int c = lane; c < chunks; c += 64) {
+      const float2 p = part[row * chunks + c];
+      se += p.x;
+      sr += p.y;
+    }
+    se = wave_sum(se);
+    sr = wave_sum(sr);
+    total += se;
+    if (lane == 0) {
+      err[row] = se;
+      if (ref_sq != nullptr) ref_sq[row] = sr;
+    }
   }
-  se = wave_sum(se);
-  sr = wave_sum(sr);
-  if (lane == 0) {
-    err[row] = se;
-    if (ref_sq != nullptr) ref_sq[row] = sr;
-  }
+  if (lane == 0 && err_batch_sum != nullptr) err_batch_sum[h] = total;
 }
 
 hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,
-                                const void *b, float *err, float *ref_sq, void *ws, hipStream_t st) {
+                                const void *b, float *err, float *err_batch_sum, float *ref_sq, void *ws,
+                                hipStream_t st) {
   const int chunks = head_sq_error_chunks(n_tokens);
   float2 *part = static_cast<float2 *>(ws);
   const dim3 grid(heads, chunks, batch);
@@ -120,8 +130,8 @@ hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim
   else
     head_sq_error_kernel<4><<<grid, SE_THREADS, 0, st>>>((const uint8_t *)a, (const uint8_t *)b, n_tokens, heads,
                                                           head_dim, chunks, part);
-  const int rows = batch * heads;
-  head_sq_error_sum_kernel<<<dim3((rows + 3) / 4), 256, 0, st>>>(part, chunks, rows, err, ref_sq);
+  head_sq_error_sum_kernel<<<dim3((heads + 3) / 4), 256, 0, st>>>(part, chunks, batch, heads, err, err_batch_sum,
+                                                                   ref_sq);
   return hipGetLastError();
 }
 

@@ -160,12 +160,14 @@ def search_tile_shapes(grid, tile, candidates, q, k, v, w1, w2, topk, score_scal
     q, k, v: raster [B, N, H, d] GPU tensors; candidates: list of (p_t, p_h, p_w).
     Returns (choice: list of candidate indices per head, err [C, B, H] and ref [B, H] as
     float32 GPU tensors, ref being the squared norm of the full output).  The outputs,
-    errors and norms come from the library's kernels; only the argmin is taken here."""
+    errors, batch sums and norms come from the library's kernels; only the argmin over the
+    candidates is taken here."""
     B, N, H, d = (int(x) for x in q.shape)
     dt = q.dtype
     if not candidates:
         raise ValueError("no candidate tilings")
     err = torch.empty((len(candidates), B, H), dtype=torch.float32, device=device)
+    total = torch.empty((len(candidates), H), dtype=torch.float32, device=device)
     ref = torch.empty((B, H), dtype=torch.float32, device=device)
     full = torch.empty_like(q)
     # full attention: every key tile kept (the un-tiled output does not depend on the tiling)
@@ -180,7 +182,7 @@ def search_tile_shapes(grid, tile, candidates, q, k, v, w1, w2, topk, score_scal
         sa = SparseAttention(Geom(B, H, d, grid, tile, [tuple(shape)] * H), dt, w1, w2, score_scale=score_scale,
                              softmax_scale=softmax_scale, device=device)
         sa.forward(q, k, v, topk, out)
-        veda_head_sq_error(out, full, err[ci], ref if ci == 0 else None, workspace=ws)
-    total = err.sum(dim=1).cpu()
+        veda_head_sq_error(out, full, err[ci], ref if ci == 0 else None, workspace=ws, err_batch_sum=total[ci])
+    total = total.cpu()
     choice = [int(torch.argmin(total[:, h]).item()) for h in range(H)]
     return choice, err, ref
