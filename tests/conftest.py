@@ -15,6 +15,22 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
 
 
+_MEASURES = []
+
+
+def record_measure(line):
+    """Keep one line of achieved parity figures (errors, exempt rows, recall); the terminal
+    summary prints them even under -q, so a run's log records what each gate saw."""
+    _MEASURES.append(str(line))
+
+
+def pytest_terminal_summary(terminalreporter):
+    if _MEASURES:
+        terminalreporter.section("parity measures")
+        for line in _MEASURES:
+            terminalreporter.write_line(line)
+
+
 def gpu_visible():
     """Whether this process can see a GPU (counting devices initialises no HIP context)."""
     try:

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle.veda_oracle as O
+from conftest import record_measure
 from workloads import SHAPES_128, get, make, padded_variant
 
 pytestmark = pytest.mark.gpu
@@ -34,8 +35,8 @@ CASES = {
                                             shape_list=((8, 4, 4), (2, 8, 8), (16, 2, 4)), topk=(80,), seed=12,
                                             sampled_q_tiles=8), None, None),
     "mid-padded": (padded_variant(get(2), sampled_q_tiles=32), 3, 16),
-    "large-padded": (padded_variant(get(3), topk=(60,)), 2, 8),
-    "long-padded": (padded_variant(get(4), topk=(120,)), 2, 4),
+    "large-padded": (padded_variant(get(3), topk=(60,)), 4, 16),
+    "long-padded": (padded_variant(get(4), topk=(120,)), 4, 8),
 }
 # Position -> key order inside a channel-major tile: groups of 16 ordered 0-3, 8-11, 4-7, 12-15
 COLS_KEY = np.array([16 * (p // 16) + [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15][p % 16]
@@ -45,6 +46,11 @@ COLS_KEY = np.array([16 * (p // 16) + [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12,
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def measure(line):
+    say(line)
+    record_measure(line)
 
 
 def to_dev_raster(arr_hm):
@@ -173,7 +179,8 @@ def test_padded_scores_topk(r):
             assert ok, (cfg.name, h, i, idx[i])
             exempt += ex
             rows += 1
-    say(f"[gpu-padded] {cfg.name}: score max|err| {worst:.3g}, {exempt}/{rows} rows in the near-tie band")
+    measure(f"[gpu-padded] {cfg.name}: score max|err| {worst:.3g} over {rows} rows of {len(r.pairs())} heads, "
+            f"{exempt} rows in the near-tie band")
     assert worst <= 2e-5
 
 
@@ -199,7 +206,8 @@ def test_padded_attention(r):
         sl = slots[slots >= 0]
         assert bitwise_equal(host(r.out[b, :, h])[sl], host(r.sa.o_t[b, h])[:len(slots)][slots >= 0]), (cfg.name, h)
     rel = math.sqrt(num / den)
-    say(f"[gpu-padded] {cfg.name} k={r.kk}: max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
+    measure(f"[gpu-padded] {cfg.name} k={r.kk}: {len(r.pairs())} heads: max|dO| {mx:.3g}  relFro {rel:.3g}  "
+            f"max|dLSE| {lse_err:.3g}")
     assert mx <= 2e-2 and rel <= 1e-2 and lse_err <= 4e-3
 
 
@@ -215,7 +223,7 @@ def test_padded_tilemap(r):
     torch.cuda.synchronize()
     tmh = host(tm)
     worst = 0.0
-    n_check = 4 if r.n_tiles_checked is not None else n_sel
+    n_check = 8 if r.n_tiles_checked is not None else n_sel
     for b, h in r.pairs():
         qt, kt, _, slots = r.oracle_head(b, h)
         ntile = len(slots) // P
@@ -228,5 +236,5 @@ def test_padded_tilemap(r):
         keep = ref >= 1e-30
         assert np.all(got[~keep] < 1e-25)
         worst = max(worst, float(np.abs(np.log(got[keep]) - np.log(ref[keep])).max()))
-    say(f"[gpu-padded] {cfg.name}: tile map max|dlog M| {worst:.3g}")
+    measure(f"[gpu-padded] {cfg.name}: tile map {n_check} rows x {len(r.pairs())} heads: max|dlog M| {worst:.3g}")
     assert worst <= 1e-3

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle.veda_oracle as O
+from conftest import record_measure
 from workloads import get, make
 
 pytestmark = pytest.mark.gpu
@@ -24,6 +25,12 @@ from video_dit_block_head_amd.pipeline import SparseAttention, dense_index  # no
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def measure(line):
+    """Print a line of achieved figures and keep it for the run's terminal summary."""
+    say(line)
+    record_measure(line)
 
 
 def to_dev_raster(arr_hm, bf16):
@@ -99,7 +106,7 @@ def r(request):
 
 
 HEAD_LIMIT = {0: None, 1: None, 2: None, 3: 6, 4: 4}        # heads for bit-exact layout checks
-SCORE_HEADS = {0: None, 1: None, 2: None, 3: None, 4: 16}   # heads for index parity
+SCORE_HEADS = {0: None, 1: None, 2: None, 3: None, 4: None}  # heads for index parity (all)
 
 
 # Position -> key order inside a channel-major tile: groups of 16 ordered 0-3, 8-11, 4-7, 12-15
@@ -166,8 +173,14 @@ def test_scores_and_topk(r):
                 assert ok, (cfg.name, h, i, idx[i], np.sort(s32[i])[::-1][kk - 2:kk + 2])
                 exempt += ex
                 rows += 1
-    say(f"[gpu-parity] {cfg.name}: score max|err| {worst:.3g}, {exempt}/{rows} rows in the near-tie band")
-    assert worst <= 2e-5
+    measure(f"[gpu-parity] {cfg.name}: score max|err| {worst:.3g} over {rows} rows of "
+            f"{len(r.heads(SCORE_HEADS[ci]))} heads, {exempt} rows in the near-tie band")
+    # fp32 MLP and score products against float64: about 1e-6 of the logit (|S| <= 16 here,
+    # 14 fp32 ulps); measured 1.6e-6 (tiny) to 9.3e-6 (long) over every row of every head
+    assert worst <= SCORE_TOL
+
+
+SCORE_TOL = 1.25e-5   # absolute, on the fp32 logits
 
 
 # ----------------------------------------------------------------------------- attention
@@ -201,14 +214,18 @@ def tol(r):
 
 
 def test_sparse_attention(r):
-    ci = r.cfg.index
-    heads = r.heads(None if ci < 4 else 24)
+    heads = r.heads()
     mx, rel, lse_err = attention_errors(r, r.idx, r.kk, heads, lse=r.lse)
-    say(f"[gpu-parity] {r.cfg.name} k={r.kk}: max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
+    measure(f"[gpu-parity] {r.cfg.name} k={r.kk}: {len(heads)} heads x {len(r.q_tiles(0))} query tiles: "
+            f"max|dO| {mx:.3g}  relFro {rel:.3g}  max|dLSE| {lse_err:.3g}")
     amax, arel = tol(r)
     assert mx <= amax and rel <= arel
-    # bf16: the kernel's normaliser sums the bf16-rounded probabilities (relative rounding
-    # <= 2^-9 each), so its log can differ from the exact LSE by up to ~2e-3.
+    # bf16: the kernel's normaliser sums the probabilities after rounding them to bf16 (the
+    # values that multiply V).  Round-to-nearest-even changes each by at most the bf16 unit
+    # roundoff 2^-8 = 3.9e-3 relative, so the sum, and with it exp(LSE), by at most that
+    # much when every kept probability rounds the same way (a near one-hot row whose
+    # dominant probability sits just above a power of two).  The fp32 accumulation adds
+    # far less.  Gate: 4e-3 on the natural-log LSE.
     assert lse_err <= (4e-3 if r.bf16 else 1e-5)
 
 
@@ -229,10 +246,11 @@ def test_dense_path(r):
     say(f"[gpu-parity] {cfg.name}: dense path k={cfg.n_tiles}")
     V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, cfg.n_tiles, 1 / math.sqrt(cfg.head_dim), o_t)
     torch.cuda.synchronize()
-    heads = r.heads({0: None, 1: None, 2: 3, 3: 2, 4: 1}[ci])
-    tph = {0: None, 1: None, 2: 8, 3: 4, 4: 2}[ci]
+    heads = r.heads({0: None, 1: None, 2: 4, 3: 4, 4: 4}[ci])
+    tph = {0: None, 1: None, 2: 8, 3: 8, 4: 4}[ci]
     mx, rel, _ = attention_errors(r, idx, cfg.n_tiles, heads, tiles_per_head=tph, o_t=o_t)
-    say(f"[gpu-parity] {cfg.name} dense: max|dO| {mx:.3g}  relFro {rel:.3g}")
+    measure(f"[gpu-parity] {cfg.name} dense (k = {cfg.n_tiles}): {len(heads)} heads x {tph or 'all'} query tiles: "
+            f"max|dO| {mx:.3g}  relFro {rel:.3g}")
     amax, arel = tol(r)
     assert mx <= amax and rel <= arel
 
@@ -241,23 +259,29 @@ def test_sparsity_sweep(r):
     cfg = r.cfg
     if len(cfg.topk) < 3:
         pytest.skip("no sparsity sweep for this workload")
-    # the selections themselves, on one head: every row against the oracle's fp32 scores
+    # the selections themselves, on four heads: every row against the oracle's fp32 scores
     # (k up to 240 exercises the compacted search over up to 512 candidates on long rows)
-    h = int(r.heads(1)[0])
-    qt, kt, _, _ = r.oracle_head(0, h)
-    s32 = O.tile_scores(O.mlp(O.trippool(qt, cfg.tile), r.wl.w1[h], r.wl.w2[h]),
-                        O.mlp(O.trippool(kt, cfg.tile), r.wl.w1[h], r.wl.w2[h]), cfg.score_scale).astype(np.float32)
+    sel_heads = [int(h) for h in r.heads(4)]
+    s32 = {}
+    for h in sel_heads:
+        qt, kt, _, _ = r.oracle_head(0, h)
+        s32[h] = O.tile_scores(O.mlp(O.trippool(qt, cfg.tile), r.wl.w1[h], r.wl.w2[h]),
+                               O.mlp(O.trippool(kt, cfg.tile), r.wl.w1[h], r.wl.w2[h]),
+                               cfg.score_scale).astype(np.float32)
     for kk in cfg.topk[1:-1]:
         idx = r.sa.score(kk)
-        got = host(idx[0, h]).astype(np.int64)
-        for i in range(cfg.n_tiles):
-            assert O.topk_agrees(s32[i], got[i], kk)[0], (cfg.name, kk, h, i)
+        for h in sel_heads:
+            got = host(idx[0, h]).astype(np.int64)
+            for i in range(cfg.n_tiles):
+                assert O.topk_agrees(s32[h][i], got[i], kk)[0], (cfg.name, kk, h, i)
         o_t = torch.empty_like(r.sa.o_t)
         say(f"[gpu-parity] {cfg.name}: k={kk}")
         V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, kk, 1 / math.sqrt(cfg.head_dim), o_t)
         torch.cuda.synchronize()
-        mx, rel, _ = attention_errors(r, idx, kk, r.heads(4), tiles_per_head=16, o_t=o_t)
-        say(f"[gpu-parity] {cfg.name} k={kk}: max|dO| {mx:.3g}  relFro {rel:.3g}")
+        heads = r.heads(8)
+        mx, rel, _ = attention_errors(r, idx, kk, heads, tiles_per_head=16, o_t=o_t)
+        measure(f"[gpu-parity] {cfg.name} k={kk}: {len(heads)} heads x 16 query tiles: max|dO| {mx:.3g}  "
+                f"relFro {rel:.3g}")
         assert mx <= 2e-2 and rel <= 1e-2
 
 
@@ -282,6 +306,22 @@ def test_topk_compaction_widths(r):
 
 
 # ----------------------------------------------------------------------------- tile map
+# Map rows compared with the oracle: every head on `each` query tiles (seeded choice among the
+# head's selected tiles), and every selected tile on the first `full` heads.
+MAP_CHECK = {0: (None, 1), 1: (None, 12), 2: (16, 1), 3: (8, 2), 4: (8, 2)}
+# |log M_gpu - log M_oracle| on entries >= 1e-30, bf16 inputs / fp32 inputs: both sides use
+# the same rounded inputs, so only the fp32 accumulation of the logits and of the row
+# log-sum-exp differs (measured <= 2.5e-5 at N = 153 600, 1.8e-6 for the fp32 workload)
+MAP_LOG_TOL = {True: 1e-4, False: 1e-5}
+
+
+def map_rows(cfg, h, n_sel):
+    each, full = MAP_CHECK[cfg.index]
+    if each is None or h < full or each >= n_sel:
+        return np.arange(n_sel)
+    return np.sort(np.random.default_rng(cfg.seed + 3000 + h).choice(n_sel, each, replace=False))
+
+
 def test_tilemap_and_recall(r):
     cfg, ci = r.cfg, r.cfg.index
     B, H, nt, P = cfg.batch, cfg.heads, cfg.n_tiles, cfg.tile
@@ -292,38 +332,49 @@ def test_tilemap_and_recall(r):
     say(f"[gpu-parity] {cfg.name}: tile map, {n_sel} query tiles per head")
     r.sa.tilemap(qtl, n_sel, tm, lse)
     torch.cuda.synchronize()
-    # oracle mask = top-k of the map (GPU top-k vs oracle top-k on the same map)
+    # oracle mask = top-k of the map: the library's top-k of the library's map
     omask = torch.empty((B, H, n_sel, r.kk), dtype=torch.int32, device="cuda")
     V.veda_topk_mask(tm, r.kk, omask)
     torch.cuda.synchronize()
     tmh, omh = host(tm), host(omask).astype(np.int64)
-    check_heads = r.heads({0: None, 1: 4, 2: 2, 3: 2, 4: 1}[ci])
-    n_check = {0: None, 1: 8, 2: 4, 3: 4, 4: 2}[ci]
-    worst = 0.0
+    tol_log = MAP_LOG_TOL[r.bf16]
+    worst, n_rows, n_band = 0.0, 0, 0
     for b in range(B):
-        for h in check_heads:
+        for h in range(H):
             qt, kt, _, _ = r.oracle_head(b, h)
-            sel = np.arange(n_sel) if n_check is None else np.linspace(0, n_sel - 1, n_check).astype(int)
+            sel = map_rows(cfg, h, n_sel)
             ref = O.tilemap(qt, kt, P, 1 / math.sqrt(cfg.head_dim), q_tiles=r.q_tiles(h)[sel])
             got = tmh[b, h, sel]
             keep = ref >= 1e-30
-            assert np.all(got[~keep] < 1e-25)
+            assert np.all(got[~keep] < 1e-25), (cfg.name, h)
             worst = max(worst, float(np.abs(np.log(got[keep]) - np.log(ref[keep])).max()))
             assert np.all(got <= 1.0 + 1e-6)
+            # the oracle mask against the oracle's own top-k of the oracle's map: entries of the
+            # two maps agree to tol_log in log space, so two entries closer than 2 tol_log may
+            # trade places (near-tie band, taken on log M)
+            lref = np.log(np.maximum(ref, 1e-300))
+            for a, row in enumerate(sel):
+                ok, ex = O.topk_agrees(lref[a], omh[b, h, row], r.kk, gap=2 * tol_log)
+                assert ok, (cfg.name, h, int(row), omh[b, h, row], O.topk_rows(lref[a][None], r.kk)[0])
+                n_band += ex
+            n_rows += len(sel)
+        # every row: the library's top-k picks the k largest of the library's map
         for h in range(H):
             for a in range(n_sel):
                 ok, _ = O.topk_agrees(tmh[b, h, a].astype(np.float64), omh[b, h, a], r.kk, gap=1e-12)
                 assert ok
     est = host(r.idx).astype(np.int64)
     recall = np.mean([O.recall(est[b, h][r.q_tiles(h)], omh[b, h]) for b in range(B) for h in range(H)])
-    say(f"[gpu-parity] {cfg.name}: tile map max|dlog M| {worst:.3g}; estimator recall vs oracle mask {recall:.3f}")
-    assert worst <= (1e-3 if r.bf16 else 1e-5)
+    measure(f"[gpu-parity] {cfg.name}: tile map {n_rows} rows of {B * H} heads vs oracle: max|dlog M| {worst:.3g}; "
+            f"oracle mask equal to the oracle's top-k ({n_band} rows in the near-tie band); "
+            f"estimator recall vs oracle mask {recall:.3f}")
+    assert worst <= tol_log
 
 
 # ----------------------------------------------------------------------------- determinism, edges
 def test_determinism(r):
-    if r.cfg.index not in (1, 2):
-        pytest.skip("checked on the small and mid workloads")
+    if r.cfg.index not in (1, 2, 3):
+        pytest.skip("checked on the small, mid and large workloads")
     o1 = r.sa.o_t.clone()
     i1 = r.idx.clone()
     idx = r.sa.score(r.kk)
