@@ -74,7 +74,9 @@ enum {
   VEDA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim/tile for this dtype) */
   VEDA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes query */
   VEDA_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
-  VEDA_ERR_HIP = -7          /* a HIP launch failed; see veda_last_hip_error() */
+  VEDA_ERR_HIP = -7,         /* a HIP launch failed; see veda_last_hip_error() */
+  VEDA_ERR_SCRATCH = -8      /* the problem needs more than the library's static scratch
+                                (veda_trippool_score_raster_noalloc) */
 };
 
 typedef enum { VEDA_F32 = 0, VEDA_BF16 = 1 } veda_dtype;
@@ -218,6 +220,24 @@ veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, con
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
                                        float *lse, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* veda_trippool_score_raster without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It allocates nothing: the MLP outputs go to a static device
+ * array of 32 MiB inside the library (each GPU it runs on holds one until the process
+ * ends), which bounds the problem to B * H * n_t <= 65536 tiles (e.g. 48 heads of 1200
+ * tiles); a larger geometry returns VEDA_ERR_SCRATCH with nothing launched.  The first
+ * call on a device looks up that device's copy (hipGetSymbolAddress); the stream must
+ * belong to the current device.  Every call on one GPU shares its copy: calls that
+ * overlap on one GPU (other streams, other host threads) race, so the caller orders
+ * them.  Arguments, outputs and every other status as in veda_trippool_score_raster. */
+veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dtype, const void *q_raster,
+                                               const void *k, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
+                                               int64_t rs_h, const float *w1_q, const float *w2_q,
+                                               const float *w1_k, const float *w2_k, int32_t mlp_hidden,
+                                               int32_t mlp_out, float score_scale, float *scores, float *probs,
+                                               float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
+                                               hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
  * gradients of the sampled Q tiles and of every K tile, per-row KL terms). */

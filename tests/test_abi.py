@@ -36,7 +36,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 20, syms
     for s in syms:
         assert hasattr(L, s), s
 
@@ -275,3 +275,26 @@ def test_binding_checks_sizes_before_taking_pointers():
     # well-formed CPU tensors get as far as the device check
     with pytest.raises(V.VedaError, match="GPU tensor"):
         V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(2 * 32 * 4).view(1, 2, 32, 4), 4, 0.088, bf(n))
+
+
+def test_noalloc_scoring_rejects_beyond_its_scratch(L):
+    """The no-allocation scoring call holds the MLP outputs of at most 65536 tiles (32 MiB of
+    static scratch): a larger geometry is refused with VEDA_ERR_SCRATCH before anything runs,
+    and its own argument checks are those of the workspace call."""
+    f = L.veda_trippool_score_raster_noalloc
+    RAS = V.RASTER
+    big = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 56)        # 56 heads x 1200 tiles = 67200
+    st = (153600 * 56 * 128, 56 * 128, 128)
+    assert f(big.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A,
+             None) == -8
+    assert b"scratch" in L.veda_status_str(-8)
+    fits = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 54)       # 64800 tiles: passes the size check,
+    st = (153600 * 54 * 128, 54 * 128, 128)                         # then a NULL K is refused
+    assert f(fits.ref, V.BF16, A, None, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A,
+             None) == NULL
+    g = geom()
+    st = (4096 * 2 * 128, 2 * 128, 128)
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None,
+             None) == NULL
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 512, 64, 0.125, None, None, None, None, 6, A,
+             None) == UNSUP

@@ -100,6 +100,8 @@ def lib():
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
                                                  vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+            "veda_trippool_score_raster_noalloc": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32,
+                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp]),
             "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
                                                   vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
@@ -451,3 +453,18 @@ def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilema
     _call("veda_oracle_tilemap_raster",
         geom.ref, _dtype_code(q), _raster(geom, q, "q", _elem_dtype(q)), kp, int(k_layout), *rs,
         float(softmax_scale), qt, int(n_sel), tm, lp, _p(workspace, "workspace"), _ws(workspace), _stream(stream))
+
+
+def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
+                                       scores=None, probs=None, q_desc=None, k_desc=None, topk=0, idx=None,
+                                       k_layout=RASTER, stream=None):
+    """veda_trippool_score_raster with no workspace: the library's static scratch holds the
+    MLP outputs (B * H * n_t <= 65536 tiles; calls that overlap on one GPU race)."""
+    w1_k = w1_q if w1_k is None else w1_k
+    w2_k = w2_q if w2_k is None else w2_k
+    rs, kp = _k_operand(geom, q, k, k_layout)
+    qp = _raster(geom, q, "q", _elem_dtype(q))
+    (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    _call("veda_trippool_score_raster_noalloc", geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e,
+          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _stream(stream))

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -108,6 +110,63 @@ veda_status check_raster(const Geo &geo, const HeadShapes &hs, veda_dtype dt, in
   return VEDA_OK;
 }
 
+// Validation shared by the raster scoring calls: everything but the workspace.  Fills the
+// kernels' geometry, shapes and raster byte strides.
+veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k_raster,
+                               veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h, const float *w1_q,
+                               const float *w2_q, const float *w1_k, const float *w2_k, int32_t mlp_hidden,
+                               int32_t mlp_out, const float *scores, const float *probs, const float *q_desc,
+                               const float *k_desc, int32_t topk, const int32_t *idx, Geo *geo, HeadShapes *hs,
+                               RasterView *rv) {
+  veda_status s = check_geom(g, dtype, geo, hs);
+  if (s != VEDA_OK) return s;
+  if (!q_raster || !k_raster || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
+  if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
+  if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
+  if (topk < 0 || topk > geo->nt) return VEDA_ERR_SHAPE;
+  if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
+  if (geo->nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
+  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
+  if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if ((s = check_raster(*geo, *hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if (geo->padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
+  const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
+  *rv = RasterView{rs_b * eb, rs_n * eb, rs_h * eb};
+  return VEDA_OK;
+}
+
+// Static scratch of the no-allocation scoring call: the MLP outputs y_q, y_k of one call
+// (2 * B * H * n_t * 64 floats; 32 MiB holds B * H * n_t <= 65536 tiles, e.g. 48 heads of
+// 1200 tiles).  Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the symbol: its device address on the current device
+// comes from hipGetSymbolAddress, once per device, and only that address is ever passed to
+// a kernel.
+constexpr size_t SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+veda_status scratch_device_ptr(void **out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return VEDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t se = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (se != hipSuccess) return hip_status(se);
+    if (p == nullptr) return VEDA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VEDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,26 +234,39 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
-  veda_status s = check_geom(g, dtype, &geo, &hs);
+  RasterView rv;
+  veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx, &geo, &hs,
+                                     &rv);
   if (s != VEDA_OK) return s;
-  if (!q_raster || !k_raster || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
-  if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
-  if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
-  if (topk < 0 || topk > geo.nt) return VEDA_ERR_SHAPE;
-  if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
-  if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
-  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
-  if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
-  if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
-  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
+  if (workspace != nullptr && !aligned16(workspace)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
-  const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
-  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs, &rv,
+                                 k_layout == VEDA_RASTER));
+}
+
+veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dtype, const void *q_raster,
+                                               const void *k_raster, veda_layout k_layout, int64_t rs_b,
+                                               int64_t rs_n, int64_t rs_h, const float *w1_q, const float *w2_q,
+                                               const float *w1_k, const float *w2_k, int32_t mlp_hidden,
+                                               int32_t mlp_out, float score_scale, float *scores, float *probs,
+                                               float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
+                                               hipStream_t stream) {
+  Geo geo;
+  HeadShapes hs;
+  RasterView rv;
+  veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx, &geo, &hs,
+                                     &rv);
+  if (s != VEDA_OK) return s;
+  if (score_workspace_bytes(geo, mlp_hidden, mlp_out) > SCRATCH_BYTES) return VEDA_ERR_SCRATCH;
+  void *ws = nullptr;
+  if ((s = scratch_device_ptr(&ws)) != VEDA_OK) return s;
+  // The MLP outputs are written whole before they are read: nothing needs clearing.
+  return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
+                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, ws, stream, &hs, &rv,
                                  k_layout == VEDA_RASTER));
 }
 
@@ -387,6 +459,7 @@ const char *veda_status_str(veda_status s) {
     case VEDA_ERR_WORKSPACE: return "workspace missing or too small";
     case VEDA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case VEDA_ERR_HIP: return "HIP launch failed";
+    case VEDA_ERR_SCRATCH: return "problem too large for the library's 32 MiB static scratch";
     default: return "unknown status";
   }
 }
