@@ -37,7 +37,7 @@
  * The raster layout is [B, N, H, d] with any element strides for b, n, h and d contiguous;
  * raster token n = (t*H + h)*W + w.
  *
- * Padded tilings (bf16, tiled calls only).  A head's shape (p_t, p_h, p_w) need not divide
+ * Padded tilings (bf16).  A head's shape (p_t, p_h, p_w) need not divide
  * the grid: the grid is then padded up to whole tiles on every axis for that head, giving
  * n_t(h) = ceil(t/p_t) * ceil(h/p_h) * ceil(w/p_w) tiles, some of them partial; a row of
  * the padded grid outside the real grid is a padding row and holds no token.  Reading of
@@ -50,8 +50,12 @@
  *  - Scores, top-k lists and maps have n_t columns per row; a head uses its first n_t(h)
  *    (top-k and maps never pick or fill the others: scores -inf, probabilities and map
  *    entries 0).  k must not exceed the smallest n_t(h).
- *  - The raster-direct calls, veda_distill_step and VEDA_F32 return VEDA_ERR_UNSUPPORTED
- *    for such a geometry; veda_oracle_tilemap needs an explicit q_tiles list.
+ *  - VEDA_F32 returns VEDA_ERR_UNSUPPORTED for such a geometry.  The raster attention and
+ *    tile-map calls read K tiled (k_layout VEDA_TILE_ROWS, else VEDA_ERR_UNSUPPORTED); the
+ *    raster scoring call reads K raster or tiled, and its k_tiled_out copy has the zero
+ *    rows too.  Raster outputs hold the real tokens only (padding rows have none).  Both
+ *    tile-map calls need an explicit q_tiles list.  veda_distill_step takes each head's
+ *    own n_t(h) key tiles (target columns past them are ignored and get no gradient).
  */
 #ifndef VEDA_H
 #define VEDA_H
@@ -200,17 +204,23 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
  * the same strides as Q) or VEDA_TILE_ROWS (tile-major [B, H, N, d], from
  * veda_tile_gather; K tiles are then contiguous 32 KB copies, which the attention and
  * tile-map kernels prefer).  V stays VEDA_TILE_COLS (v_layout, checked as in
- * veda_sparse_attn_fwd).  The output of
- * veda_sparse_attn_fwd_raster is raster (same strides) and its lse is [B, H, N] in raster
- * token order; the tile-map lse keeps its [B, H, n_sel * P] tile-row order.  Extra status:
- * VEDA_ERR_UNSUPPORTED if an in-tile token offset times the token stride reaches 2^31
- * bytes.  Other arguments, outputs and workspaces as in the tiled calls. */
+ * veda_sparse_attn_fwd).  The output of veda_sparse_attn_fwd_raster is raster (same
+ * strides) and its lse is [B, H, t*h*w] in raster token order; the tile-map lse keeps its
+ * [B, H, n_sel * P] tile-row order.  Extra status: VEDA_ERR_UNSUPPORTED if an in-tile
+ * token offset times the token stride reaches 2^31 bytes.  Other arguments, outputs and
+ * workspaces as in the tiled calls.
+ * veda_trippool_score_raster also takes k_tiled_out (nullable; only with k_layout
+ * VEDA_RASTER, else VEDA_ERR_SHAPE): [B, H, N, d] of `dtype`, which receives K's tile-major
+ * copy (exactly what veda_tile_gather writes with VEDA_TILE_ROWS), written as K is read for
+ * pooling, so that one pass over K both scores it and tiles it for the attention and
+ * tile-map calls (the paper's future work on kernel fusion). */
 veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
                                        float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                       void *k_tiled_out, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                         veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                         const void *v_cols, veda_layout v_layout, const int32_t *kv_idx,
@@ -237,7 +247,7 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
                                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               hipStream_t stream);
+                                               void *k_tiled_out, hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
  * gradients of the sampled Q tiles and of every K tile, per-row KL terms). */

@@ -99,9 +99,9 @@ def lib():
             "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
-                                                 vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+                                                 vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
             "veda_trippool_score_raster_noalloc": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32,
-                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp]),
+                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp, vp]),
             "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
                                                   vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
@@ -416,11 +416,16 @@ def _k_operand(geom, q, k, k_layout, *others):
     return _raster_strides(q, *others), _p(k, "k", True, dt, _tiled_numel(geom))
 
 
+def _k_tiled_out(geom, q, t):
+    return _p(t, "k_tiled_out", True, _elem_dtype(q), _tiled_numel(geom))
+
+
 def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125, scores=None,
                                probs=None, q_desc=None, k_desc=None, topk=0, idx=None, workspace=None,
-                               k_layout=RASTER, stream=None):
+                               k_layout=RASTER, k_tiled_out=None, stream=None):
     """veda_trippool_score on raster Q [B, N, H, d] (read through each head's tiling); K
-    raster too, or tile-major with k_layout=ROWS."""
+    raster too, or tile-major with k_layout=ROWS.  With a raster K, k_tiled_out (if given)
+    receives K's tile-major copy, written while K is pooled."""
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
     rs, kp = _k_operand(geom, q, k, k_layout)
@@ -428,8 +433,9 @@ def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, sco
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
     outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
     _call("veda_trippool_score_raster",
-        geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e, hidden, mout, float(score_scale),
-        *outs[:4], int(topk), outs[4], _p(workspace, "workspace"), _ws(workspace), _stream(stream))
+          geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e, hidden, mout, float(score_scale),
+          *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), _p(workspace, "workspace"),
+          _ws(workspace), _stream(stream))
 
 
 def veda_sparse_attn_fwd_raster(geom, q, k, v_cols, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
@@ -442,7 +448,7 @@ def veda_sparse_attn_fwd_raster(geom, q, k, v_cols, kv_idx, kk, softmax_scale, o
         geom.ref, _dtype_code(q), _raster(geom, q, "q", dt), kp, int(k_layout), *rs,
         _p(v_cols, "v_cols", True, dt, _tiled_numel(geom)), int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
         float(softmax_scale), _raster(geom, o, "o", dt),
-        _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tiled), _stream(stream))
+        _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tokens), _stream(stream))
 
 
 def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilemap, lse=None, workspace=None,
@@ -457,7 +463,7 @@ def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilema
 
 def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
                                        scores=None, probs=None, q_desc=None, k_desc=None, topk=0, idx=None,
-                                       k_layout=RASTER, stream=None):
+                                       k_layout=RASTER, k_tiled_out=None, stream=None):
     """veda_trippool_score_raster with no workspace: the library's static scratch holds the
     MLP outputs (B * H * n_t <= 65536 tiles; calls that overlap on one GPU race)."""
     w1_k = w1_q if w1_k is None else w1_k
@@ -467,4 +473,5 @@ def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=N
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
     outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
     _call("veda_trippool_score_raster_noalloc", geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e,
-          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _stream(stream))
+          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out),
+          _stream(stream))

@@ -15,7 +15,7 @@ static thread_local int g_last_hip_error = 0;
 namespace {
 
 constexpr int SCORE_MAX_NT = 1536;  // the score kernel holds a row of <= 1536 scores in registers
-constexpr int DISTILL_MAX_NT = 1280;
+constexpr int DISTILL_MAX_NT = 1536;  // the KL row kernel holds a row of <= 1536 logits in registers
 constexpr int TILEMAP_MAX_NT_F32 = 1280;  // the fp32 tile map keeps one row of maxima in LDS
 constexpr int TILEMAP_MAX_NT = 1536;
 
@@ -116,22 +116,23 @@ veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void 
                                veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h, const float *w1_q,
                                const float *w2_q, const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                int32_t mlp_out, const float *scores, const float *probs, const float *q_desc,
-                               const float *k_desc, int32_t topk, const int32_t *idx, Geo *geo, HeadShapes *hs,
-                               RasterView *rv) {
-  veda_status s = check_geom(g, dtype, geo, hs);
+                               const float *k_desc, int32_t topk, const int32_t *idx, const void *k_tiled_out,
+                               Geo *geo, HeadShapes *hs, RasterView *rv) {
+  int nt_min;
+  veda_status s = check_geom(g, dtype, geo, hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !w1_q || !w2_q || !w1_k || !w2_k) return VEDA_ERR_NULL;
   if (scores == nullptr && probs == nullptr && idx == nullptr) return VEDA_ERR_NULL;
   if ((topk > 0) != (idx != nullptr)) return idx ? VEDA_ERR_SHAPE : VEDA_ERR_NULL;
-  if (topk < 0 || topk > geo->nt) return VEDA_ERR_SHAPE;
+  if (topk < 0 || topk > nt_min) return VEDA_ERR_SHAPE;
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo->nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
-  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx};
+  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, k_tiled_out};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if (k_tiled_out != nullptr && k_layout != VEDA_RASTER) return VEDA_ERR_SHAPE;  // the copy is of a raster K
   if ((s = check_raster(*geo, *hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
-  if (geo->padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
   const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
   *rv = RasterView{rs_b * eb, rs_n * eb, rs_h * eb};
   return VEDA_OK;
@@ -231,20 +232,21 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
                                        float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                       void *k_tiled_out, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
-                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx, &geo, &hs,
-                                     &rv);
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
+                                     k_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (workspace != nullptr && !aligned16(workspace)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER));
+                                 k_layout == VEDA_RASTER, k_tiled_out));
 }
 
 veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dtype, const void *q_raster,
@@ -253,13 +255,13 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
                                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               hipStream_t stream) {
+                                               void *k_tiled_out, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
-                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx, &geo, &hs,
-                                     &rv);
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
+                                     k_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (score_workspace_bytes(geo, mlp_hidden, mlp_out) > SCRATCH_BYTES) return VEDA_ERR_SCRATCH;
   void *ws = nullptr;
@@ -267,7 +269,7 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
   // The MLP outputs are written whole before they are read: nothing needs clearing.
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, ws, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER));
+                                 k_layout == VEDA_RASTER, k_tiled_out));
 }
 
 veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k, int32_t *idx,
@@ -305,17 +307,18 @@ veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, co
                                         float softmax_scale, void *o_raster, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
-  veda_status s = check_geom(g, dtype, &geo, &hs);
+  int nt_min;
+  veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !v_cols || !kv_idx || !o_raster) return VEDA_ERR_NULL;
   if (v_layout != VEDA_TILE_COLS) return VEDA_ERR_UNSUPPORTED;
-  if (k < 1 || k > geo.nt) return VEDA_ERR_SHAPE;
+  if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
   const void *ptrs[] = {q_raster, k_raster, v_cols, kv_idx, o_raster, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
-  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
+  if (geo.padded && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_UNSUPPORTED;  // padded: K tiled
   return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
                                               rs_h, v_cols, kv_idx, k, softmax_scale, o_raster, lse, stream));
 }
@@ -369,14 +372,14 @@ veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, con
   veda_status s = check_geom(g, dtype, &geo, &hs);
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !tilemap) return VEDA_ERR_NULL;
-  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && n_sel != geo.nt)) return VEDA_ERR_SHAPE;
+  if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && (n_sel != geo.nt || geo.padded))) return VEDA_ERR_SHAPE;
   if (geo.nt > (dtype == VEDA_F32 ? TILEMAP_MAX_NT_F32 : TILEMAP_MAX_NT)) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_raster, k_raster, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
-  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // padded tilings: tiled operands only
+  if (geo.padded && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_UNSUPPORTED;  // padded: K tiled
   if (workspace == nullptr || workspace_bytes < tilemap_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
   const int64_t eb = dtype == VEDA_BF16 ? 2 : 4;
   const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
@@ -394,15 +397,14 @@ veda_status veda_distill_step(const veda_geom *g, veda_dtype dtype, const void *
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !w1 || !w2 || !q_tiles || !target || !loss || !dw1 || !dw2) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt) return VEDA_ERR_SHAPE;
-  if (geo.padded) return VEDA_ERR_UNSUPPORTED;  // the distillation step takes dividing shapes only
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo.nt > DISTILL_MAX_NT) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, w1, w2, q_tiles, target, loss, dw1, dw2, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < distill_workspace_bytes(geo, n_sel)) return VEDA_ERR_WORKSPACE;
-  return hip_status(launch_distill(geo, dtype, q_tiled, k_tiled, w1, w2, score_scale, q_tiles, n_sel, target, loss,
-                                   dw1, dw2, lr, workspace, stream));
+  return hip_status(launch_distill(geo, hs, dtype, q_tiled, k_tiled, w1, w2, score_scale, q_tiles, n_sel, target,
+                                   loss, dw1, dw2, lr, workspace, stream));
 }
 
 size_t veda_head_sq_error_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t heads) {

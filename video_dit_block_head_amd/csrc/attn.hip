@@ -53,7 +53,9 @@ __device__ __forceinline__ float half_sum(float v) {
 // RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
 // the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
 // order; RK: the same for K.  Otherwise tile-major.  V is always channel-major tiled.
-// PAD: padded tiling (tiled operands only): per-head tile counts and partial key tiles.
+// PAD: padded tiling: per-head tile counts and partial key tiles (K tiled); with RQ the
+// padding query rows of a partial query tile are neither read (Q taken as zero, as the
+// gather stores it) nor written.
 template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
@@ -86,13 +88,22 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   // Q fragments first, consumed by an empty asm so that they have arrived before the first
   // copy is issued (otherwise the compiler sinks the loads and waits for them in the loop).
   const int qrow = i * 128 + 32 * w + lr;
-  // this lane's query row: tiled row qrow, or its raster token
+  // this lane's query row: tiled row qrow, or its raster token (a real token unless the row
+  // is padding of a partial tile of a padded tiling)
   const int64_t qtok = RQ ? tile_origin(i, pt, ph, pw, g.Hs, g.Ws) + tile_intra(32 * w + lr, ph, pw, g.Hs, g.Ws) : 0;
+  const bool qreal = !(RQ && PAD) || row_real(i, 32 * w + lr, pt, ph, pw, g.T, g.Hs, g.Ws);
   const __bf16 *qp = RQ ? reinterpret_cast<const __bf16 *>(reinterpret_cast<const char *>(q) + rhead + qtok * rv.sn)
                         : q + head + (int64_t)qrow * 128;
   bf16x8_t qf[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
+  for (int s = 0; s < 8; ++s) {
+    if (qreal) {
+      qf[s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)0.0f;
+    }
+  }
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
   uint32_t off[8], koff[8];
@@ -239,19 +250,24 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   const float inv = 1.0f / l_tot;
   __bf16 *orow = RQ ? reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(o) + rhead + qtok * rv.sn)
                     : o + head + (int64_t)qrow * 128;
+  if (qreal) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * db + 8 * r4 + 4 * hi;
-      bf16x4_t v;
-      v[0] = (__bf16)(acc_o[db][4 * r4 + 0] * inv);
-      v[1] = (__bf16)(acc_o[db][4 * r4 + 1] * inv);
-      v[2] = (__bf16)(acc_o[db][4 * r4 + 2] * inv);
-      v[3] = (__bf16)(acc_o[db][4 * r4 + 3] * inv);
-      *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
-    }
-  if (lse != nullptr && hi == 0) lse[bh * g.N + (RQ ? qtok : (int64_t)qrow)] = (m_run + log2f(l_tot)) * LN2;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * db + 8 * r4 + 4 * hi;
+        bf16x4_t v;
+        v[0] = (__bf16)(acc_o[db][4 * r4 + 0] * inv);
+        v[1] = (__bf16)(acc_o[db][4 * r4 + 1] * inv);
+        v[2] = (__bf16)(acc_o[db][4 * r4 + 2] * inv);
+        v[3] = (__bf16)(acc_o[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<bf16x4_t *>(orow + d0) = v;
+      }
+  }
+  // LSE: [B, H, tiled rows], or [B, H, real tokens] in raster order
+  const int64_t lse_stride = RQ ? (int64_t)g.T * g.Hs * g.Ws : (int64_t)g.N;
+  if (lse != nullptr && hi == 0 && qreal)
+    lse[bh * lse_stride + (RQ ? qtok : (int64_t)qrow)] = (m_run + log2f(l_tot)) * LN2;
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row, keys one at a time from LDS.
@@ -317,8 +333,8 @@ static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &
                           const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
                           float *lse, hipStream_t st) {
   if (dt == VEDA_BF16) {
-    if (!RQ && !RK && g.padded)
-      attn_bf16_kernel<false, false, true><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+    if (!RK && g.padded)  // padded tilings read K tiled (the C ABI refuses a raster K)
+      attn_bf16_kernel<RQ, false, true><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
           rv);
     else

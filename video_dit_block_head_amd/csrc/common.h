@@ -90,9 +90,11 @@ __device__ __forceinline__ void tile_row_words(const TileBox &bx, int ph, int pw
 }
 
 // The same token as origin(j) + intra(o): the first is uniform over a tile, the second is
-// the same for row o of every tile of a head.  Used only with shapes that divide the grid.
+// the same for row o of every tile of a head.  Tiles are numbered over the grid padded up
+// to whole tiles; on a padded tiling origin + intra names a real token only for the rows
+// inside the tile's box (in_box), and the others must not be read or written.
 __device__ __forceinline__ int64_t tile_origin(int j, int pt, int ph, int pw, int Hs, int Ws) {
-  const int ntw = Ws / pw, nth = Hs / ph;
+  const int ntw = (Ws + pw - 1) / pw, nth = (Hs + ph - 1) / ph;
   const int jw = j % ntw, jh = (j / ntw) % nth, jt = j / (ntw * nth);
   return ((int64_t)(jt * pt) * Hs + jh * ph) * Ws + jw * pw;
 }
@@ -125,6 +127,13 @@ __device__ __forceinline__ uint4 load_stream16(const void *p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16-byte store marked non-temporal: a write-once copy does not displace reused data in L2.
+__device__ __forceinline__ void store_stream16(void *p, const uint4 &v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
 }
 
 __device__ __forceinline__ uint32_t float_key(float x) {

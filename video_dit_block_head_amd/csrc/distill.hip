@@ -69,13 +69,17 @@ template <int MAXM>
 __global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ y, int n_sel,
                                                       const float *__restrict__ target, float scale,
                                                       float inv_rows, float *__restrict__ ds, float *__restrict__ dyq,
-                                                      float *__restrict__ loss_rows, Geo g) {
+                                                      float *__restrict__ loss_rows, Geo g, HeadShapes hs) {
   __shared__ float dsl[4][64 * MAXM];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;  // (b*H + h)*n_sel + a
   if (row >= (int64_t)g.B * g.H * n_sel) return;      // whole wave; no barrier follows
   const int64_t bh = row / n_sel;
   const int nt = g.nt;
+  // this head's key tiles: the columns past them (padded tilings) are not in the softmax,
+  // carry no target and get no gradient
+  const int hh = (int)(bh % g.H);
+  const int nth = g.padded ? head_tiles(hs.s[hh][0], hs.s[hh][1], hs.s[hh][2], g.T, g.Hs, g.Ws) : nt;
   const int64_t a = row - bh * n_sel;       // list position: the Q rows are the listed tiles
   const float *yq = y + (bh * nt + a) * DS_OUT;
   const float *yk = y + (((int64_t)g.B * g.H + bh) * nt) * DS_OUT;
@@ -87,7 +91,7 @@ __global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ 
     const int j = 64 * u + lane;
     s[u] = -INFINITY;
     mt[u] = 0.f;
-    if (j < nt) {
+    if (j < nth) {
       const float4 *kr = reinterpret_cast<const float4 *>(yk + (int64_t)j * DS_OUT);
       const float4 *qr = reinterpret_cast<const float4 *>(yq);
       float acc = 0.f;
@@ -110,19 +114,22 @@ __global__ void __launch_bounds__(256) kl_grad_kernel(const float *__restrict__ 
   float se = 0.f;
 #pragma unroll
   for (int u = 0; u < MAXM; ++u)
-    if (64 * u + lane < nt) se += expf(s[u] - mx);
+    if (64 * u + lane < nth) se += expf(s[u] - mx);
   se = wave_sum(se);
   const float lse = mx + logf(se), inv_m = 1.0f / msum;
   float kl = 0.f;
 #pragma unroll
   for (int u = 0; u < MAXM; ++u) {
     const int j = 64 * u + lane;
-    if (j < nt) {
+    if (j < nth) {
       const float p = mt[u] * inv_m, logq = s[u] - lse;
       if (p > 0.f) kl += p * (logf(p) - logq);
       const float d = (expf(logq) - p) * inv_rows;
       ds[row * nt + j] = d;
       dsl[wv][j] = d;
+    } else if (j < nt) {
+      ds[row * nt + j] = 0.f;
+      dsl[wv][j] = 0.f;
     }
   }
   kl = wave_sum(kl);
@@ -287,15 +294,15 @@ __global__ void __launch_bounds__(256) sgd_kernel(float *__restrict__ w, const f
 
 template <int MAXM>
 static void launch_kl(const Geo &g, const float *y, int n_sel, const float *target,
-                      float scale, float inv_rows, const DistillWs &w, hipStream_t st) {
+                      float scale, float inv_rows, const DistillWs &w, const HeadShapes &hs, hipStream_t st) {
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
   kl_grad_kernel<MAXM><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(y, n_sel, target, scale, inv_rows, w.ds,
-                                                                       w.dy, w.loss, g);
+                                                                       w.dy, w.loss, g, hs);
 }
 
-hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void *k, float *w1, float *w2,
-                          float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
-                          float *dw1, float *dw2, float lr, void *ws, hipStream_t st) {
+hipError_t launch_distill(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k, float *w1,
+                          float *w2, float score_scale, const int32_t *q_tiles, int n_sel, const float *target,
+                          float *loss, float *dw1, float *dw2, float lr, void *ws, hipStream_t st) {
   size_t off[7];
   ws_parts(g, n_sel, off);
   char *base = static_cast<char *>(ws);
@@ -306,19 +313,23 @@ hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void
   // forward: descriptors and MLP outputs of every Q and K tile (shared weights)
   // Q rows: the listed tiles only (an unlisted Q tile gets no gradient); the pre-activation
   // hidden layer goes to h1, which the backward rows kernel turns into GELU
-  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st, nullptr,
+  // (on a padded tiling the descriptors of the tiles past a head's own count, and so their
+  // MLP outputs and gradients, are zero)
+  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1, w2, w1, w2, w.y, w.desc, w.desc + desc_half, st, &hs,
                                         nullptr, false, w.h1, q_tiles, n_sel);
   if (pe != hipSuccess) return pe;
   const int64_t rows = (int64_t)g.B * g.H * n_sel;
   const float inv_rows = 1.0f / (float)rows;
   if (g.nt <= 64)
-    launch_kl<1>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<1>(g, w.y, n_sel, target, score_scale, inv_rows, w, hs, st);
   else if (g.nt <= 256)
-    launch_kl<4>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<4>(g, w.y, n_sel, target, score_scale, inv_rows, w, hs, st);
   else if (g.nt <= 640)
-    launch_kl<10>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
-  else
-    launch_kl<20>(g, w.y, n_sel, target, score_scale, inv_rows, w, st);
+    launch_kl<10>(g, w.y, n_sel, target, score_scale, inv_rows, w, hs, st);
+  else if (g.nt <= 1280)
+    launch_kl<20>(g, w.y, n_sel, target, score_scale, inv_rows, w, hs, st);
+  else  // the widest padded heads (e.g. (16, 2, 4) on T = 40: 1440 tiles)
+    launch_kl<24>(g, w.y, n_sel, target, score_scale, inv_rows, w, hs, st);
   const dim3 gi(g.nt, g.B * g.H);
   dyk_kernel<<<gi, 64, 0, st>>>(n_sel, w.ds, w.y, score_scale, w.dy, g);
   const int ngrp = (g.nt + 31) / 32;

@@ -9,13 +9,14 @@ hipError_t launch_gather(const Geo &g, const HeadShapes &hs, veda_dtype dt, void
                          int64_t rs_n, int64_t rs_h, void *tiled, veda_layout layout, int inverse, hipStream_t st);
 
 // Scoring: pool -> MLP -> scores / softmax / top-k.  ws layout: see score.hip.  With rv
-// (and hs) set, Q is a raster tensor read through each head's tiling, and K too if k_raster.
+// (and hs) set, Q is a raster tensor read through each head's tiling, and K too if k_raster;
+// k_tiled_out (raster K only) receives K's tile-major copy, written as K is pooled.
 size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out);
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st, const HeadShapes *hs = nullptr, const RasterView *rv = nullptr,
-                        bool k_raster = false);
+                        bool k_raster = false, void *k_tiled_out = nullptr);
 
 // TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL;
 // the pre-activation hidden layer z [Q|K][B][H][n_t][256] if non-NULL.  With qlist
@@ -25,7 +26,7 @@ hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const voi
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs = nullptr,
                            const RasterView *rv = nullptr, bool k_raster = false, float *z = nullptr,
-                           const int32_t *qlist = nullptr, int nlist = 0);
+                           const int32_t *qlist = nullptr, int nlist = 0, void *k_tiled_out = nullptr);
 
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);
@@ -48,9 +49,9 @@ hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void
 
 // Distillation step (see distill.hip).
 size_t distill_workspace_bytes(const Geo &g, int n_sel);
-hipError_t launch_distill(const Geo &g, veda_dtype dt, const void *q, const void *k, float *w1, float *w2,
-                          float score_scale, const int32_t *q_tiles, int n_sel, const float *target, float *loss,
-                          float *dw1, float *dw2, float lr, void *ws, hipStream_t st);
+hipError_t launch_distill(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k, float *w1,
+                          float *w2, float score_scale, const int32_t *q_tiles, int n_sel, const float *target,
+                          float *loss, float *dw1, float *dw2, float lr, void *ws, hipStream_t st);
 
 int head_sq_error_chunks(int n_tokens);  // token chunks per head (one partial pair each)
 hipError_t launch_head_sq_error(int batch, int n_tokens, int heads, int head_dim, veda_dtype dt, const void *a,

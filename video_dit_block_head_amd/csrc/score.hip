@@ -10,7 +10,8 @@
 //                    (v_mfma_f32_16x16x4f32, 16 outputs per wave).  Three workgroups per
 //                    CU, so other workgroups' streaming overlaps one's MFMA work.  For the
 //                    distillation step it can take a list of Q tiles and also keep the
-//                    pre-activation hidden layer.
+//                    pre-activation hidden layer.  Reading a raster K, it can also write
+//                    K's tile-major copy as it streams it (the K gather fused into pooling).
 //  score_topk_kernel 16 query-tile rows per workgroup: S = y_q y_k^T on fp32 MFMA
 //                    (v_mfma_f32_16x16x4f32) into an LDS row block, then one wave per row
 //                    for softmax and top-k (ballot/popcount; deterministic); 4, 8 or 16
@@ -50,13 +51,14 @@ static constexpr int PM_HST = 260;    // hidden block row stride (floats)
 
 // RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through each
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
-// PAD: padded tiling (tiled operands only): per-head tile counts, partial tiles.
+// PAD: padded tiling: per-head tile counts, partial tiles (their real rows only).
 template <int EB, bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
                 float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, float *__restrict__ zout,
-                const int32_t *__restrict__ qlist, int nlist, Geo g, HeadShapes hs, RasterView rv) {
+                const int32_t *__restrict__ qlist, int nlist, Geo g, HeadShapes hs, RasterView rv,
+                uint8_t *__restrict__ kout) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
@@ -118,12 +120,31 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
         mn[e] = fminf(mn[e], x[e]);
       }
     };
-    if (j < nth && !(RQ || RK) && PAD && box_rows(bx) < P) {
-      // a partial tile of a padded tiling (tiled operands only): its real rows, one at a time
-      const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
+    // K's tile-major copy, if asked for (raster K only): rows as loaded; zero rows for the
+    // padding rows of a partial tile and for the tiles past this head's own count
+    uint8_t *kdst = (RK && which && kout != nullptr)
+                        ? kout + ((int64_t)b * g.H + h) * (int64_t)g.N * 256 + (int64_t)j * P * 256 + c * 16
+                        : nullptr;
+    if (j < nth && PAD && box_rows(bx) < P) {
+      // a partial tile of a padded tiling: its real rows, one at a time (raster rows at
+      // origin + intra, which names a real token only inside the tile's box)
+      const uint8_t *src = rast ? src0 + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn + c * 16
+                                : src0 + (int64_t)j * P * 256 + c * 16;
+      const int64_t rstride = rast ? rv.sn : 256;
 #pragma unroll 1
-      for (int o = rg; o < P; o += 4)
-        if (in_box(o, ph, pw, bx)) accum(load_stream16(src + o * 256));
+      for (int o = rg; o < P; o += 4) {
+        if (in_box(o, ph, pw, bx)) {
+          const int64_t ro = rast ? (int64_t)tile_intra(o, ph, pw, g.Hs, g.Ws) * rstride : (int64_t)o * 256;
+          const uint4 v = load_stream16(src + ro);
+          accum(v);
+          if (kdst != nullptr) store_stream16(kdst + o * 256, v);
+        } else if (kdst != nullptr) {
+          store_stream16(kdst + o * 256, make_uint4(0u, 0u, 0u, 0u));
+        }
+      }
+    } else if (PAD && j >= nth && j < g.nt) {
+      if (kdst != nullptr)
+        for (int o = rg; o < P; o += 4) store_stream16(kdst + o * 256, make_uint4(0u, 0u, 0u, 0u));
     } else if (j < nth) {
       // raster rows: 32-bit offsets from the tile's origin, half a tile (16 loads) at a time
       constexpr int NL = (RQ || RK) ? P / 8 : P / 4;
@@ -135,6 +156,10 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 #pragma unroll
           for (int i = 0; i < NL; ++i)
             v[i] = load_stream16(src + (uint32_t)(tile_intra(rg + 4 * (NL * part + i), ph, pw, g.Hs, g.Ws) * (int)rv.sn));
+          if (kdst != nullptr) {  // uniform: K's tile-major copy, rows as loaded
+#pragma unroll
+            for (int i = 0; i < NL; ++i) store_stream16(kdst + (rg + 4 * (NL * part + i)) * 256, v[i]);
+          }
         } else {
           const uint8_t *src = src0 + (int64_t)j * P * 256 + c * 16;
 #pragma unroll
@@ -410,38 +435,39 @@ template <int EB, bool RQ, bool RK>
 static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
                               float *q_desc, float *k_desc, float *z, const int32_t *qlist, int nlist,
-                              hipStream_t st) {
+                              uint8_t *kout, hipStream_t st) {
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
-  if (!RQ && !RK && g.padded)
-    pool_mlp_kernel<EB, false, false, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k,
-                                                                w2k, y, q_desc, k_desc, z, qlist, nlist, g, hs, rv);
+  if (g.padded)
+    pool_mlp_kernel<EB, RQ, RK, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
+                                                          y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout);
   else
     pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
-                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv);
+                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
-                           bool k_raster, float *z, const int32_t *qlist, int nlist) {
+                           bool k_raster, float *z, const int32_t *qlist, int nlist, void *k_tiled_out) {
+  uint8_t *kout = static_cast<uint8_t *>(k_tiled_out);
   const HeadShapes hs0 = hs != nullptr ? *hs : HeadShapes{};  // tiled operands: shapes matter only when padded
   const RasterView rv0{0, 0, 0};
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
     if (bf)
-      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
     else
-      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
   } else if (k_raster) {
     if (bf)
-      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
     else
-      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
   } else {
     if (bf)
-      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
     else
-      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, st);
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
   }
   return hipGetLastError();
 }
@@ -449,12 +475,14 @@ hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const voi
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
-                        void *ws, hipStream_t st, const HeadShapes *hs, const RasterView *rv, bool k_raster) {
+                        void *ws, hipStream_t st, const HeadShapes *hs, const RasterView *rv, bool k_raster,
+                        void *k_tiled_out) {
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
   const HeadShapes hsv = hs != nullptr ? *hs : HeadShapes{};
-  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster);
+  const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster,
+                                        nullptr, nullptr, 0, k_tiled_out);
   if (pe != hipSuccess) return pe;
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, hsv, st);

@@ -40,7 +40,8 @@ static constexpr int TM_QT = 2;
 
 // RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through the
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
-// PAD: padded tiling (tiled operands only): per-head tile counts, partial tiles.
+// PAD: padded tiling: per-head tile counts, partial tiles (K tiled); with RQ the padding
+// query rows of a partial tile are not read (Q taken as zero, as the gather stores it).
 template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
@@ -79,13 +80,22 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = 64 * (w & 1) + 32 * qb + lr;
+    // origin + intra names a real token unless the row is padding of a partial tile
+    const bool real = !(RQ && PAD) || row_real(i, r, pt, ph, pw, g.T, g.Hs, g.Ws);
     const __bf16 *qp =
         RQ ? reinterpret_cast<const __bf16 *>(reinterpret_cast<const char *>(q) + rhead +
                                                   (tile_origin(i, pt, ph, pw, g.Hs, g.Ws) +
                                                    tile_intra(r, ph, pw, g.Hs, g.Ws)) * rv.sn)
                : qh + ((int64_t)i * 128 + r) * 128;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
+    for (int s = 0; s < 8; ++s) {
+      if (real) {
+        qf[qb][s] = *reinterpret_cast<const bf16x8_t *>(qp + 16 * s + 8 * hi);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qb][s][e] = (__bf16)0.0f;
+      }
+    }
   }
   asm volatile("" ::"v"(qf[0][0]), "v"(qf[0][1]), "v"(qf[0][2]), "v"(qf[0][3]), "v"(qf[0][4]), "v"(qf[0][5]),
                "v"(qf[0][6]), "v"(qf[0][7]));
@@ -323,9 +333,9 @@ static void launch_tilemap_t(const Geo &g, const HeadShapes &hs, const RasterVie
                                               tm_align256((size_t)g.B * g.H * n_sel * (size_t)g.nt * g.P * sizeof(float)));
     const dim3 grid(groups * splits), pgrid(g.H * g.B, n_sel);
     const __bf16 *qq = (const __bf16 *)q, *kk = (const __bf16 *)k;
-    if (!RQ && !RK && g.padded) {
-      tilemap_bf16_kernel<false, false, true><<<grid, 256, 0, st>>>(qq, kk, scale * TM_LOG2E, q_tiles, n_sel, splits,
-                                                                    rowmax, part, g, hs, rv);
+    if (!RK && g.padded) {  // padded tilings read K tiled (the C ABI refuses a raster K)
+      tilemap_bf16_kernel<RQ, false, true><<<grid, 256, 0, st>>>(qq, kk, scale * TM_LOG2E, q_tiles, n_sel, splits,
+                                                                 rowmax, part, g, hs, rv);
       tilemap_pool_kernel<true><<<pgrid, 256, 0, st>>>(rowmax, part, splits, q_tiles, n_sel, tilemap, lse, g, hs);
     } else {
       tilemap_bf16_kernel<RQ, RK, false><<<grid, 256, 0, st>>>(qq, kk, scale * TM_LOG2E, q_tiles, n_sel, splits,

@@ -105,12 +105,14 @@ class SparseAttention:
     def _k(self, k):
         return (self.k_t, ROWS) if k is None else (k, RASTER)
 
-    def score_raster(self, q, topk, k=None, scores=None, probs=None, q_desc=None, k_desc=None):
+    def score_raster(self, q, topk, k=None, scores=None, probs=None, q_desc=None, k_desc=None, tile_k=False):
+        """Scoring on raster Q; K raster (k given) or its tiled copy.  tile_k (raster K only):
+        also write K's tiled copy while pooling it, in place of gather_kv's K gather."""
         idx = self.idx_buffer(topk) if topk > 0 else None
         kt, lay = self._k(k)
         veda_trippool_score_raster(self.geom, q, kt, self.w1, self.w2, self.w1_k, self.w2_k, self.score_scale,
                                    scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc, topk=topk, idx=idx,
-                                   workspace=self.ws, k_layout=lay)
+                                   workspace=self.ws, k_layout=lay, k_tiled_out=self.k_t if tile_k else None)
         return idx
 
     def attend_raster(self, q, idx, out, lse=None, k=None):
@@ -129,9 +131,10 @@ class SparseAttention:
         return out
 
     def forward_raster(self, q, k, v, topk, out):
-        """Same result as forward(), without the tiled copies of Q and O."""
-        self.gather_kv(k, v)
-        idx = self.score_raster(q, topk)
+        """Same result as forward(), without the tiled copies of Q and O; K is tiled by the
+        scoring pass as it reads it, V by the gather."""
+        self.gather_v(v)
+        idx = self.score_raster(q, topk, k=k, tile_k=True)
         return self.attend_raster(q, idx, out)
 
     def forward(self, q, k, v, topk, out):
