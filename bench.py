@@ -110,6 +110,130 @@ def cpu_baseline(cfg, wl, kk, n_sel, budget_s=15.0):
     }
 
 
+def timed(fn, reps):
+    """Mean milliseconds of `reps` calls of fn() between HIP events on the current stream
+    (after one untimed call)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def long_sweep(reps=5, dense_reps=2):
+    """The 720P-10 s-shaped workload (B 1, 48 heads, latent 40x48x80 so N = 153 600, 1200
+    tiles per head) on the default path: the scoring pass (TripPool -> MLP -> scores ->
+    top-k) and the tile-skipping attention at 80, 90 and 95 % of key tiles skipped, and
+    this library's own dense path (every tile kept) for the speedups."""
+    import numpy as np
+    import torch
+    import video_dit_block_head_amd as V
+    from video_dit_block_head_amd.pipeline import SparseAttention, dense_index
+    from workloads import get, make
+    cfg = get("long")
+    say(f"[bench] long workload: generating (N={cfg.n_tokens}, H={cfg.heads})")
+    wl = make(cfg)
+    B, H, N, d, P, nt = cfg.batch, cfg.heads, cfg.n_tokens, cfg.head_dim, cfg.tile, cfg.n_tiles
+    geom = V.Geom(B, H, d, cfg.grid, P, wl.shapes)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    del wl
+    sa = SparseAttention(geom, torch.bfloat16, torch.from_numpy(make_weights(cfg)[0]),
+                         torch.from_numpy(make_weights(cfg)[1]), score_scale=cfg.score_scale)
+    out = torch.empty_like(q)
+    sa.gather_kv(k, v)
+    rows = {}
+    say("[bench] long workload: sparsity sweep")
+    for kk in sorted(cfg.topk[:-1], reverse=True):          # 240, 120, 60 of 1200
+        score_ms = timed(lambda: sa.score_raster(q, kk), reps)
+        idx = sa.idx_buffer(kk)
+        attn_ms = timed(lambda: sa.attend_raster(q, idx, out), reps)
+        fl = cfg.kept_flops(kk)
+        sbytes = 2 * B * H * N * d * 2 + B * H * nt * kk * 4
+        rows[f"k{kk}"] = {"skipped_pct": round(100 * (1 - kk / nt), 1), "attn_ms": round(attn_ms, 3),
+                          "attn_tflops": round(fl / (attn_ms * 1e-3) / 1e12, 1),
+                          "attn_frac_bf16_peak": round(fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "scoring_ms": round(score_ms, 4),
+                          "scoring_frac_hbm_peak": round(sbytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    say("[bench] long workload: dense path (k = n_t)")
+    didx = dense_index(geom)
+    dense_ms = timed(lambda: sa.attend_raster(q, didx, out), dense_reps)
+    for r in rows.values():
+        r["speedup_vs_dense"] = round(dense_ms / r["attn_ms"], 2)
+    res = {"workload": f"long: B={B} H={H} d={d} latent {'x'.join(map(str, cfg.grid))} (N={N}), tile {P}, "
+                       f"{nt} tiles per head",
+           "sweep": rows,
+           "dense": {"ms": round(dense_ms, 2), "tflops": round(cfg.kept_flops(nt) / (dense_ms * 1e-3) / 1e12, 1)}}
+    del sa, q, k, v, out, didx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def make_weights(cfg):
+    """The workload's estimator weights (the generator's first draws after the axis scales
+    and sinks), without generating Q, K and V again."""
+    from workloads import make
+    wl = make(cfg, heads=[])
+    return wl.w1, wl.w2
+
+
+def distill_recall(sa, q, k, v, qtl, n_sel, cfg, steps=60, lr=0.1, seed_offset=4000):
+    """The estimator before and after `steps` plain SGD steps of the distillation call on the
+    sampled query tiles (training rows), on those rows and on as many held-out query tiles
+    of every head: tile recall of the kept list against the oracle mask (the k largest
+    entries of each max-pooled map row), and the share of each normalised map row (the
+    distillation target) that falls outside the kept tiles."""
+    import numpy as np
+    import torch
+    import video_dit_block_head_amd as V
+    B, H, nt, kk = cfg.batch, cfg.heads, cfg.n_tiles, cfg.topk[0]
+    rng = np.random.default_rng(cfg.seed + seed_offset)
+    held = []
+    for h in range(H):
+        rest = np.setdiff1d(np.arange(nt), qtl[0, h].cpu().numpy())
+        held.append(np.sort(rng.choice(rest, n_sel, replace=False)))
+    htl = torch.from_numpy(np.stack(held).astype(np.int32)[None].repeat(B, 0)).cuda()
+    sa.gather(q, k, v)
+    maps = {}
+    for tag, tl in (("train", qtl), ("held_out", htl)):
+        m = torch.empty((B, H, n_sel, nt), dtype=torch.float32, device="cuda")
+        sa.tilemap(tl, n_sel, m)
+        o = torch.empty((B, H, n_sel, kk), dtype=torch.int32, device="cuda")
+        V.veda_topk_mask(m, kk, o)
+        maps[tag] = (tl, m, o)
+
+    def measure(tag):
+        tl, m, o = maps[tag]
+        est = sa.score(kk).long()
+        est = torch.gather(est, 2, tl.long()[..., None].expand(B, H, n_sel, kk)).reshape(-1, kk)
+        hit = torch.zeros((est.shape[0], nt), dtype=torch.float32, device="cuda").scatter_(1, est, 1.0)
+        rec = float(hit.gather(1, o.reshape(-1, kk).long()).sum()) / (est.shape[0] * kk)
+        p = m.reshape(-1, nt) / m.reshape(-1, nt).sum(dim=1, keepdim=True)
+        missed = float((p * (1.0 - hit)).sum(dim=1).mean())
+        return {"tile_recall": round(rec, 4), "target_mass_outside_kept": round(missed, 5)}
+
+    w1, w2 = sa.w1.clone(), sa.w2.clone()
+    before = {t: measure(t) for t in maps}
+    losses = []
+    for _ in range(steps):
+        loss, _, _ = sa.distill_step(qtl, maps["train"][1], lr=lr)
+        losses.append(loss)
+    after = {t: measure(t) for t in maps}
+    sa.w1.copy_(w1)
+    sa.w2.copy_(w2)
+    return {"sgd_steps": steps, "lr": lr, "loss_first": round(float(losses[0].item()), 4),
+            "loss_last": round(float(losses[-1].item()), 4), "before": before, "after": after,
+            "chance_recall": round(kk / nt, 4),
+            "note": "train: the sampled query tiles the steps fit (their max-pooled maps); held_out: as many other "
+                    "query tiles per head, not trained on; the KL fit moves target mass into the kept tiles, "
+                    "which is not the same as ranking the oracle's top k"}
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +248,8 @@ def main():
                          "gathered); tiled: explicit gather of Q, K, V and scatter of O")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the distillation step and the per-head error kernel")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long (N = 153 600) workload's sparsity sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -184,13 +310,13 @@ def main():
             sa.tilemap(qtl, n_sel, tmap)
             ev[5].record()
     else:
-        stages = ["gather_kv", "score_topk", "sparse_attn", "tilemap"]
+        stages = ["gather_v", "score_topk_tile_k", "sparse_attn", "tilemap"]
 
         def step(ev):
             ev[0].record()
-            sa.gather_kv(k, v)
+            sa.gather_v(v)
             ev[1].record()
-            idx = sa.score_raster(q, kk)
+            idx = sa.score_raster(q, kk, k=k, tile_k=True)   # also writes K's tiled copy
             ev[2].record()
             sa.attend_raster(q, idx, out)
             ev[3].record()
@@ -223,7 +349,19 @@ def main():
     kept = cfg.kept_flops(kk)
     attn_tflops = kept / (attn_ms * 1e-3) / 1e12
     score_bytes = 2 * B * H * N * d * 2 + B * H * nt * kk * 4
-    score_ms = float(np.mean(per_stage["score_topk"]))
+    if args.path == "tiled":
+        score_ms = float(np.mean(per_stage["score_topk"]))
+        fused = None
+    else:
+        # the step's scoring stage also writes K's tiled copy (B H N d bf16 more); the scoring
+        # pass itself (Q and K read, the lists written) is timed alone below
+        fused_ms = float(np.mean(per_stage["score_topk_tile_k"]))
+        fused_bytes = score_bytes + B * H * N * d * 2
+        fused = {"ms": round(fused_ms, 4), "bytes": fused_bytes,
+                 "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                 "note": "the step's scoring stage: raster Q and K read once, K's tile-major copy written, "
+                         "lists written"}
+        score_ms = timed(lambda: sa.score_raster(q, kk), 20)
     say(f"[bench] step {ms_step:.2f} ms; stages (median ms) {json.dumps({s: round(x, 3) for s, x in med.items()})}")
 
     # tile recall of the last step: the estimator's kept list against the oracle mask (the k
@@ -303,7 +441,8 @@ def main():
         herr_ms = e0.elapsed_time(e1) / reps
         herr_bytes = 2 * B * N * H * d * 2
         # Padded tilings: the same workload with its full shape cycle, where (8,4,4) does not divide
-        # T = 20, on the padded tiled path (gather Q K V, score, attend, scatter, tile map)
+        # T = 20, on the default path (gather V; score with K tiled on the way; attention and
+        # tile map with Q and O raster)
         pcfg = padded_variant(cfg)
         pshapes = pcfg.head_shapes()
         pgeom = V.Geom(B, H, d, cfg.grid, P, pshapes)
@@ -318,12 +457,11 @@ def main():
             pmap = torch.empty((B, H, n_sel, pgeom.n_tiles), dtype=torch.float32, device="cuda")
             pout = torch.empty_like(q)
 
-            def pstep():
-                psa.gather(q, k, v)
-                pidx = psa.score(kk)
-                psa.attend(pidx)
-                psa.scatter(pout)
-                psa.tilemap(pqt, n_sel, pmap)
+            def pstep():   # the default path: V gathered, K tiled by the scoring pass, Q and O raster
+                psa.gather_v(v)
+                pidx = psa.score_raster(q, kk, k=k, tile_k=True)
+                psa.attend_raster(q, pidx, pout)
+                psa.tilemap_raster(q, pqt, n_sel, pmap)
                 return pidx
 
             pidx = pstep()
@@ -336,7 +474,7 @@ def main():
             pstep_ms = e0.elapsed_time(e1) / reps
             e0.record()
             for _ in range(reps):
-                psa.attend(pidx)
+                psa.attend_raster(q, pidx, pout)
             e1.record()
             torch.cuda.synchronize()
             pattn_ms = e0.elapsed_time(e1) / reps
@@ -347,7 +485,10 @@ def main():
                        "padded_step_ms": round(pstep_ms, 3), "padded_attn_ms": round(pattn_ms, 3),
                        "padded_attn_tflops": round(pflops / (pattn_ms * 1e-3) / 1e12, 1)}
             del psa, pmap, pout
+        say("[bench] distillation: tile recall before and after SGD steps")
+        drec = distill_recall(sa, q, k, v, qtl, n_sel, cfg)
         nxt = {"distill_step_ms": round(distill_ms, 4),
+               "distill_recall": drec,
                # the step reads every K tile and the sampled Q tiles once
                "distill_step_qk_read_gbps": round(B * H * (nt + n_sel) * P * d * 2 / (distill_ms * 1e-3) / 1e9, 1),
                "distill_sampled_query_tiles_per_head": n_sel,
@@ -367,6 +508,13 @@ def main():
         torch.cuda.synchronize()
         say("[bench] copy calibration: 3 x 1 GiB device copies")
         del src, dst
+
+    long_row = None
+    if not args.no_long:
+        del sa
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        long_row = long_sweep()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -397,6 +545,7 @@ def main():
         "scoring_ms": round(score_ms, 4),
         "scoring_gbps": round(score_bytes / (score_ms * 1e-3) / 1e9, 1),
         "scoring_frac_hbm_peak": round(score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "scoring_in_step_with_k_tiling": fused,
         "scoring_with_probs": {"ms": round(score_p_ms, 4), "gbps": round(score_p_bytes / (score_p_ms * 1e-3) / 1e9, 1),
                                "frac_hbm_peak": round(score_p_bytes / (score_p_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                                "bytes": score_p_bytes},
@@ -406,6 +555,7 @@ def main():
                         "note": "estimator with the synthetic (untrained) MLP weights against the oracle mask"},
         "dense": dense,
         "next_rows": nxt,
+        "long_workload": long_row,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
