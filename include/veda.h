@@ -27,13 +27,15 @@
  * padded tilings see below):
  *  - VEDA_TILE_ROWS: [B, H, N, d]; row r holds token perm_h[r] of the raster sequence,
  *    where tile r / P is numbered row-major over the tile grid (t/p_t, h/p_h, w/p_w) and
- *    r % P row-major over (p_t, p_h, p_w).  Q, K and the attention output use it.
+ *    r % P row-major over (p_t, p_h, p_w).  Q, K, V and the attention output use it.
  *  - VEDA_TILE_COLS: [B, H, n_t, d, P]; the same tiles, each stored channel-major:
  *    element (position p, channel c) of tile j at ((j*d + c)*P + p) holds token
  *    key(p) of the tile, where within every group of 16 positions the tokens are ordered
  *    0-3, 8-11, 4-7, 12-15 (key(p) = 16*(p/16) + {0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15}
- *    [p%16]).  V uses it: that is the order in which the attention kernel's probability
- *    fragments meet V in the MFMA, so every V operand is one contiguous 16-byte read.
+ *    [p%16]).  The attention calls also take V in it: that is the order in which the
+ *    attention kernel's probability fragments meet V in the MFMA, so every V operand is
+ *    one contiguous 16-byte read (a VEDA_TILE_ROWS V takes two transposed 8-byte reads per
+ *    operand instead, at the same speed; the results are bit-identical).
  * The raster layout is [B, N, H, d] with any element strides for b, n, h and d contiguous;
  * raster token n = (t*H + h)*W + w.
  *
@@ -51,9 +53,10 @@
  *    (top-k and maps never pick or fill the others: scores -inf, probabilities and map
  *    entries 0).  k must not exceed the smallest n_t(h).
  *  - VEDA_F32 returns VEDA_ERR_UNSUPPORTED for such a geometry.  The raster attention and
- *    tile-map calls read K tiled (k_layout VEDA_TILE_ROWS, else VEDA_ERR_UNSUPPORTED); the
- *    raster scoring call reads K raster or tiled, and its k_tiled_out copy has the zero
- *    rows too.  Raster outputs hold the real tokens only (padding rows have none).  Both
+ *    tile-map calls read K tiled (k_layout VEDA_TILE_ROWS, else VEDA_ERR_UNSUPPORTED), and
+ *    the raster attention V tiled too (a raster V: VEDA_ERR_UNSUPPORTED); the raster
+ *    scoring call reads K raster or tiled, and its k_tiled_out and v_tiled_out copies have
+ *    the zero rows too.  Raster outputs hold the real tokens only (padding rows have none).  Both
  *    tile-map calls need an explicit q_tiles list.  veda_distill_step takes each head's
  *    own n_t(h) key tiles (target columns past them are ignored and get no gradient).
  */
@@ -156,10 +159,10 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  * O = softmax(Q_i K_sel^T * softmax_scale) V_sel over the keys of the tiles
  * kv_idx[b, h, i, 0..k-1], the softmax renormalised over those keys.
  *   q_tiled, k_tiled: VEDA_TILE_ROWS
- *   v_tiled, v_layout: V and the layout the caller holds it in.  Only VEDA_TILE_COLS
- *           (channel-major tiles, as veda_tile_gather writes them with that layout) is
- *           read; any other layout returns VEDA_ERR_UNSUPPORTED with nothing launched (a
- *           VEDA_TILE_ROWS V must first go through veda_tile_gather with VEDA_TILE_COLS)
+ *   v_tiled, v_layout: V and the layout it is in: VEDA_TILE_ROWS (tile-major, as Q and K)
+ *           or VEDA_TILE_COLS (channel-major tiles); both give bit-identical results.
+ *           VEDA_RASTER returns VEDA_ERR_UNSUPPORTED (no strides here: see the raster
+ *           call), any other value VEDA_ERR_SHAPE, with nothing launched
  *   kv_idx: [B, H, n_t, k] int32, each entry in [0, n_t), no repeats within a row
  *           (k == n_t with every tile listed is dense attention).  Entries outside
  *           [0, n_t) are clamped into it (no out-of-bounds access; the result is then
@@ -203,8 +206,10 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
  * is raster token origin_h(j) + intra_h(r).  k_layout says where K is: VEDA_RASTER (with
  * the same strides as Q) or VEDA_TILE_ROWS (tile-major [B, H, N, d], from
  * veda_tile_gather; K tiles are then contiguous 32 KB copies, which the attention and
- * tile-map kernels prefer).  V stays VEDA_TILE_COLS (v_layout, checked as in
- * veda_sparse_attn_fwd).  The output of veda_sparse_attn_fwd_raster is raster (same
+ * tile-map kernels prefer).  veda_sparse_attn_fwd_raster takes V as VEDA_TILE_ROWS,
+ * VEDA_TILE_COLS or VEDA_RASTER (v_layout; a raster V has the strides of Q and is read
+ * through the tiling like a raster K, bit-identical but slower than a tiled V, whose tiles
+ * are contiguous 32 KB copies).  The output of veda_sparse_attn_fwd_raster is raster (same
  * strides) and its lse is [B, H, t*h*w] in raster token order; the tile-map lse keeps its
  * [B, H, n_sel * P] tile-row order.  Extra status: VEDA_ERR_UNSUPPORTED if an in-tile
  * token offset times the token stride reaches 2^31 bytes.  Other arguments, outputs and
@@ -213,17 +218,21 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
  * VEDA_RASTER, else VEDA_ERR_SHAPE): [B, H, N, d] of `dtype`, which receives K's tile-major
  * copy (exactly what veda_tile_gather writes with VEDA_TILE_ROWS), written as K is read for
  * pooling, so that one pass over K both scores it and tiles it for the attention and
- * tile-map calls (the paper's future work on kernel fusion). */
+ * tile-map calls (the paper's future work on kernel fusion).  It also takes v_raster and
+ * v_tiled_out (both NULL, or both set, else VEDA_ERR_NULL; any k_layout): a raster V with
+ * the strides of Q, and [B, H, N, d] of `dtype` that receives V's VEDA_TILE_ROWS copy
+ * (exactly what veda_tile_gather writes), streamed by workgroups of the same launch that
+ * only copy, so that the scoring pass also leaves V tiled for the attention call. */
 veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
                                        float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *k_tiled_out, void *workspace, size_t workspace_bytes,
-                                       hipStream_t stream);
+                                       void *k_tiled_out, const void *v_raster, void *v_tiled_out, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                         veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
-                                        const void *v_cols, veda_layout v_layout, const int32_t *kv_idx,
+                                        const void *v, veda_layout v_layout, const int32_t *kv_idx,
                                         int32_t k_kept,
                                         float softmax_scale, void *o_raster, float *lse, hipStream_t stream);
 veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
@@ -247,7 +256,8 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
                                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               void *k_tiled_out, hipStream_t stream);
+                                               void *k_tiled_out, const void *v_raster, void *v_tiled_out,
+                                               hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
  * gradients of the sampled Q tiles and of every K tile, per-row KL terms). */

@@ -73,15 +73,17 @@ def test_padded_tile_counts(L):
 
 
 def test_padded_rejected_where_unsupported(L):
-    """A padded tiling goes through the raster calls with K tiled (the raster attention and
-    tile map refuse a raster K), and the all-tiles tile map needs an explicit list; each
-    refusal comes before anything is launched."""
+    """A padded tiling goes through the raster calls with K and V tiled (the raster attention
+    and tile map refuse a raster K, the attention a raster V), and the all-tiles tile map
+    needs an explicit list; each refusal comes before anything is launched."""
     g = geom(grid=(20, 16, 32), shapes=((8, 4, 4), (2, 8, 8)))
     n_t = g.n_tiles                                           # 3 * 4 * 8 = 96 > 80 (dividing head)
     st = (g.n_tokens * 2 * 128, 2 * 128, 128)
     RAS, big = V.RASTER, 1 << 40
     assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, 4, 0.088, A, None,
                                          None) == UNSUP
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, RAS, A, 4, 0.088, A, None,
+                                         None) == UNSUP                      # a raster V, likewise
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, RAS, *st, 0.088, A, 4, A, None, A, big, None) == UNSUP
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, None, n_t, A, None, A, big,
                                         None) == SHAPE
@@ -93,7 +95,7 @@ def test_padded_rejected_where_unsupported(L):
     assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, 81, A, A,
                                  big, None) == SHAPE
     assert L.veda_trippool_score_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None,
-                                        None, 81, A, None, A, big, None) == SHAPE
+                                        None, 81, A, None, None, None, A, big, None) == SHAPE
     assert L.veda_distill_step(g.ref, V.BF16, A, A, A, A, 256, 64, 0.125, A, n_t + 1, A, A, A, A, 0.0, A, big,
                                None) == SHAPE
 
@@ -160,15 +162,16 @@ def test_attn_validation(L):
     assert f(geom(d=64).ref, V.BF16, A, A, A, C, A, 4, 0.088, A, None, None) == UNSUP
 
 
-def test_attn_refuses_v_not_channel_major(L):
-    """V is read channel-major (VEDA_TILE_COLS) only: a tile-major or raster V is refused
-    with a status, never computed as if it were channel-major."""
+def test_attn_v_layout_validation(L):
+    """V may be channel-major or tile-major in both calls and raster in the raster call; a
+    raster V in the tiled call (no strides) and an unknown layout are refused with a status,
+    never computed as if V were in another layout."""
     g = geom()
-    for lay in (V.ROWS, V.RASTER, 7):
-        assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, lay, A, 4, 0.088, A, None, None) == UNSUP
-        st = (4096 * 2 * 128, 2 * 128, 128)
-        assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, lay, A, 4, 0.088, A, None,
-                                             None) == UNSUP
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.RASTER, A, 4, 0.088, A, None, None) == UNSUP
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, 7, A, 4, 0.088, A, None, None) == SHAPE
+    st = (4096 * 2 * 128, 2 * 128, 128)
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, 7, A, 4, 0.088, A, None,
+                                         None) == SHAPE
 
 
 def test_tilemap_validation(L):
@@ -236,13 +239,20 @@ def test_raster_validation(L):
     assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, C, A, 4,
              0.088, A, None, None) == UNSUP
     s = L.veda_trippool_score_raster
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None, A,
-             1 << 30, None) == NULL
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None, None,
+             None, A, 1 << 30, None) == NULL
     # K's tiled copy comes only from a raster K, and must be aligned
-    assert s(g.ref, V.BF16, A, A, V.ROWS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, B_, A,
-             1 << 30, None) == SHAPE
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, MIS, A,
-             1 << 30, None) == ALIGN
+    assert s(g.ref, V.BF16, A, A, V.ROWS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, B_, None,
+             None, A, 1 << 30, None) == SHAPE
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, MIS, None,
+             None, A, 1 << 30, None) == ALIGN
+    # V's tiled copy needs the raster V and the output together, both aligned
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, A,
+             None, A, 1 << 30, None) == NULL
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, None,
+             B_, A, 1 << 30, None) == NULL
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, A,
+             MIS, A, 1 << 30, None) == ALIGN
     t = L.veda_oracle_tilemap_raster
     assert t(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, A, 0, A, None, A, 1 << 40, None) == SHAPE
 
@@ -296,15 +306,17 @@ def test_noalloc_scoring_rejects_beyond_its_scratch(L):
     big = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 56)        # 56 heads x 1200 tiles = 67200
     st = (153600 * 56 * 128, 56 * 128, 128)
     assert f(big.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A, None,
-             None) == -8
+             None, None, None) == -8
     assert b"scratch" in L.veda_status_str(-8)
     fits = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 54)       # 64800 tiles: passes the size check,
     st = (153600 * 54 * 128, 54 * 128, 128)                         # then a NULL K is refused
     assert f(fits.ref, V.BF16, A, None, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A, None,
-             None) == NULL
+             None, None, None) == NULL
     g = geom()
     st = (4096 * 2 * 128, 2 * 128, 128)
     assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None,
-             None) == NULL
+             None, None, None) == NULL
     assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 512, 64, 0.125, None, None, None, None, 6, A, None,
-             None) == UNSUP
+             None, None, None) == UNSUP
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None,
+             A, None, None) == NULL                                    # V's copy: both or neither

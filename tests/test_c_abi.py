@@ -49,7 +49,7 @@ def test_sizes(c_out):
 def test_validation(c_out):
     assert int(c_out["attn_null"]) == -1      # VEDA_ERR_NULL
     assert int(c_out["attn_dtype"]) == -3     # VEDA_ERR_DTYPE
-    assert int(c_out["attn_v_rows"]) == -4    # VEDA_ERR_UNSUPPORTED: V must be channel-major
+    assert int(c_out["attn_v_raster"]) == -4  # VEDA_ERR_UNSUPPORTED: a raster V needs the raster call
     assert int(c_out["topk_k0"]) == -2        # VEDA_ERR_SHAPE
     assert int(c_out["topk_empty"]) == 0      # zero rows: nothing to do
     assert int(c_out["tiled_tokens_bad"]) == -2

@@ -113,6 +113,14 @@ class PaddedRun:
             self._oh[(b, h)] = tuple(O.to_tiles(self.wl.head(w, b, h), slots) for w in ("q", "k", "v")) + (slots,)
         return self._oh[(b, h)]
 
+    def v_cols(self):
+        """V gathered channel-major (VEDA_TILE_COLS), made once."""
+        if not hasattr(self, "_v_cols"):
+            self._v_cols = torch.empty_like(self.sa.v_t)
+            V.veda_tile_gather(self.geom, self.v, self._v_cols, V.COLS)
+            torch.cuda.synchronize()
+        return self._v_cols
+
     def q_tiles(self, h):
         t = self.wl.sample_tiles(h)
         if self.n_tiles_checked is not None:
@@ -137,9 +145,11 @@ def test_padded_gather(r):
         gq, gk = host(r.sa.q_t[b, h]), host(r.sa.k_t[b, h])
         assert bitwise_equal(gq[:n], qt) and bitwise_equal(gk[:n], kt), (cfg.name, h)
         assert not gq[n:].any() and not gk[n:].any(), (cfg.name, h, "rows past the head's tiles")
+        gv = host(r.sa.v_t[b, h])
+        assert bitwise_equal(gv[:n], vt) and not gv[n:].any(), (cfg.name, h, "v")
         ntile = n // P
-        vcols = host(r.sa.v_t[b, h]).reshape(r.nt, d, P).transpose(0, 2, 1)[:ntile]
-        assert bitwise_equal(vcols, vt.reshape(ntile, P, d)[:, COLS_KEY[:P], :]), (cfg.name, h, "v")
+        vcols = host(r.v_cols()[b, h]).reshape(r.nt, d, P).transpose(0, 2, 1)[:ntile]
+        assert bitwise_equal(vcols, vt.reshape(ntile, P, d)[:, COLS_KEY[:P], :]), (cfg.name, h, "v channel-major")
     back = torch.empty_like(r.q)
     V.veda_tile_gather(r.geom, back, r.sa.q_t, V.ROWS, inverse=True)
     torch.cuda.synchronize()
@@ -252,10 +262,13 @@ def test_padded_raster_path(r):
         scores, qd, kd = torch.empty_like(r.scores), torch.empty_like(r.qd), torch.empty_like(r.kd)
         idx = torch.full_like(r.idx, -1)
         k_copy = torch.full_like(sa.k_t, float("nan")) if k_layout == V.RASTER else None
+        v_copy = torch.full_like(sa.v_t, float("nan"))
         V.veda_trippool_score_raster(g, r.q, r.k if k_layout == V.RASTER else sa.k_t, sa.w1, sa.w2,
                                      score_scale=cfg.score_scale, scores=scores, q_desc=qd, k_desc=kd, topk=r.kk,
-                                     idx=idx, workspace=sa.ws, k_layout=k_layout, k_tiled_out=k_copy)
+                                     idx=idx, workspace=sa.ws, k_layout=k_layout, k_tiled_out=k_copy,
+                                     v=r.v, v_tiled_out=v_copy)
         torch.cuda.synchronize()
+        assert torch.equal(v_copy.view(torch.int16), sa.v_t.view(torch.int16)), (cfg.name, "V's copy")
         assert torch.equal(qd, r.qd) and torch.equal(kd, r.kd), (cfg.name, k_layout)
         for h in range(H):   # a head's own rows (the rows past its tiles are not written)
             nth = g.head_tiles(h)
@@ -268,6 +281,21 @@ def test_padded_raster_path(r):
     sa.attend_raster(r.q, r.idx, out, lse)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), r.out.view(torch.int16)), cfg.name
+    # V channel-major (the attention above read it tile-major), in both calls
+    v_cols = r.v_cols()
+    o_t = torch.empty_like(sa.o_t)
+    lse_t2 = torch.empty_like(r.lse)
+    V.veda_sparse_attn_fwd(g, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse_t2, v_layout=V.COLS)
+    out2 = torch.zeros_like(r.q)
+    V.veda_sparse_attn_fwd_raster(g, r.q, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, out2, k_layout=V.ROWS,
+                                  v_layout=V.COLS)
+    torch.cuda.synchronize()
+    for h in range(H):   # a head's own rows (rows past its tiles are not written)
+        rows = g.head_tiles(h) * P
+        assert torch.equal(o_t[:, h, :rows].view(torch.int16), sa.o_t[:, h, :rows].view(torch.int16)), (cfg.name, h)
+        assert torch.equal(lse_t2[:, h, :rows], r.lse[:, h, :rows]), (cfg.name, h)
+    assert torch.equal(out2.view(torch.int16), r.out.view(torch.int16)), cfg.name
+    del o_t, out2
     lse_r, lse_t = lse.cpu().numpy(), r.lse.cpu().numpy()
     for b in range(B):
         for h in range(H):

@@ -91,6 +91,14 @@ class Run:
     def q_tiles(self, h):
         return self.wl.sample_tiles(h)
 
+    def v_cols(self):
+        """V gathered channel-major (VEDA_TILE_COLS), made once."""
+        if not hasattr(self, "_v_cols"):
+            self._v_cols = torch.empty_like(self.sa.v_t)
+            V.veda_tile_gather(self.geom, self.v, self._v_cols, V.COLS)
+            torch.cuda.synchronize()
+        return self._v_cols
+
 
 CFGS = [0, 1, 2, 3, 4]
 
@@ -127,9 +135,10 @@ def test_gather_bitexact(r):
             qt, kt, vt, perm = r.oracle_head(b, h)
             assert bitwise_equal(host(r.sa.q_t[b, h]), qt), (cfg.name, h, "q")
             assert bitwise_equal(host(r.sa.k_t[b, h]), kt), (cfg.name, h, "k")
-            vcols = host(r.sa.v_t[b, h]).reshape(nt, d, P).transpose(0, 2, 1)        # [tile][pos][c]
+            assert bitwise_equal(host(r.sa.v_t[b, h]), vt), (cfg.name, h, "v")
+            vcols = host(r.v_cols()[b, h]).reshape(nt, d, P).transpose(0, 2, 1)      # [tile][pos][c]
             vkeys = vt.reshape(nt, P, d)[:, COLS_KEY[:P], :]                          # same order
-            assert bitwise_equal(vcols, vkeys), (cfg.name, h, "v")
+            assert bitwise_equal(vcols, vkeys), (cfg.name, h, "v channel-major")
     # scatter(gather(q)) is the identity
     back = torch.empty_like(r.q)
     V.veda_tile_gather(r.geom, back, r.sa.q_t, V.ROWS, inverse=True)
@@ -458,6 +467,36 @@ def test_topk_mask_standalone(n_cols, k):
     assert np.array_equal(host(mask), m)
 
 
+# ----------------------------------------------------------------------------- V layouts
+def same_bits(a, b):
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return a.dtype == b.dtype and torch.equal(a.view(view), b.view(view))
+
+
+def test_v_layouts_match(r):
+    """Attention with V channel-major (COLS: one 16-byte LDS read per operand) or raster
+    (transposed LDS reads, as for the tile-major V of the tests above) gives bit for bit the
+    output and LSE of the tile-major V, which the tests above check against the oracle: the
+    same products meet the same MFMA slots in the same order.  Tiled call with a COLS V;
+    raster call with K tiled or raster and V COLS or raster."""
+    cfg, sa = r.cfg, r.sa
+    say(f"[gpu-parity] {cfg.name}: V layouts")
+    v_cols = r.v_cols()
+    o_t = torch.empty_like(sa.o_t)
+    lse = torch.empty_like(r.lse)
+    V.veda_sparse_attn_fwd(r.geom, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse, v_layout=V.COLS)
+    torch.cuda.synchronize()
+    assert same_bits(o_t, sa.o_t) and same_bits(lse, r.lse), cfg.name
+    del o_t
+    for k_layout, kop in ((V.ROWS, sa.k_t), (V.RASTER, r.k)):
+        for v_layout, vop in ((V.COLS, v_cols), (V.RASTER, r.v)):
+            out = torch.zeros_like(r.out)
+            V.veda_sparse_attn_fwd_raster(r.geom, r.q, kop, vop, r.idx, r.kk, sa.softmax_scale, out,
+                                          k_layout=k_layout, v_layout=v_layout)
+            torch.cuda.synchronize()
+            assert same_bits(out, r.out), (cfg.name, k_layout, v_layout)
+
+
 # ----------------------------------------------------------------------------- raster path
 @pytest.mark.parametrize("k_raster", [False, True], ids=["k_tiled", "k_raster"])
 def test_raster_path_matches_tiled(r, k_raster):
@@ -499,10 +538,19 @@ def test_raster_path_matches_tiled(r, k_raster):
         # the scoring pass that also writes K's tile-major copy: the copy equals the gather's,
         # and the selections are unchanged
         k_copy = torch.full_like(sa.k_t, float("nan"))
+        v_copy = torch.full_like(sa.v_t, float("nan"))
         idx2 = torch.full_like(idx, -1)
         V.veda_trippool_score_raster(r.geom, r.q, r.k, sa.w1, sa.w2, score_scale=cfg.score_scale, topk=r.kk,
-                                     idx=idx2, workspace=sa.ws, k_layout=V.RASTER, k_tiled_out=k_copy)
+                                     idx=idx2, workspace=sa.ws, k_layout=V.RASTER, k_tiled_out=k_copy,
+                                     v=r.v, v_tiled_out=v_copy)
         torch.cuda.synchronize()
         assert torch.equal(idx2, r.idx)
-        assert torch.equal(k_copy.view(torch.int16) if r.bf16 else k_copy.view(torch.int32),
-                           sa.k_t.view(torch.int16) if r.bf16 else sa.k_t.view(torch.int32))
+        assert same_bits(k_copy, sa.k_t) and same_bits(v_copy, sa.v_t)
+    else:
+        # V's copy from the scoring launch with a tiled K as well
+        v_copy = torch.full_like(sa.v_t, float("nan"))
+        idx2 = torch.full_like(idx, -1)
+        V.veda_trippool_score_raster(r.geom, r.q, sa.k_t, sa.w1, sa.w2, score_scale=cfg.score_scale, topk=r.kk,
+                                     idx=idx2, workspace=sa.ws, k_layout=V.ROWS, v=r.v, v_tiled_out=v_copy)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, r.idx) and same_bits(v_copy, sa.v_t)

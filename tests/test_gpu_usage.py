@@ -2,9 +2,10 @@
 
 - A fused QKV projection emits one [B, N, 3, H, d] tensor; the raster calls take Q, K and V as
   strided views of it (token stride 3*H*d) and give bit for bit what contiguous copies give.
-- The default step (gather V; scoring with K's tiled copy, through the no-allocation call;
-  attention and tile map with raster Q and O) captured into a HIP graph: every replay, with
-  eager work and synchronisations between them, gives the eager step's results bit for bit.
+- The default step (scoring through the no-allocation call, its launch also writing K's and
+  V's tiled copies; attention and tile map with raster Q and O) captured into a HIP graph:
+  every replay, with eager work and synchronisations between them, gives the eager step's
+  results bit for bit.
   The no-allocation call is there for exactly such callers: nothing in the captured step
   allocates or clears memory.
 Both compare against the calls that test_gpu_parity checks against the oracle."""
@@ -70,9 +71,9 @@ def test_graph_capture_noalloc_step():
     tm_ws = torch.empty(V.veda_oracle_tilemap_workspace_bytes(geom, n_sel), dtype=torch.uint8, device="cuda")
 
     def step():
-        sa.gather_v(v)
         V.veda_trippool_score_raster_noalloc(geom, q, k, sa.w1, sa.w2, score_scale=cfg.score_scale, topk=kk,
-                                             idx=idx, k_layout=V.RASTER, k_tiled_out=sa.k_t)
+                                             idx=idx, k_layout=V.RASTER, k_tiled_out=sa.k_t, v=v,
+                                             v_tiled_out=sa.v_t)
         V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, sa.v_t, idx, kk, sa.softmax_scale, out, k_layout=V.ROWS)
         V.veda_oracle_tilemap_raster(geom, q, sa.k_t, sa.softmax_scale, qtl, n_sel, tmap, workspace=tm_ws,
                                      k_layout=V.ROWS)

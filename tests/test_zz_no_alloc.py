@@ -24,7 +24,7 @@ def run_case(name, topk, k_layout):
     B, H, d, P, nt = cfg.batch, cfg.heads, cfg.head_dim, cfg.tile, cfg.n_tiles
     geom = V.Geom(B, H, d, cfg.grid, P, wl.shapes)
     up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).permute(0, 2, 1, 3).contiguous()
-    q, k = up(wl.q), up(wl.k)
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
     if k_layout == V.ROWS:
         kt = torch.empty((B, H, geom.n_tiled, d), dtype=torch.bfloat16, device="cuda")
         V.veda_tile_gather(geom, k, kt, V.ROWS)
@@ -39,21 +39,24 @@ def run_case(name, topk, k_layout):
                     idx=torch.full((B, H, nt, topk), -1, dtype=torch.int32, device="cuda"))
 
     ref, got = outputs(), outputs()
-    if k_layout == V.RASTER:   # with a raster K, both calls also write K's tile-major copy
-        ref["k_tiled_out"] = torch.zeros((B, H, geom.n_tiled, d), dtype=torch.bfloat16, device="cuda")
-        got["k_tiled_out"] = torch.ones_like(ref["k_tiled_out"])
+    vin = {}
+    if k_layout == V.RASTER:   # with a raster K, both calls also write K's and V's tile-major copies
+        for key in ("k_tiled_out", "v_tiled_out"):
+            ref[key] = torch.zeros((B, H, geom.n_tiled, d), dtype=torch.bfloat16, device="cuda")
+            got[key] = torch.ones_like(ref[key])
+        vin = dict(v=v)
     ws = torch.empty(V.veda_trippool_workspace_bytes(geom, 256, 64), dtype=torch.uint8, device="cuda")
     V.veda_trippool_score_raster(geom, q, k, w1, w2, score_scale=cfg.score_scale, topk=topk, workspace=ws,
-                                 k_layout=k_layout, **ref)
+                                 k_layout=k_layout, **vin, **ref)
     V.veda_trippool_score_raster_noalloc(geom, q, k, w1, w2, score_scale=cfg.score_scale, topk=topk,
-                                         k_layout=k_layout, **got)
+                                         k_layout=k_layout, **vin, **got)
     torch.cuda.synchronize()
     for key in ref:
         a, b = ref[key], got[key]
         if a.dtype == torch.bfloat16:
             a, b = a.view(torch.int16), b.view(torch.int16)
         assert torch.equal(a, b), (name, key)
-    say(f"[no-alloc] {name}: k={topk} layout={k_layout}: scores, probs, descriptors and top-k identical")
+    say(f"[no-alloc] {name}: k={topk} layout={k_layout}: " + ", ".join(ref) + " identical")
 
 
 def test_noalloc_matches_workspace_call_twice():

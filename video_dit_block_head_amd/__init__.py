@@ -99,9 +99,9 @@ def lib():
             "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
-                                                 vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+                                                 vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "veda_trippool_score_raster_noalloc": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32,
-                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp, vp]),
+                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
             "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
                                                   vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
@@ -297,8 +297,11 @@ def _kv_idx(geom, kv_idx, k):
 
 
 def veda_sparse_attn_fwd(geom, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse=None,
-                         v_layout=COLS, stream=None):
-    """v_tiled holds V in v_layout; the library reads COLS only (anything else is refused)."""
+                         v_layout=ROWS, stream=None):
+    """v_tiled holds V in v_layout: COLS (channel-major tiles) or ROWS (tile-major, like Q
+    and K)."""
+    if v_layout not in (COLS, ROWS):
+        raise VedaError("v_layout must be COLS or ROWS (a raster V goes to veda_sparse_attn_fwd_raster)")
     dt = _elem_dtype(q_tiled)
     n = _tiled_numel(geom)
     _call("veda_sparse_attn_fwd",
@@ -420,33 +423,53 @@ def _k_tiled_out(geom, q, t):
     return _p(t, "k_tiled_out", True, _elem_dtype(q), _tiled_numel(geom))
 
 
+def _v_copy(geom, q, v, v_tiled_out):
+    """Checked pointers of the V copy of the raster scoring calls: both or neither."""
+    if (v is None) != (v_tiled_out is None):
+        raise VedaError("v and v_tiled_out go together")
+    if v is None:
+        return None, None
+    dt = _elem_dtype(q)
+    return _raster(geom, v, "v", dt), _p(v_tiled_out, "v_tiled_out", True, dt, _tiled_numel(geom))
+
+
 def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125, scores=None,
                                probs=None, q_desc=None, k_desc=None, topk=0, idx=None, workspace=None,
-                               k_layout=RASTER, k_tiled_out=None, stream=None):
+                               k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None):
     """veda_trippool_score on raster Q [B, N, H, d] (read through each head's tiling); K
     raster too, or tile-major with k_layout=ROWS.  With a raster K, k_tiled_out (if given)
-    receives K's tile-major copy, written while K is pooled."""
+    receives K's tile-major copy, written while K is pooled; with a raster V (strides of Q),
+    v_tiled_out receives V's tile-major copy from the same launch."""
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
-    rs, kp = _k_operand(geom, q, k, k_layout)
+    rs, kp = _k_operand(geom, q, k, k_layout, *(() if v is None else (v,)))
     qp = _raster(geom, q, "q", _elem_dtype(q))
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
     outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    vc = _v_copy(geom, q, v, v_tiled_out)
     _call("veda_trippool_score_raster",
           geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e, hidden, mout, float(score_scale),
-          *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), _p(workspace, "workspace"),
+          *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), *vc, _p(workspace, "workspace"),
           _ws(workspace), _stream(stream))
 
 
-def veda_sparse_attn_fwd_raster(geom, q, k, v_cols, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
-                                v_layout=COLS, stream=None):
+def veda_sparse_attn_fwd_raster(geom, q, k, v, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
+                                v_layout=ROWS, stream=None):
     """veda_sparse_attn_fwd with raster Q and output O [B, N, H, d]; K raster or tile-major
-    (k_layout=ROWS); V channel-major tiled; lse [B, H, N] in raster token order."""
+    (k_layout=ROWS); V channel-major tiled (COLS), tile-major (ROWS) or raster (RASTER, with
+    the strides of Q and O); lse [B, H, N] in raster token order."""
     dt = _elem_dtype(q)
-    rs, kp = _k_operand(geom, q, k, k_layout, o)
+    if v_layout == RASTER:
+        rs, kp = _k_operand(geom, q, k, k_layout, o, v)
+        vp = _raster(geom, v, "v", dt)
+    elif v_layout in (COLS, ROWS):
+        rs, kp = _k_operand(geom, q, k, k_layout, o)
+        vp = _p(v, "v", True, dt, _tiled_numel(geom))
+    else:
+        raise VedaError("v_layout must be COLS, ROWS or RASTER")
     _call("veda_sparse_attn_fwd_raster",
         geom.ref, _dtype_code(q), _raster(geom, q, "q", dt), kp, int(k_layout), *rs,
-        _p(v_cols, "v_cols", True, dt, _tiled_numel(geom)), int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
+        vp, int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
         float(softmax_scale), _raster(geom, o, "o", dt),
         _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tokens), _stream(stream))
 
@@ -463,15 +486,16 @@ def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilema
 
 def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
                                        scores=None, probs=None, q_desc=None, k_desc=None, topk=0, idx=None,
-                                       k_layout=RASTER, k_tiled_out=None, stream=None):
+                                       k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None):
     """veda_trippool_score_raster with no workspace: the library's static scratch holds the
     MLP outputs (B * H * n_t <= 65536 tiles; calls that overlap on one GPU race)."""
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
-    rs, kp = _k_operand(geom, q, k, k_layout)
+    rs, kp = _k_operand(geom, q, k, k_layout, *(() if v is None else (v,)))
     qp = _raster(geom, q, "q", _elem_dtype(q))
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
     outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    vc = _v_copy(geom, q, v, v_tiled_out)
     _call("veda_trippool_score_raster_noalloc", geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e,
-          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out),
+          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), *vc,
           _stream(stream))

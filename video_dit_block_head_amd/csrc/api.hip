@@ -117,7 +117,8 @@ veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void 
                                const float *w2_q, const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                int32_t mlp_out, const float *scores, const float *probs, const float *q_desc,
                                const float *k_desc, int32_t topk, const int32_t *idx, const void *k_tiled_out,
-                               Geo *geo, HeadShapes *hs, RasterView *rv) {
+                               const void *v_raster, const void *v_tiled_out, Geo *geo, HeadShapes *hs,
+                               RasterView *rv) {
   int nt_min;
   veda_status s = check_geom(g, dtype, geo, hs, &nt_min);
   if (s != VEDA_OK) return s;
@@ -127,7 +128,9 @@ veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void 
   if (topk < 0 || topk > nt_min) return VEDA_ERR_SHAPE;
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo->nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
-  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, k_tiled_out};
+  if ((v_raster == nullptr) != (v_tiled_out == nullptr)) return VEDA_ERR_NULL;  // V's copy: both or neither
+  const void *ptrs[] = {q_raster, k_raster, w1_q,   w2_q,        w1_k,     w2_k,       scores,
+                        probs,    q_desc,   k_desc, idx, k_tiled_out, v_raster, v_tiled_out};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
@@ -232,21 +235,21 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
                                        float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *k_tiled_out, void *workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+                                       void *k_tiled_out, const void *v_raster, void *v_tiled_out, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
                                      w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
-                                     k_tiled_out, &geo, &hs, &rv);
+                                     k_tiled_out, v_raster, v_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (workspace != nullptr && !aligned16(workspace)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER, k_tiled_out));
+                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out));
 }
 
 veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dtype, const void *q_raster,
@@ -255,13 +258,14 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
                                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               void *k_tiled_out, hipStream_t stream) {
+                                               void *k_tiled_out, const void *v_raster, void *v_tiled_out,
+                                               hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
                                      w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
-                                     k_tiled_out, &geo, &hs, &rv);
+                                     k_tiled_out, v_raster, v_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (score_workspace_bytes(geo, mlp_hidden, mlp_out) > SCRATCH_BYTES) return VEDA_ERR_SCRATCH;
   void *ws = nullptr;
@@ -269,7 +273,7 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
   // The MLP outputs are written whole before they are read: nothing needs clearing.
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, ws, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER, k_tiled_out));
+                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out));
 }
 
 veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k, int32_t *idx,
@@ -291,36 +295,38 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
   veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !v_tiled || !kv_idx || !o_tiled) return VEDA_ERR_NULL;
-  if (v_layout != VEDA_TILE_COLS) return VEDA_ERR_UNSUPPORTED;  // V is read channel-major only
+  if (v_layout == VEDA_RASTER) return VEDA_ERR_UNSUPPORTED;  // no raster strides in the tiled call
+  if (v_layout != VEDA_TILE_ROWS && v_layout != VEDA_TILE_COLS) return VEDA_ERR_SHAPE;
   if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
   const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, o_tiled, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
-  return hip_status(launch_sparse_attn(geo, hs, dtype, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse,
-                                       stream));
+  return hip_status(launch_sparse_attn(geo, hs, dtype, q_tiled, k_tiled, v_tiled, v_layout, kv_idx, k, softmax_scale,
+                                       o_tiled, lse, stream));
 }
 
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
                                         const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
                                         int64_t rs_h,
-                                        const void *v_cols, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
+                                        const void *v, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
                                         float softmax_scale, void *o_raster, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
   veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
-  if (!q_raster || !k_raster || !v_cols || !kv_idx || !o_raster) return VEDA_ERR_NULL;
-  if (v_layout != VEDA_TILE_COLS) return VEDA_ERR_UNSUPPORTED;
+  if (!q_raster || !k_raster || !v || !kv_idx || !o_raster) return VEDA_ERR_NULL;
   if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
-  const void *ptrs[] = {q_raster, k_raster, v_cols, kv_idx, o_raster, lse};
+  const void *ptrs[] = {q_raster, k_raster, v, kv_idx, o_raster, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
+  if (v_layout != VEDA_RASTER && v_layout != VEDA_TILE_ROWS && v_layout != VEDA_TILE_COLS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
-  if (geo.padded && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_UNSUPPORTED;  // padded: K tiled
+  // padded tilings: K and V tiled (the copies read whole tiles)
+  if (geo.padded && (k_layout != VEDA_TILE_ROWS || v_layout == VEDA_RASTER)) return VEDA_ERR_UNSUPPORTED;
   return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
-                                              rs_h, v_cols, kv_idx, k, softmax_scale, o_raster, lse, stream));
+                                              rs_h, v, v_layout, kv_idx, k, softmax_scale, o_raster, lse, stream));
 }
 
 size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {

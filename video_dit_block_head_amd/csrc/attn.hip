@@ -4,14 +4,19 @@
 // bf16 path (d = 128, P = 128), gfx950 MFMA v_mfma_f32_32x32x16_bf16:
 //  - one workgroup (4 waves) per query tile, two workgroups per CU; wave w owns queries
 //    32w .. 32w+31;
-//  - the kept K tile ([key][d]) and V tile ([d][key], channel-major in HBM) are copied
-//    straight into LDS (global_load_lds, no register staging) with the XOR swizzle
-//    "16-byte chunk c of row r at slot c ^ (r & 15)", which makes every MFMA operand read
-//    a conflict-free 16-byte LDS read, issued four MFMAs ahead of its use (scheduling
-//    groups: the default schedule read one ahead).  K and V have their own buffers: the
-//    next K tile streams in during softmax + P V, the next V tile during the next Q K^T.
-//    Three barriers per key tile: K(t) read (K buffer free), V(t) complete, and V(t) read
-//    with K(t+1) complete;
+//  - the kept K tile ([key][d]) and V tile are copied straight into LDS (global_load_lds,
+//    no register staging) with an XOR swizzle of the 16-byte chunks of each row, which
+//    makes every MFMA operand read conflict-free; the reads are issued four MFMAs ahead of
+//    their use (scheduling groups: the default schedule read one ahead).  K and V have
+//    their own buffers: the next K tile streams in during softmax + P V, the next V tile
+//    during the next Q K^T.  Three barriers per key tile: K(t) read (K buffer free), V(t)
+//    complete, and V(t) read with K(t+1) complete;
+//  - V comes in one of three layouts.  Channel-major tiles ([d][key], keys in the order in
+//    which the probabilities reach the MFMA) make each V operand one 16-byte row read.
+//    Tile-major rows ([key][d], like K) and the raster tensor itself are read with
+//    ds_read_b64_tr_b16: two transposed 8-byte reads per operand, each giving a lane one
+//    channel of four consecutive keys; their rows use the quad swizzle, which keeps these
+//    reads conflict-free too (K then uses it as well, so both copies share offsets);
 //  - S^T = K Q^T (32 keys x 32 queries per MFMA block) puts one query per lane column, so
 //    the row max needs one exchange between lane halves; O^T = V^T P^T keeps each lane's
 //    accumulators on its own query, so the online-softmax rescale is lane-local;
@@ -50,17 +55,22 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// V layouts of the attention kernels: channel-major tiles, tile-major rows, raster.
+enum { VM_COLS = 0, VM_ROWS = 1, VM_RAST = 2 };
+
 // RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
 // the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
-// order; RK: the same for K.  Otherwise tile-major.  V is always channel-major tiled.
-// PAD: padded tiling: per-head tile counts and partial key tiles (K tiled); with RQ the
-// padding query rows of a partial query tile are neither read (Q taken as zero, as the
-// gather stores it) nor written.
-template <bool RQ, bool RK, bool PAD>
+// order; RK: the same for K.  Otherwise tile-major.  VM: V's layout (VM_RAST with the
+// strides of Q).  PAD: padded tiling: per-head tile counts and partial key tiles (K and V
+// tiled); with RQ the padding query rows of a partial query tile are neither read (Q taken
+// as zero, as the gather stores it) nor written.
+template <bool RQ, bool RK, bool PAD, int VM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
                  const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
                  float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv) {
+  constexpr bool VROW = VM != VM_COLS;          // V read with transposed reads
+  constexpr int SW = VROW ? SWZ_QUAD : SWZ_ROW;  // swizzle of both LDS tiles
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   const int i = L % g.nt;
   const int64_t bh = L / g.nt;
@@ -72,7 +82,7 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   // raster: byte offset of (b, n = 0, h); a tile's rows are origin(j) + intra(r) tokens on
   const int64_t rhead = (int64_t)bb * rv.sb + (int64_t)hh * rv.sh;
   const char *kh = RK ? reinterpret_cast<const char *>(k) + rhead : reinterpret_cast<const char *>(k + head);
-  const char *vh = reinterpret_cast<const char *>(vt + head);
+  const char *vh = VM == VM_RAST ? reinterpret_cast<const char *>(vt) + rhead : reinterpret_cast<const char *>(vt + head);
   const int32_t *list = kv_idx + (bh * g.nt + i) * kk;
   // this head's tiles (fewer than nt for a head of a padded tiling with fewer tiles)
   const int nth = PAD ? head_tiles(hs.s[hh][0], hs.s[hh][1], hs.s[hh][2], g.T, g.Hs, g.Ws) : g.nt;
@@ -80,6 +90,9 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   const int last = nth - 1;
   auto k_tile = [&](int j) -> const char * {
     return RK ? kh + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn : kh + (int64_t)j * 32768;
+  };
+  auto v_tile = [&](int j) -> const char * {
+    return VM == VM_RAST ? vh + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn : vh + (int64_t)j * 32768;
   };
 
   __shared__ uint4 Ks[128 * 16];
@@ -106,20 +119,43 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   }
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
 
-  uint32_t off[8], koff[8];
-  tile_dma_offsets(w, lane, off);
-  if (RK)
-    tile_dma_offsets_raster(w, lane, ph, pw, g.Hs, g.Ws, rv.sn, koff);
+  // copy offsets of a tile-major tile and of a raster one (computed only if K or V is raster)
+  uint32_t toff[8], roff[8];
+  tile_dma_offsets<SW>(w, lane, toff);
+  if (RK || VM == VM_RAST)
+    tile_dma_offsets_raster<SW>(w, lane, ph, pw, g.Hs, g.Ws, rv.sn, roff);
   else
 #pragma unroll
-    for (int e = 0; e < 8; ++e) koff[e] = off[e];
+    for (int e = 0; e < 8; ++e) roff[e] = toff[e];
+  const uint32_t(&koff)[8] = RK ? roff : toff;
+  const uint32_t(&voff)[8] = VM == VM_RAST ? roff : toff;
   const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
+  // Transposed V reads (VROW): for MFMA block (s, db) lane l needs channel 32 db + l % 32 of
+  // keys 16 s + 4 hi + {0..3} (k-slots 0-3) and 16 s + 8 + 4 hi + {0..3} (slots 4-7), the
+  // keys whose probabilities sit in those slots of pb[s].  Within each 16-lane group lane i
+  // reads key row (first key) + i / 4, 8 bytes at channel 16 c' + 4 (i % 4), and the
+  // instruction hands lane i channel 16 c' + i of the four rows.  Byte offset in the V tile
+  // of read (p, db), before the key-block term (16 s + 8 p) * 256 that goes into the
+  // instruction's offset: (4 hi + i/4) * 256 + 16 * (chunk ^ swz) + 8 (i & 1) with chunk =
+  // 4 db + 2 ((l / 16) & 1) + (i % 4) / 2 and swz = g(i / 4) ^ (2 p + hi).
+  uint32_t vrd[2][4];
+  if (VROW) {
+    const int i16 = lane & 15, rq = i16 >> 2;
+    const int cb = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int slot = (4 * db + cb) ^ row_swz<SWZ_QUAD>(8 * p + 4 * hi + rq);
+        vrd[p][db] = vs_lds + (uint32_t)((4 * hi + rq) * 256 + 16 * slot + 8 * (i16 & 1));
+      }
+  }
   // The kept list is read 64 entries at a time into one register (lane l holds entry 64c + l)
   // and each step takes its entry with a readlane: no scalar load waits inside the loop.
   int lchunk = list[min(lane, kk - 1)];
   int jn = min(max(__builtin_amdgcn_readlane(lchunk, 0), 0), last);  // out-of-range entries are clamped
   tile_to_lds(k_tile(jn), ks_lds, w, koff);
-  tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
+  tile_to_lds(v_tile(jn), vs_lds, w, voff);
   wait_vmem<8>();
   barrier();  // K(0) is complete
 
@@ -157,7 +193,7 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 #pragma unroll
     for (int f = 0; f < 32; ++f) {
       const int kb = f & 3, s = f >> 2, row = 32 * kb + lr;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ (lr & 15))]);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Ks[row * 16 + ((2 * s + hi) ^ row_swz<SW>(lr))]);
       acc_s[kb] = mfma32(a, qf[s], acc_s[kb]);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -228,22 +264,31 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int drow = 32 * db + lr;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&Vs[drow * 16 + ((2 * s + hi) ^ (drow & 15))]);
+        bf16x8_t a;
+        if (VROW) {
+          typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(uintptr_t)(vrd[0][db] + 4096 * s));
+          const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)(uintptr_t)(vrd[1][db] + 4096 * s + 2048));
+          a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          const int drow = 32 * db + lr;
+          a = *reinterpret_cast<const bf16x8_t *>(&Vs[drow * 16 + ((2 * s + hi) ^ (drow & 15))]);
+        }
         acc_o[db] = mfma32(a, pb[s], acc_o[db]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // operand reads four MFMAs ahead
+    constexpr int NRD = VROW ? 2 : 1;  // LDS reads per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NRD, 0);  // operand reads four MFMAs ahead
 #pragma unroll
     for (int f = 0; f < 28; ++f) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     wait_lds();
     wait_vmem<0>();  // this wave's part of K(t+1) has landed
     barrier();       // every wave is done with V(t), and K(t+1) is complete
-    if (more) tile_to_lds(vh + (int64_t)jn * 32768, vs_lds, w, off);
+    if (more) tile_to_lds(v_tile(jn), vs_lds, w, voff);
   }
 
   const float l_tot = half_sum(l_run);
@@ -271,7 +316,7 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 }
 
 // fp32 path (d = 64, P = 64): one thread per query row, keys one at a time from LDS.
-template <bool RQ, bool RK>
+template <bool RQ, bool RK, int VM>
 __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ vt, const int32_t *__restrict__ kv_idx,
                                                       int kk, float scale, float *__restrict__ o,
@@ -303,7 +348,10 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
     for (int e = t; e < 64 * 64; e += 64) {
       const int r = e >> 6, c = e & 63;
       Ks[r][c] = k[at(RK, j * 64 + r, c)];  // row r = key, c = channel
-      Vs[cols_key(c)][r] = vt[head + ((int64_t)j * 64 + r) * 64 + c];  // channel-major: r = channel, c = position
+      if (VM == VM_COLS)
+        Vs[cols_key(c)][r] = vt[head + ((int64_t)j * 64 + r) * 64 + c];  // channel-major: r = channel, c = position
+      else
+        Vs[r][c] = vt[at(VM == VM_RAST, j * 64 + r, c)];
     }
     __syncthreads();
     for (int x = 0; x < 64; ++x) {
@@ -328,42 +376,60 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
   }
 }
 
-template <bool RQ, bool RK>
+template <bool RQ, bool RK, int VM>
 static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
                           const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
                           float *lse, hipStream_t st) {
   if (dt == VEDA_BF16) {
-    if (!RK && g.padded)  // padded tilings read K tiled (the C ABI refuses a raster K)
-      attn_bf16_kernel<RQ, false, true><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+    constexpr bool PADDABLE = !RK && VM != VM_RAST;  // padded tilings read K and V tiled (the C ABI checks)
+    if (PADDABLE && g.padded)
+      attn_bf16_kernel<RQ, false, PADDABLE, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
           rv);
     else
-      attn_bf16_kernel<RQ, RK, false><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
+      attn_bf16_kernel<RQ, RK, false, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
           rv);
   } else
-    attn_f32_kernel<RQ, RK><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
-                                                                 (const float *)v, kv_idx, kk, scale, (float *)o, lse,
-                                                                 g, hs, rv);
+    attn_f32_kernel<RQ, RK, VM><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
+                                                                     (const float *)v, kv_idx, kk, scale, (float *)o,
+                                                                     lse, g, hs, rv);
+}
+
+template <bool RQ, bool RK>
+static void launch_attn_v(int vm, const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt,
+                          const void *q, const void *k, const void *v, const int32_t *kv_idx, int kk, float scale,
+                          void *o, float *lse, hipStream_t st) {
+  if (vm == VM_COLS)
+    launch_attn_t<RQ, RK, VM_COLS>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+  else if (vm == VM_ROWS)
+    launch_attn_t<RQ, RK, VM_ROWS>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+  else if constexpr (RQ)  // a raster V comes only with raster Q (its strides)
+    launch_attn_t<RQ, RK, VM_RAST>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+}
+
+static int v_mode(veda_layout v_layout) {
+  return v_layout == VEDA_TILE_COLS ? VM_COLS : v_layout == VEDA_RASTER ? VM_RAST : VM_ROWS;
 }
 
 hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
-                              const void *v, const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
-                              hipStream_t st) {
-  launch_attn_t<false, false>(g, hs, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+                              const void *v, veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
+                              float *lse, hipStream_t st) {
+  launch_attn_v<false, false>(v_mode(v_layout), g, hs, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse,
+                              st);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                                      bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
-                                     const int32_t *kv_idx, int kk, float scale, void *o, float *lse,
-                                     hipStream_t st) {
+                                     veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
+                                     float *lse, hipStream_t st) {
   const int64_t eb = dt == VEDA_BF16 ? 2 : 4;
   const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
   if (k_raster)
-    launch_attn_t<true, true>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, true>(v_mode(v_layout), g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   else
-    launch_attn_t<true, false>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, false>(v_mode(v_layout), g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 

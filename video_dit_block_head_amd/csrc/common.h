@@ -265,21 +265,37 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t m
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0_addr) : "memory");
 }
 
+// Row swizzles of a 128 x 256-byte tile in LDS: 16-byte chunk c of row r sits at slot
+// c ^ swz(r).
+//  - SWZ_ROW, swz(r) = r & 15: sixteen consecutive rows read at one chunk (16-byte reads,
+//    one row per lane) hit sixteen different slots.
+//  - SWZ_QUAD, swz(r) = g(r & 3) ^ ((r >> 2) & 3) with g = {0, 10, 12, 6}: still a
+//    permutation of the sixteen slots over any sixteen aligned rows, and in addition, within
+//    every aligned quad of rows, bits 1-2 and bits 2-3 of swz take four different values.
+//    Transposed 8-byte reads of four rows x 32 or 64 contiguous bytes then fall on
+//    different banks (two or four chunks of each row side by side).
+enum { SWZ_ROW = 0, SWZ_QUAD = 1 };
+template <int SW>
+__host__ __device__ __forceinline__ int row_swz(int r) {
+  return SW == SWZ_ROW ? (r & 15) : (((0x6CA0 >> (4 * (r & 3))) & 15) ^ ((r >> 2) & 3));
+}
+
 // The calling wave copies rows [32w, 32w+32) of a 128 x 256-byte tile into LDS, 4 rows per
-// instruction; LDS slot (r, s) receives global chunk (r, s ^ (r & 15)).  off[e] is the
-// lane's byte offset in the tile for instruction e.
+// instruction; LDS slot (r, s) receives global chunk (r, s ^ swz(r)).  off[e] is the lane's
+// byte offset in the tile for instruction e.
 __device__ __forceinline__ void tile_to_lds(const char *src, uint32_t lds_base, int w, const uint32_t (&off)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) dma16(src, off[e], lds_base + (uint32_t)((32 * w + 4 * e) * 256));
 }
 
 // Per-lane byte offsets of tile_to_lds for wave w: instruction e covers rows 32w+4e .. +3,
-// lane -> (row 32w + 4e + lane/16, slot lane%16), source chunk slot ^ (row & 15).
+// lane -> (row 32w + 4e + lane/16, slot lane%16), source chunk slot ^ swz(row).
+template <int SW = SWZ_ROW>
 __device__ __forceinline__ void tile_dma_offsets(int w, int lane, uint32_t (&off)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int r = 32 * w + 4 * e + (lane >> 4);
-    off[e] = (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+    off[e] = (uint32_t)(r * 256 + (((lane & 15) ^ row_swz<SW>(r)) << 4));
   }
 }
 
@@ -287,12 +303,13 @@ __device__ __forceinline__ void tile_dma_offsets(int w, int lane, uint32_t (&off
 // from the tile's origin, so the per-lane offsets are those of tile_dma_offsets with the
 // row's byte offset replaced by intra(row) * (token stride); the tile's origin goes into
 // the scalar base address.  Offsets stay below 4 GiB for every supported grid.
+template <int SW = SWZ_ROW>
 __device__ __forceinline__ void tile_dma_offsets_raster(int w, int lane, int ph, int pw, int Hs, int Ws,
                                                         int64_t sn, uint32_t (&off)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int r = 32 * w + 4 * e + (lane >> 4);
-    const int chunk = (lane & 15) ^ (r & 15);
+    const int chunk = (lane & 15) ^ row_swz<SW>(r);
     off[e] = (uint32_t)((int64_t)tile_intra(r, ph, pw, Hs, Ws) * sn + chunk * 16);
   }
 }

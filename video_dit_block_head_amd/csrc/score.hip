@@ -11,7 +11,10 @@
 //                    CU, so other workgroups' streaming overlaps one's MFMA work.  For the
 //                    distillation step it can take a list of Q tiles and also keep the
 //                    pre-activation hidden layer.  Reading a raster K, it can also write
-//                    K's tile-major copy as it streams it (the K gather fused into pooling).
+//                    K's tile-major copy as it streams it (the K gather fused into pooling),
+//                    and with raster Q, workgroups of a third kind stream a raster V into
+//                    its tile-major copy (the V gather in the same launch, filling the HBM
+//                    time that the others spend in the MLP).
 //  score_topk_kernel 16 query-tile rows per workgroup: S = y_q y_k^T on fp32 MFMA
 //                    (v_mfma_f32_16x16x4f32) into an LDS row block, then one wave per row
 //                    for softmax and top-k (ballot/popcount; deterministic); 4, 8 or 16
@@ -52,24 +55,29 @@ static constexpr int PM_HST = 260;    // hidden block row stride (floats)
 // RQ (RK): Q (K) is a raster [B, N, H, d] tensor (byte strides in rv) read through each
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
 // PAD: padded tiling: per-head tile counts, partial tiles (their real rows only).
+// vout (RQ only, else null): the items are (b, h, Q|K|V, group), and a V item copies its 32
+// tiles of the raster V vsrc (strides of Q) to their tile-major place in vout, as the K
+// items write kout (zero rows where the tiling has no token), and does nothing else.
 template <int EB, bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
                 float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, float *__restrict__ zout,
                 const int32_t *__restrict__ qlist, int nlist, Geo g, HeadShapes hs, RasterView rv,
-                uint8_t *__restrict__ kout) {
+                uint8_t *__restrict__ kout, const uint8_t *__restrict__ vsrc, uint8_t *__restrict__ vout) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
   constexpr int D3 = 3 * D;
   constexpr int PF = 8;                   // weight prefetch distance (MFMA steps)
-  // Items ordered (b, h, Q|K, group); each XCD walks a contiguous range, so the workgroups
-  // that share a head's weights share that XCD's L2.
+  // Items ordered (b, h, Q|K[|V], group); each XCD walks a contiguous range, so the
+  // workgroups that share a head's weights share that XCD's L2.
   const int ngrp = (g.nt + PM_ROWS - 1) / PM_ROWS;
+  const int nwh = (RQ && vout != nullptr) ? 3 : 2;
   const int L = xcd_tile(blockIdx.x, gridDim.x);
-  const int r0 = (L % ngrp) * PM_ROWS, which = (L / ngrp) & 1, h = (L / (2 * ngrp)) % g.H,
-            b = L / (2 * ngrp * g.H);
+  const int r0 = (L % ngrp) * PM_ROWS, which = (L / ngrp) % nwh, h = (L / (nwh * ngrp)) % g.H,
+            b = L / (nwh * ngrp * g.H);
+  const bool vcopy = which == 2;  // uniform: a V item (copy only)
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
   __shared__ float Ds[PM_ROWS * PM_DS];   // descriptors, then the hidden layer
@@ -77,15 +85,16 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
   // ---- TripPool: lane (rg = lane/16, c = lane%16) accumulates rows rg, rg + 4, ... of its
   // 16-byte channel chunk c; the 4 row groups are combined as (g0 + g1) + (g2 + g3).
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
-  const bool rast = which ? RK : RQ;  // uniform over the workgroup
+  const bool rast = which == 0 ? RQ : (which == 1 ? RK : true);  // uniform over the workgroup
   const int nth = PAD ? head_tiles(pt, ph, pw, g.T, g.Hs, g.Ws) : g.nt;  // this head's tiles
   // With a query-tile list, the Q rows are its entries (row r pools tile qlist[b, h, r]) and
   // there are nlist of them; groups past the list have nothing to do.
   const bool listed = qlist != nullptr && which == 0;
   if (listed && r0 >= nlist) return;  // whole workgroup, before any barrier
   const int32_t *qrow = listed ? qlist + ((int64_t)b * g.H + h) * nlist : nullptr;
-  const uint8_t *src0 = rast ? (which ? k : q) + (int64_t)b * rv.sb + (int64_t)h * rv.sh
-                             : (which ? k : q) + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
+  const uint8_t *base = which == 0 ? q : (which == 1 ? k : vsrc);
+  const uint8_t *src0 = rast ? base + (int64_t)b * rv.sb + (int64_t)h * rv.sh
+                             : base + ((int64_t)b * g.H + h) * (int64_t)g.N * D * EB;
   const int rg = lane >> 4, c = lane & 15;
 #pragma unroll 1
   for (int tt = 0; tt < 8; ++tt) {
@@ -120,10 +129,11 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
         mn[e] = fminf(mn[e], x[e]);
       }
     };
-    // K's tile-major copy, if asked for (raster K only): rows as loaded; zero rows for the
-    // padding rows of a partial tile and for the tiles past this head's own count
-    uint8_t *kdst = (RK && which && kout != nullptr)
-                        ? kout + ((int64_t)b * g.H + h) * (int64_t)g.N * 256 + (int64_t)j * P * 256 + c * 16
+    // K's (raster K only) or V's tile-major copy, if asked for: rows as loaded; zero rows
+    // for the padding rows of a partial tile and for the tiles past this head's own count
+    uint8_t *cdst = (RK && which == 1) ? kout : (vcopy ? vout : nullptr);
+    uint8_t *kdst = cdst != nullptr
+                        ? cdst + ((int64_t)b * g.H + h) * (int64_t)g.N * 256 + (int64_t)j * P * 256 + c * 16
                         : nullptr;
     if (j < nth && PAD && box_rows(bx) < P) {
       // a partial tile of a padded tiling: its real rows, one at a time (raster rows at
@@ -136,7 +146,7 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
         if (in_box(o, ph, pw, bx)) {
           const int64_t ro = rast ? (int64_t)tile_intra(o, ph, pw, g.Hs, g.Ws) * rstride : (int64_t)o * 256;
           const uint4 v = load_stream16(src + ro);
-          accum(v);
+          if (!vcopy) accum(v);
           if (kdst != nullptr) store_stream16(kdst + o * 256, v);
         } else if (kdst != nullptr) {
           store_stream16(kdst + o * 256, make_uint4(0u, 0u, 0u, 0u));
@@ -165,10 +175,13 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
 #pragma unroll
           for (int i = 0; i < NL; ++i) v[i] = load_stream16(src + (rg + 4 * (NL * part + i)) * 256);
         }
+        if (!vcopy) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) accum(v[i]);
+          for (int i = 0; i < NL; ++i) accum(v[i]);
+        }
       }
     }
+    if (vcopy) continue;  // a V item only copies
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       s[e] += __shfl_xor(s[e], 16);
@@ -190,6 +203,7 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
       }
     }
   }
+  if (vcopy) return;  // whole workgroup, before any barrier
   __syncthreads();
   float *dout = which ? kdesc : qdesc;
   if (dout != nullptr) {
@@ -435,39 +449,46 @@ template <int EB, bool RQ, bool RK>
 static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
                               float *q_desc, float *k_desc, float *z, const int32_t *qlist, int nlist,
-                              uint8_t *kout, hipStream_t st) {
-  const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * 2 * g.B);
+                              uint8_t *kout, const uint8_t *vsrc, uint8_t *vout, hipStream_t st) {
+  if (!RQ) vout = nullptr;  // a V copy comes only with raster Q (its strides)
+  const int nwh = vout != nullptr ? 3 : 2;
+  const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * nwh * g.B);
   if (g.padded)
     pool_mlp_kernel<EB, RQ, RK, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
-                                                          y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout);
+                                                          y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout, vsrc,
+                                                          vout);
   else
     pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
-                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout);
+                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout, vsrc,
+                                                           vout);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
-                           bool k_raster, float *z, const int32_t *qlist, int nlist, void *k_tiled_out) {
+                           bool k_raster, float *z, const int32_t *qlist, int nlist, void *k_tiled_out,
+                           const void *v_raster, void *v_tiled_out) {
   uint8_t *kout = static_cast<uint8_t *>(k_tiled_out);
+  const uint8_t *vsrc = static_cast<const uint8_t *>(v_raster);
+  uint8_t *vout = static_cast<uint8_t *>(v_tiled_out);
   const HeadShapes hs0 = hs != nullptr ? *hs : HeadShapes{};  // tiled operands: shapes matter only when padded
   const RasterView rv0{0, 0, 0};
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
     if (bf)
-      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
     else
-      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
   } else if (k_raster) {
     if (bf)
-      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
     else
-      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
   } else {
     if (bf)
-      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
     else
-      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, st);
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
   }
   return hipGetLastError();
 }
@@ -476,13 +497,13 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st, const HeadShapes *hs, const RasterView *rv, bool k_raster,
-                        void *k_tiled_out) {
+                        void *k_tiled_out, const void *v_raster, void *v_tiled_out) {
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
   const HeadShapes hsv = hs != nullptr ? *hs : HeadShapes{};
   const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster,
-                                        nullptr, nullptr, 0, k_tiled_out);
+                                        nullptr, nullptr, 0, k_tiled_out, v_raster, v_tiled_out);
   if (pe != hipSuccess) return pe;
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, hsv, st);

@@ -8,7 +8,7 @@ import math
 
 import torch
 
-from . import (COLS, RASTER, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
+from . import (RASTER, ROWS, Geom, veda_distill_step, veda_distill_workspace_bytes, veda_head_sq_error,
                veda_head_sq_error_workspace_bytes,
                veda_oracle_tilemap, veda_oracle_tilemap_raster, veda_oracle_tilemap_workspace_bytes,
                veda_sparse_attn_fwd, veda_sparse_attn_fwd_raster, veda_tile_gather, veda_trippool_score,
@@ -31,7 +31,7 @@ class SparseAttention:
         shape = (g.batch, g.heads, g.n_tiled, g.head_dim)   # n_tiled = n_tokens unless the tiling is padded
         self.q_t = torch.empty(shape, dtype=dtype, device=device)
         self.k_t = torch.empty(shape, dtype=dtype, device=device)
-        self.v_t = torch.empty(shape, dtype=dtype, device=device)   # COLS layout, same size
+        self.v_t = torch.empty(shape, dtype=dtype, device=device)   # tile-major (ROWS), like q_t and k_t
         self.o_t = torch.empty(shape, dtype=dtype, device=device)
         nbytes = veda_trippool_workspace_bytes(g, self.w1.shape[-1], self.w2.shape[-1])
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -48,7 +48,7 @@ class SparseAttention:
         """q, k, v: [B, N, H, d] (last dim contiguous)."""
         veda_tile_gather(self.geom, q, self.q_t, ROWS)
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
-        veda_tile_gather(self.geom, v, self.v_t, COLS)
+        veda_tile_gather(self.geom, v, self.v_t, ROWS)
 
     def score(self, topk, scores=None, probs=None, q_desc=None, k_desc=None):
         idx = self.idx_buffer(topk) if topk > 0 else None
@@ -59,7 +59,7 @@ class SparseAttention:
 
     def attend(self, idx, lse=None):
         veda_sparse_attn_fwd(self.geom, self.q_t, self.k_t, self.v_t, idx, int(idx.shape[-1]),
-                             self.softmax_scale, self.o_t, lse)
+                             self.softmax_scale, self.o_t, lse, v_layout=ROWS)
         return self.o_t
 
     def scatter(self, out):
@@ -94,31 +94,35 @@ class SparseAttention:
         return loss, dw1, dw2
 
     # ---- raster-direct path: Q and O stay in the raster layout.  K is read raster (pass k)
-    # or from its tiled copy (k=None: gather_kv first); V is always tiled.
+    # or from its tiled copy (k=None: gather_kv first, or the scoring pass with tile_k); V
+    # from its tiled copy (gather_kv, gather_v, or the scoring pass given v).
     def gather_kv(self, k, v):
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
-        veda_tile_gather(self.geom, v, self.v_t, COLS)
+        veda_tile_gather(self.geom, v, self.v_t, ROWS)
 
     def gather_v(self, v):
-        veda_tile_gather(self.geom, v, self.v_t, COLS)
+        veda_tile_gather(self.geom, v, self.v_t, ROWS)
 
     def _k(self, k):
         return (self.k_t, ROWS) if k is None else (k, RASTER)
 
-    def score_raster(self, q, topk, k=None, scores=None, probs=None, q_desc=None, k_desc=None, tile_k=False):
+    def score_raster(self, q, topk, k=None, scores=None, probs=None, q_desc=None, k_desc=None, tile_k=False,
+                     v=None):
         """Scoring on raster Q; K raster (k given) or its tiled copy.  tile_k (raster K only):
-        also write K's tiled copy while pooling it, in place of gather_kv's K gather."""
+        also write K's tiled copy while pooling it, in place of gather_kv's K gather; v (raster,
+        strides of q): the same launch also writes V's tiled copy, in place of gather_v."""
         idx = self.idx_buffer(topk) if topk > 0 else None
         kt, lay = self._k(k)
         veda_trippool_score_raster(self.geom, q, kt, self.w1, self.w2, self.w1_k, self.w2_k, self.score_scale,
                                    scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc, topk=topk, idx=idx,
-                                   workspace=self.ws, k_layout=lay, k_tiled_out=self.k_t if tile_k else None)
+                                   workspace=self.ws, k_layout=lay, k_tiled_out=self.k_t if tile_k else None,
+                                   v=v, v_tiled_out=None if v is None else self.v_t)
         return idx
 
     def attend_raster(self, q, idx, out, lse=None, k=None):
         kt, lay = self._k(k)
         veda_sparse_attn_fwd_raster(self.geom, q, kt, self.v_t, idx, int(idx.shape[-1]), self.softmax_scale, out,
-                                    lse, k_layout=lay)
+                                    lse, k_layout=lay, v_layout=ROWS)
         return out
 
     def tilemap_raster(self, q, q_tiles, n_sel, out, lse=None, k=None):
@@ -131,10 +135,9 @@ class SparseAttention:
         return out
 
     def forward_raster(self, q, k, v, topk, out):
-        """Same result as forward(), without the tiled copies of Q and O; K is tiled by the
-        scoring pass as it reads it, V by the gather."""
-        self.gather_v(v)
-        idx = self.score_raster(q, topk, k=k, tile_k=True)
+        """Same result as forward(), without the tiled copies of Q and O; the scoring launch
+        tiles K as it pools it and streams V into its tiled copy beside."""
+        idx = self.score_raster(q, topk, k=k, tile_k=True, v=v)
         return self.attend_raster(q, idx, out)
 
     def forward(self, q, k, v, topk, out):
