@@ -386,8 +386,24 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     score_p_ms = e0.elapsed_time(e1) / 10
-    score_p_bytes = score_bytes + B * H * nt * nt * 4
+    score_p_bytes = alone_bytes + B * H * nt * nt * 4   # the call alone, plus the probabilities
     del probs
+
+    # the step's attention with V in each layout the kernel reads (bit-identical outputs):
+    # tile-major rows (the default, copied by the scoring launch), channel-major tiles, and
+    # the raster tensor itself
+    v_layouts = None
+    if args.path != "tiled":
+        v_cols = torch.empty_like(sa.v_t)
+        V.veda_tile_gather(geom, v, v_cols, V.COLS)
+        o2 = torch.empty_like(out)
+        v_layouts = {}
+        for name, vop, lay in (("rows", sa.v_t, V.ROWS), ("cols", v_cols, V.COLS), ("raster", v, V.RASTER)):
+            ms = timed(lambda: V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, vop, sa.idx_buffer(kk), kk,
+                                                             sa.softmax_scale, o2, k_layout=V.ROWS, v_layout=lay), 5)
+            v_layouts[f"{name}_ms"] = round(ms, 3)
+        v_layouts["note"] = "attention alone with raster Q and O, tiled K, 5 calls each after the timed steps"
+        del v_cols, o2
 
     # this library's own dense path (k = n_t, 0 % skipping), for the speedup
     dense = None
@@ -557,6 +573,7 @@ def main():
         "tile_recall": {"value": round(recall, 4), "k": kk, "sampled_query_tiles_per_head": n_sel,
                         "chance": round(kk / nt, 4),
                         "note": "estimator with the synthetic (untrained) MLP weights against the oracle mask"},
+        "attention_v_layouts": v_layouts,
         "dense": dense,
         "next_rows": nxt,
         "long_workload": long_row,
