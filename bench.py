@@ -397,12 +397,14 @@ def main():
         v_cols = torch.empty_like(sa.v_t)
         V.veda_tile_gather(geom, v, v_cols, V.COLS)
         o2 = torch.empty_like(out)
-        v_layouts = {}
-        for name, vop, lay in (("rows", sa.v_t, V.ROWS), ("cols", v_cols, V.COLS), ("raster", v, V.RASTER)):
-            ms = timed(lambda: V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, vop, sa.idx_buffer(kk), kk,
-                                                             sa.softmax_scale, o2, k_layout=V.ROWS, v_layout=lay), 5)
-            v_layouts[f"{name}_ms"] = round(ms, 3)
-        v_layouts["note"] = "attention alone with raster Q and O, tiled K, 5 calls each after the timed steps"
+        runs = {"rows": [], "cols": [], "raster": []}
+        for _ in range(3):   # interleaved rounds: the layouts see the same clock drift
+            for name, vop, lay in (("rows", sa.v_t, V.ROWS), ("cols", v_cols, V.COLS), ("raster", v, V.RASTER)):
+                runs[name].append(timed(lambda: V.veda_sparse_attn_fwd_raster(
+                    geom, q, sa.k_t, vop, sa.idx_buffer(kk), kk, sa.softmax_scale, o2, k_layout=V.ROWS, v_layout=lay), 3))
+        v_layouts = {f"{name}_ms": round(float(np.median(t)), 3) for name, t in runs.items()}
+        v_layouts["note"] = ("attention alone with raster Q and O, tiled K; median of three interleaved rounds of "
+                             "3 calls per layout, after the timed steps")
         del v_cols, o2
 
     # this library's own dense path (k = n_t, 0 % skipping), for the speedup
