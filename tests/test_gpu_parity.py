@@ -404,7 +404,8 @@ def small_geom_case(batch, grid, shapes, seed=7):
 
 
 def test_batch_and_edge_k():
-    """batch > 1, k = 1 and k = n_t, on a 4x8x16 grid with three tile shapes."""
+    """batch > 1, k = 1 and k = n_t, on a 4x8x16 grid with three tile shapes, against the
+    oracle; and the default raster path against the tiled one on the same batches."""
     shapes = [(1, 8, 16), (2, 8, 8), (4, 4, 8)]
     geom, (q, k, v) = small_geom_case(2, (4, 8, 16), shapes)
     rng = np.random.default_rng(3)
@@ -432,6 +433,15 @@ def test_batch_and_edge_k():
                 got = host(sa.o_t[b, h])
                 assert np.abs(got - ref).max() <= 2e-2
                 assert math.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 1e-2
+        # the default raster path (K and V tiled by the scoring launch) on two batches: the
+        # same lists and, bit for bit, the same output as the tiled path just checked
+        out_t, out_r = torch.empty_like(q), torch.empty_like(q)
+        sa.scatter(out_t)
+        idx_t = idx.clone()
+        sa.forward_raster(q, k, v, kk, out_r)
+        torch.cuda.synchronize()
+        assert torch.equal(sa.idx_buffer(kk), idx_t), kk
+        assert torch.equal(out_r.view(torch.int16), out_t.view(torch.int16)), kk
 
 
 def test_strided_raster_gather():
