@@ -557,6 +557,8 @@ def main():
                    "batch": B, "heads": H, "seq_len": N, "head_dim": d, "tile": P, "topk": kk, "n_tiles": nt,
                    "tile_shapes": sorted(set(wl.shapes)), "tilemap_query_tiles_per_head": n_sel},
         "sparse_attn_ms_per_call": round(attn_ms, 4),
+        "sparse_attn_ms_median_min": [round(float(np.median(per_stage["sparse_attn"])), 4),
+                                      round(float(np.min(per_stage["sparse_attn"])), 4)],
         "sparse_attn_tflops": round(attn_tflops, 1),
         "sparse_attn_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "scoring_ms": round(score_ms, 4),
