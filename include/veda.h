@@ -94,8 +94,9 @@ typedef enum { VEDA_TILE_ROWS = 0, VEDA_TILE_COLS = 1, VEDA_RASTER = 2 } veda_la
 /* Problem geometry.  [Technical Summary §2.2: the per-(layer, head) tiling
  * pi = (p_t, p_h, p_w) factorises the hardware tile.] */
 typedef struct {
-  int32_t batch, heads, head_dim;  /* B, H (<= VEDA_MAX_HEADS), d */
-  int32_t t, h, w;                 /* latent grid */
+  int32_t batch, heads, head_dim;  /* B, H (<= VEDA_MAX_HEADS), d; all >= 1 */
+  int32_t t, h, w;                 /* latent grid, each >= 1, t*h*w <= 2^30 (an empty
+                                      problem is VEDA_ERR_SHAPE, not a no-op) */
   int32_t tile;                    /* P tokens per tile */
   const int32_t *tile_shapes;      /* HOST int32[heads][3] (p_t, p_h, p_w); each product
                                       == tile; a shape that does not divide (t, h, w)

@@ -57,6 +57,19 @@ def gather(L, g, dt=V.BF16, raster=A, tiled=B_, strides=(4096 * 2 * 128, 2 * 128
     return L.veda_tile_gather(g.ref if g is not None else None, dt, raster, *strides, tiled, layout, inverse, None)
 
 
+def test_empty_geometries_are_refused(L):
+    """An empty batch, head set or grid is a shape error on every geometry-taking call,
+    returned before anything is launched (the top-k call alone takes rows = 0 as nothing to do)."""
+    for kw in (dict(batch=0), dict(heads=0, shapes=((2, 8, 8),))):
+        g = geom(**kw)
+        assert L.veda_tiled_tokens(g.ref, V.BF16) == SHAPE
+        assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.ROWS, A, 1, 0.088, A, None, None) == SHAPE
+        assert gather(L, g) == SHAPE
+    g = geom(grid=(0, 16, 32))
+    assert L.veda_tiled_tokens(g.ref, V.BF16) == SHAPE
+    assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, 0.088, A, 1, A, None, A, 1 << 40, None) == SHAPE
+
+
 def test_padded_tile_counts(L):
     """Tiles per head on the grid padded up to whole tiles, and the tiled rows per head."""
     g = geom(grid=(20, 48, 80), shapes=((8, 4, 4), (2, 8, 8), (1, 8, 16)))
