@@ -202,16 +202,19 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
  * [Technical Summary §2.3 and the paper's future work on fusing the tiling into the
  * kernels]  They compute exactly what veda_trippool_score, veda_sparse_attn_fwd and
  * veda_oracle_tilemap compute (bit for bit), but read Q (and write O) in the raster layout
- * [B, N, H, d] with element strides rs_b, rs_n, rs_h (d contiguous, 16-byte aligned rows
- * and strides), going through each head's tiling in the kernels: row r of tile j of head h
+ * [B, N, H, d] with element strides rs_b, rs_n, rs_h for Q (os_b, os_n, os_h for O; d
+ * contiguous, 16-byte aligned rows and strides), going through each head's tiling in the
+ * kernels: row r of tile j of head h
  * is raster token origin_h(j) + intra_h(r).  k_layout says where K is: VEDA_RASTER (with
  * the same strides as Q) or VEDA_TILE_ROWS (tile-major [B, H, N, d], from
  * veda_tile_gather; K tiles are then contiguous 32 KB copies, which the attention and
  * tile-map kernels prefer).  veda_sparse_attn_fwd_raster takes V as VEDA_TILE_ROWS,
  * VEDA_TILE_COLS or VEDA_RASTER (v_layout; a raster V has the strides of Q and is read
  * through the tiling like a raster K, bit-identical but slower than a tiled V, whose tiles
- * are contiguous 32 KB copies).  The output of veda_sparse_attn_fwd_raster is raster (same
- * strides) and its lse is [B, H, t*h*w] in raster token order; the tile-map lse keeps its
+ * are contiguous 32 KB copies).  The output of veda_sparse_attn_fwd_raster is raster
+ * [B, N, H, d] with its own element strides os_b, os_n, os_h (checked as rs_*; e.g. Q, K
+ * and V views of one packed QKV tensor and a separate contiguous O) and its lse is
+ * [B, H, t*h*w] in raster token order; the tile-map lse keeps its
  * [B, H, n_sel * P] tile-row order.  Extra status: VEDA_ERR_UNSUPPORTED if an in-tile
  * token offset times the token stride reaches 2^31 bytes.  Other arguments, outputs and
  * workspaces as in the tiled calls.
@@ -234,8 +237,8 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                         veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                         const void *v, veda_layout v_layout, const int32_t *kv_idx,
-                                        int32_t k_kept,
-                                        float softmax_scale, void *o_raster, float *lse, hipStream_t stream);
+                                        int32_t k_kept, float softmax_scale, void *o_raster, int64_t os_b,
+                                        int64_t os_n, int64_t os_h, float *lse, hipStream_t stream);
 veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,

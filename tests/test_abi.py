@@ -93,9 +93,9 @@ def test_padded_rejected_where_unsupported(L):
     n_t = g.n_tiles                                           # 3 * 4 * 8 = 96 > 80 (dividing head)
     st = (g.n_tokens * 2 * 128, 2 * 128, 128)
     RAS, big = V.RASTER, 1 << 40
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, 4, 0.088, A, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, 4, 0.088, A, *st, None,
                                          None) == UNSUP
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, RAS, A, 4, 0.088, A, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, RAS, A, 4, 0.088, A, *st, None,
                                          None) == UNSUP                      # a raster V, likewise
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, RAS, *st, 0.088, A, 4, A, None, A, big, None) == UNSUP
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, None, n_t, A, None, A, big,
@@ -103,7 +103,7 @@ def test_padded_rejected_where_unsupported(L):
     assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, 0.088, None, n_t, A, None, A, big, None) == SHAPE
     # k may not exceed the smallest per-head tile count (80 here), on every path
     assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.COLS, A, 81, 0.088, A, None, None) == SHAPE
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, V.COLS, A, 81, 0.088, A, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, V.COLS, A, 81, 0.088, A, *st, None,
                                          None) == SHAPE
     assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, 81, A, A,
                                  big, None) == SHAPE
@@ -183,7 +183,7 @@ def test_attn_v_layout_validation(L):
     assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.RASTER, A, 4, 0.088, A, None, None) == UNSUP
     assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, 7, A, 4, 0.088, A, None, None) == SHAPE
     st = (4096 * 2 * 128, 2 * 128, 128)
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, 7, A, 4, 0.088, A, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, 7, A, 4, 0.088, A, *st, None,
                                          None) == SHAPE
 
 
@@ -244,13 +244,18 @@ def test_raster_validation(L):
     st = (4096 * 2 * 128, 2 * 128, 128)
     RAS = V.RASTER
     C = V.COLS
-    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, C, A, 4, 0.088, A, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, None, RAS, *st, A, C, A, 4, 0.088, A, None, None) == NULL
-    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, C, A, 4, 0.088, A, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, C, A, 4, 0.088, A, None, None) == SHAPE   # K layout
-    # in-tile token offset x token stride beyond 2^31 bytes
+    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, C, A, 4, 0.088, A, *st, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, None, RAS, *st, A, C, A, 4, 0.088, A, *st, None, None) == NULL
+    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, C, A, 4, 0.088, A, *st, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, C, A, 4, 0.088, A, *st, None, None) == SHAPE   # K layout
+    # O has strides of its own, checked like Q's
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, 4, 0.088, A, 4096 * 256, 260, 128, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, 4, 0.088, A, -1, 256, 128, None, None) == SHAPE
+    # in-tile token offset x token stride beyond 2^31 bytes (Q's or O's)
     assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, C, A, 4,
-             0.088, A, None, None) == UNSUP
+             0.088, A, *st, None, None) == UNSUP
+    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, *st, A, C, A, 4,
+             0.088, A, 0, 1 << 20, 128, None, None) == UNSUP
     s = L.veda_trippool_score_raster
     assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None, None,
              None, A, 1 << 30, None) == NULL

@@ -1,7 +1,9 @@
 """The library as a DiT block would call it, on one MI355X.
 
 - A fused QKV projection emits one [B, N, 3, H, d] tensor; the raster calls take Q, K and V as
-  strided views of it (token stride 3*H*d) and give bit for bit what contiguous copies give.
+  strided views of it (token stride 3*H*d) and give bit for bit what contiguous copies give,
+  with the output a view of a packed tensor as well, a contiguous tensor, or head-major
+  storage (the output has strides of its own).
 - The default step (scoring through the no-allocation call, its launch also writing K's and
   V's tiled copies; attention and tile map with raster Q and O) captured into a HIP graph:
   every replay, with eager work and synchronisations between them, gives the eager step's
@@ -57,6 +59,16 @@ def test_packed_qkv_views(name):
     assert torch.equal(sa.idx_buffer(kk), idx_ref), name
     assert torch.equal(bits(ov), bits(ref)), name
     assert not out_packed[:, :, 1:].any(), "the output view wrote outside its slots"
+    # the output with strides of its own: a contiguous [B, N, H, d] tensor, and a head-major
+    # [B, H, N, d] storage seen as [B, N, H, d]
+    out_c = torch.zeros_like(ref)
+    sa.forward_raster(qv, kv_, vv, kk, out_c)
+    hm = torch.zeros((q.shape[0], q.shape[2], q.shape[1], q.shape[3]), dtype=q.dtype, device="cuda")
+    out_h = hm.permute(0, 2, 1, 3)
+    assert out_h.stride(1) != ov.stride(1) and out_h.stride(2) != ov.stride(2)
+    sa.forward_raster(qv, kv_, vv, kk, out_h)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out_c), bits(ref)) and torch.equal(bits(out_h), bits(ref)), name
 
 
 def test_graph_capture_noalloc_step():

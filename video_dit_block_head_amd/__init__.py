@@ -103,7 +103,7 @@ def lib():
             "veda_trippool_score_raster_noalloc": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32,
                                                          i32, f32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
             "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
-                                                  vp, vp]),
+                                                  i64, i64, i64, vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
                                                  vp]),
             "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
@@ -457,20 +457,21 @@ def veda_sparse_attn_fwd_raster(geom, q, k, v, kv_idx, kk, softmax_scale, o, lse
                                 v_layout=ROWS, stream=None):
     """veda_sparse_attn_fwd with raster Q and output O [B, N, H, d]; K raster or tile-major
     (k_layout=ROWS); V channel-major tiled (COLS), tile-major (ROWS) or raster (RASTER, with
-    the strides of Q and O); lse [B, H, N] in raster token order."""
+    the strides of Q); O with strides of its own; lse [B, H, N] in raster token order."""
     dt = _elem_dtype(q)
     if v_layout == RASTER:
-        rs, kp = _k_operand(geom, q, k, k_layout, o, v)
+        rs, kp = _k_operand(geom, q, k, k_layout, v)
         vp = _raster(geom, v, "v", dt)
     elif v_layout in (COLS, ROWS):
-        rs, kp = _k_operand(geom, q, k, k_layout, o)
+        rs, kp = _k_operand(geom, q, k, k_layout)
         vp = _p(v, "v", True, dt, _tiled_numel(geom))
     else:
         raise VedaError("v_layout must be COLS, ROWS or RASTER")
+    op = _raster(geom, o, "o", dt)
     _call("veda_sparse_attn_fwd_raster",
         geom.ref, _dtype_code(q), _raster(geom, q, "q", dt), kp, int(k_layout), *rs,
         vp, int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
-        float(softmax_scale), _raster(geom, o, "o", dt),
+        float(softmax_scale), op, *_raster_strides(o),
         _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tokens), _stream(stream))
 
 

@@ -309,7 +309,8 @@ veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, co
                                         const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
                                         int64_t rs_h,
                                         const void *v, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
-                                        float softmax_scale, void *o_raster, float *lse, hipStream_t stream) {
+                                        float softmax_scale, void *o_raster, int64_t os_b, int64_t os_n,
+                                        int64_t os_h, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
@@ -323,10 +324,12 @@ veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, co
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
   if (v_layout != VEDA_RASTER && v_layout != VEDA_TILE_ROWS && v_layout != VEDA_TILE_COLS) return VEDA_ERR_SHAPE;
   if ((s = check_raster(geo, hs, dtype, rs_b, rs_n, rs_h)) != VEDA_OK) return s;
+  if ((s = check_raster(geo, hs, dtype, os_b, os_n, os_h)) != VEDA_OK) return s;
   // padded tilings: K and V tiled (the copies read whole tiles)
   if (geo.padded && (k_layout != VEDA_TILE_ROWS || v_layout == VEDA_RASTER)) return VEDA_ERR_UNSUPPORTED;
   return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
-                                              rs_h, v, v_layout, kv_idx, k, softmax_scale, o_raster, lse, stream));
+                                              rs_h, v, v_layout, kv_idx, k, softmax_scale, o_raster, os_b, os_n, os_h,
+                                              lse, stream));
 }
 
 size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {

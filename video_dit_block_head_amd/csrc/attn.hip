@@ -58,9 +58,9 @@ __device__ __forceinline__ float half_sum(float v) {
 // V layouts of the attention kernels: channel-major tiles, tile-major rows, raster.
 enum { VM_COLS = 0, VM_ROWS = 1, VM_RAST = 2 };
 
-// RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv) read and written through
-// the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in raster
-// order; RK: the same for K.  Otherwise tile-major.  VM: V's layout (VM_RAST with the
+// RQ: Q and O are raster [B, N, H, d] tensors (byte strides in rv and ro) read and written
+// through the head's tiling (token of row r of tile j = origin(j) + intra(r)), and LSE is in
+// raster order; RK: the same for K (strides rv).  Otherwise tile-major.  VM: V's layout (VM_RAST with the
 // strides of Q).  PAD: padded tiling: per-head tile counts and partial key tiles (K and V
 // tiled); with RQ the padding query rows of a partial query tile are neither read (Q taken
 // as zero, as the gather stores it) nor written.
@@ -68,7 +68,7 @@ template <bool RQ, bool RK, bool PAD, int VM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
                  const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
-                 float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv) {
+                 float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv, RasterView ro) {
   constexpr bool VROW = VM != VM_COLS;          // V read with transposed reads
   constexpr int SW = VROW ? SWZ_QUAD : SWZ_ROW;  // swizzle of both LDS tiles
   const int L = xcd_tile(blockIdx.x, gridDim.x);
@@ -293,7 +293,8 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
 
   const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
-  __bf16 *orow = RQ ? reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(o) + rhead + qtok * rv.sn)
+  __bf16 *orow = RQ ? reinterpret_cast<__bf16 *>(reinterpret_cast<char *>(o) + (int64_t)bb * ro.sb +
+                                                   (int64_t)hh * ro.sh + qtok * ro.sn)
                     : o + head + (int64_t)qrow * 128;
   if (qreal) {
 #pragma unroll
@@ -320,18 +321,20 @@ template <bool RQ, bool RK, int VM>
 __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ vt, const int32_t *__restrict__ kv_idx,
                                                       int kk, float scale, float *__restrict__ o,
-                                                      float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv) {
+                                                      float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv,
+                                                      RasterView ro) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t head = ((int64_t)b * g.H + h) * (int64_t)g.N * 64;
   const int32_t *list = kv_idx + (((int64_t)b * g.H + h) * g.nt + i) * kk;
   const int pt = hs.s[h][0], ph = hs.s[h][1], pw = hs.s[h][2];
-  const int64_t rhead = (int64_t)b * rv.sb + (int64_t)h * rv.sh;  // raster bytes of (b, 0, h)
-  // element index of (tiled row, channel) of Q/O (raster if RQ) or K (raster if RK)
-  auto at = [&](bool raster, int row, int c) -> int64_t {
+  // element index of (tiled row, channel) of Q or K (raster if RQ / RK, strides rv), or of
+  // O (raster if RQ, strides ro)
+  auto at_v = [&](bool raster, const RasterView &r, int row, int c) -> int64_t {
     if (!raster) return head + (int64_t)row * 64 + c;
     const int64_t tok = tile_origin(row / 64, pt, ph, pw, g.Hs, g.Ws) + tile_intra(row % 64, ph, pw, g.Hs, g.Ws);
-    return (rhead + tok * rv.sn) / 4 + c;
+    return ((int64_t)b * r.sb + (int64_t)h * r.sh + tok * r.sn) / 4 + c;
   };
+  auto at = [&](bool raster, int row, int c) -> int64_t { return at_v(raster, rv, row, c); };
   const int qrow = i * 64 + t;
   float qr[64], acc[64];
 #pragma unroll
@@ -369,7 +372,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
   }
   const float inv = 1.0f / l;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) o[at(RQ, qrow, c)] = acc[c] * inv;
+  for (int c = 0; c < 64; ++c) o[at_v(RQ, ro, qrow, c)] = acc[c] * inv;
   if (lse != nullptr) {
     const int64_t pos = RQ ? tile_origin(i, pt, ph, pw, g.Hs, g.Ws) + tile_intra(t, ph, pw, g.Hs, g.Ws) : qrow;
     lse[((int64_t)b * g.H + h) * g.N + pos] = m + logf(l);
@@ -377,7 +380,8 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
 }
 
 template <bool RQ, bool RK, int VM>
-static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt, const void *q,
+static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const RasterView &ro, veda_dtype dt,
+                          const void *q,
                           const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
                           float *lse, hipStream_t st) {
   if (dt == VEDA_BF16) {
@@ -385,27 +389,28 @@ static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &
     if (PADDABLE && g.padded)
       attn_bf16_kernel<RQ, false, PADDABLE, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
-          rv);
+          rv, ro);
     else
       attn_bf16_kernel<RQ, RK, false, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
-          rv);
+          rv, ro);
   } else
     attn_f32_kernel<RQ, RK, VM><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
                                                                      (const float *)v, kv_idx, kk, scale, (float *)o,
-                                                                     lse, g, hs, rv);
+                                                                     lse, g, hs, rv, ro);
 }
 
 template <bool RQ, bool RK>
-static void launch_attn_v(int vm, const Geo &g, const HeadShapes &hs, const RasterView &rv, veda_dtype dt,
+static void launch_attn_v(int vm, const Geo &g, const HeadShapes &hs, const RasterView &rv, const RasterView &ro,
+                          veda_dtype dt,
                           const void *q, const void *k, const void *v, const int32_t *kv_idx, int kk, float scale,
                           void *o, float *lse, hipStream_t st) {
   if (vm == VM_COLS)
-    launch_attn_t<RQ, RK, VM_COLS>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_COLS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   else if (vm == VM_ROWS)
-    launch_attn_t<RQ, RK, VM_ROWS>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_ROWS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   else if constexpr (RQ)  // a raster V comes only with raster Q (its strides)
-    launch_attn_t<RQ, RK, VM_RAST>(g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_RAST>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
 }
 
 static int v_mode(veda_layout v_layout) {
@@ -415,21 +420,21 @@ static int v_mode(veda_layout v_layout) {
 hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                               const void *v, veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
                               float *lse, hipStream_t st) {
-  launch_attn_v<false, false>(v_mode(v_layout), g, hs, RasterView{0, 0, 0}, dt, q, k, v, kv_idx, kk, scale, o, lse,
-                              st);
+  launch_attn_v<false, false>(v_mode(v_layout), g, hs, RasterView{0, 0, 0}, RasterView{0, 0, 0}, dt, q, k, v, kv_idx,
+                              kk, scale, o, lse, st);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                                      bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
                                      veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                                     float *lse, hipStream_t st) {
+                                     int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t st) {
   const int64_t eb = dt == VEDA_BF16 ? 2 : 4;
-  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb};
+  const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb}, ro{os_b * eb, os_n * eb, os_h * eb};
   if (k_raster)
-    launch_attn_v<true, true>(v_mode(v_layout), g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, true>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   else
-    launch_attn_v<true, false>(v_mode(v_layout), g, hs, rv, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, false>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 

@@ -40,12 +40,13 @@ hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt,
                               const void *v, veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
                               float *lse, hipStream_t st);
 
-// Q and O in raster layout [B, N, H, d] (element strides rs_*), K raster or tile-major,
-// V channel-major tiled, tile-major, or raster with Q's strides.
+// Q (element strides rs_*) and O (element strides os_*) in raster layout [B, N, H, d], K
+// raster (Q's strides) or tile-major, V channel-major tiled, tile-major, or raster with Q's
+// strides.
 hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                                      bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
                                      veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                                     float *lse, hipStream_t st);
+                                     int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t st);
 
 size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,
