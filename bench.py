@@ -401,7 +401,8 @@ def main():
         for _ in range(3):   # interleaved rounds: the layouts see the same clock drift
             for name, vop, lay in (("rows", sa.v_t, V.ROWS), ("cols", v_cols, V.COLS), ("raster", v, V.RASTER)):
                 runs[name].append(timed(lambda: V.veda_sparse_attn_fwd_raster(
-                    geom, q, sa.k_t, vop, sa.idx_buffer(kk), kk, sa.softmax_scale, o2, k_layout=V.ROWS, v_layout=lay), 3))
+                    geom, q, sa.k_t, vop, sa.idx_buffer(kk), kk, sa.softmax_scale, o2, k_layout=V.ROWS, v_layout=lay,
+                    k_bound=sa.k_bound), 3))
         v_layouts = {f"{name}_ms": round(float(np.median(t)), 3) for name, t in runs.items()}
         v_layouts["note"] = ("attention alone with raster Q and O, tiled K; median of three interleaved rounds of "
                              "3 calls per layout, after the timed steps")

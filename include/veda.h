@@ -136,6 +136,11 @@ size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int
  *   scores:     out [B, H, n_t, n_t] f32, nullable
  *   probs:      out [B, H, n_t, n_t] f32 row softmax, nullable
  *   q_desc, k_desc: out [B, H, n_t, 3d] f32, nullable
+ *   k_bound:    out [B, H, n_t] f32, nullable: for each key tile j,
+ *               sqrt(sum over channels c of max(max_c^2, min_c^2)) with max_c, min_c its
+ *               max and min descriptors - an upper bound of the L2 norm of every key row
+ *               of the tile (0 for tiles past a padded head's own n_t(h)); the attention
+ *               calls take it to fix their softmax offset
  *   topk, idx:  topk in [1, n_t] with idx out [B, H, n_t, topk] int32; or topk = 0, idx NULL
  * At least one of scores / probs / idx must be requested.  Implemented for
  * mlp_hidden = 256 and mlp_out = 64.  workspace >= veda_trippool_workspace_bytes. */
@@ -145,7 +150,7 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype,
                                 const float *w1_k, const float *w2_k,
                                 int32_t mlp_hidden, int32_t mlp_out, float score_scale,
                                 float *scores, float *probs, float *q_desc, float *k_desc,
-                                int32_t topk, int32_t *idx,
+                                float *k_bound, int32_t topk, int32_t *idx,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Tile selection at a sparsity level.  [Technical Summary §4: 90% / 95% of key tiles
@@ -168,12 +173,27 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  *           (k == n_t with every tile listed is dense attention).  Entries outside
  *           [0, n_t) are clamped into it (no out-of-bounds access; the result is then
  *           not meaningful).
+ *   k_bound: [B, H, n_t] f32 upper bounds of the key-row norms of each key tile of this
+ *           K (the k_bound output of the scoring call that read it), nullable.  The bf16
+ *           kernel offsets each row's exponentials by its first kept tile's row maximum m;
+ *           without k_bound it takes every later tile's row maximum too and moves m when
+ *           one exceeds it by more than 8 (log2 units).  With k_bound, the 32 rows of a
+ *           wave keep m fixed and take no further row maximum when every row's
+ *           b = softmax_scale * |q| * max over its kept tiles of k_bound (at or above each
+ *           of its logits) lies at most 64 (log2) above its m, so that no exponential
+ *           exceeds 2^64; the result is then the same bit for bit unless a later tile's
+ *           row maximum exceeds m by more than 8, and the same softmax up to rounding
+ *           otherwise.  Rows whose first tile's maximum lies above b by more than 8 (a
+ *           k_bound of another K) take the running maximum.  A k_bound below the true
+ *           norms can still overflow the exponentials of later tiles: the output is then
+ *           not meaningful, with no out-of-bounds access.  The fp32 kernel ignores it.
+ *   softmax_scale: > 0 and finite (else VEDA_ERR_SHAPE)
  *   o_tiled: out VEDA_TILE_ROWS, same dtype
  *   lse:     out [B, H, N] f32 natural-log log-sum-exp of each query row, nullable */
 veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype,
                                  const void *q_tiled, const void *k_tiled, const void *v_tiled,
-                                 veda_layout v_layout, const int32_t *kv_idx, int32_t k, float softmax_scale,
-                                 void *o_tiled, float *lse, hipStream_t stream);
+                                 veda_layout v_layout, const int32_t *kv_idx, const float *k_bound, int32_t k,
+                                 float softmax_scale, void *o_tiled, float *lse, hipStream_t stream);
 
 /* Workspace (bytes) that veda_oracle_tilemap needs: B*H*n_sel*n_t*P floats. */
 size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel);
@@ -190,6 +210,7 @@ size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel);
  *   q_tiled, k_tiled: VEDA_TILE_ROWS
  *   q_tiles: DEVICE int32 [B, H, n_sel] in [0, n_t) (entries outside are clamped), or
  *            NULL (then n_sel must be n_t)
+ *   softmax_scale: > 0 and finite (else VEDA_ERR_SHAPE)
  *   tilemap: out [B, H, n_sel, n_t] f32;  lse: out [B, H, n_sel * P] f32, nullable
  *   workspace: >= veda_oracle_tilemap_workspace_bytes(g, n_sel) bytes of device memory */
 veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
@@ -201,7 +222,8 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype,
 /* Raster-direct variants (no tiled copies of Q or O, and optionally none of K).
  * [Technical Summary §2.3 and the paper's future work on fusing the tiling into the
  * kernels]  They compute exactly what veda_trippool_score, veda_sparse_attn_fwd and
- * veda_oracle_tilemap compute (bit for bit), but read Q (and write O) in the raster layout
+ * veda_oracle_tilemap compute (bit for bit; attention given the same k_bound), but read Q
+ * (and write O) in the raster layout
  * [B, N, H, d] with element strides rs_b, rs_n, rs_h for Q (os_b, os_n, os_h for O; d
  * contiguous, 16-byte aligned rows and strides), going through each head's tiling in the
  * kernels: row r of tile j of head h
@@ -231,14 +253,14 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
-                                       float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *k_tiled_out, const void *v_raster, void *v_tiled_out, void *workspace,
-                                       size_t workspace_bytes, hipStream_t stream);
+                                       float *probs, float *q_desc, float *k_desc, float *k_bound, int32_t topk,
+                                       int32_t *idx, void *k_tiled_out, const void *v_raster, void *v_tiled_out,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                         veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                         const void *v, veda_layout v_layout, const int32_t *kv_idx,
-                                        int32_t k_kept, float softmax_scale, void *o_raster, int64_t os_b,
-                                        int64_t os_n, int64_t os_h, float *lse, hipStream_t stream);
+                                        const float *k_bound, int32_t k_kept, float softmax_scale, void *o_raster,
+                                        int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t stream);
 veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k,
                                        veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h,
                                        float softmax_scale, const int32_t *q_tiles, int32_t n_sel, float *tilemap,
@@ -259,9 +281,9 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                int64_t rs_h, const float *w1_q, const float *w2_q,
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
-                                               float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               void *k_tiled_out, const void *v_raster, void *v_tiled_out,
-                                               hipStream_t stream);
+                                               float *q_desc, float *k_desc, float *k_bound, int32_t topk,
+                                               int32_t *idx, void *k_tiled_out, const void *v_raster,
+                                               void *v_tiled_out, hipStream_t stream);
 
 /* Workspace (bytes) that veda_distill_step needs (descriptors, MLP activations and
  * gradients of the sampled Q tiles and of every K tile, per-row KL terms). */

@@ -21,15 +21,15 @@ int main(void) {
   printf("tilemap_ws_64 %zu\n", veda_oracle_tilemap_workspace_bytes(&g, 64));
   printf("trippool_ws %zu\n", veda_trippool_workspace_bytes(&g, 256, 64));
   /* validation only: each of these returns before anything is launched */
-  printf("attn_null %d\n", (int)veda_sparse_attn_fwd(&g, VEDA_BF16, NULL, NULL, NULL, VEDA_TILE_COLS, NULL, 60,
-                                                      0.088f, NULL, NULL, 0));
-  printf("attn_dtype %d\n", (int)veda_sparse_attn_fwd(&g, (veda_dtype)7, NULL, NULL, NULL, VEDA_TILE_COLS, NULL, 60,
-                                                       0.088f, NULL, NULL, 0));
+  printf("attn_null %d\n", (int)veda_sparse_attn_fwd(&g, VEDA_BF16, NULL, NULL, NULL, VEDA_TILE_COLS, NULL, NULL,
+                                                      60, 0.088f, NULL, NULL, 0));
+  printf("attn_dtype %d\n", (int)veda_sparse_attn_fwd(&g, (veda_dtype)7, NULL, NULL, NULL, VEDA_TILE_COLS, NULL,
+                                                       NULL, 60, 0.088f, NULL, NULL, 0));
   /* a raster V has no strides in the tiled call and is refused (the fake addresses below
      are never dereferenced) */
   printf("attn_v_raster %d\n", (int)veda_sparse_attn_fwd(&g, VEDA_BF16, (const void *)256, (const void *)512,
-                                                          (const void *)768, VEDA_RASTER, (const int32_t *)1024, 60,
-                                                          0.088f, (void *)1280, NULL, 0));
+                                                          (const void *)768, VEDA_RASTER, (const int32_t *)1024, NULL,
+                                                          60, 0.088f, (void *)1280, NULL, 0));
   printf("topk_k0 %d\n", (int)veda_topk_mask(4, 10, NULL, 0, NULL, NULL, 0));
   printf("topk_empty %d\n", (int)veda_topk_mask(0, 10, (const float *)16, 3, (int32_t *)16, NULL, 0));
   int32_t bad[40][3];

@@ -63,7 +63,7 @@ def test_empty_geometries_are_refused(L):
     for kw in (dict(batch=0), dict(heads=0, shapes=((2, 8, 8),))):
         g = geom(**kw)
         assert L.veda_tiled_tokens(g.ref, V.BF16) == SHAPE
-        assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.ROWS, A, 1, 0.088, A, None, None) == SHAPE
+        assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.ROWS, A, None, 1, 0.088, A, None, None) == SHAPE
         assert gather(L, g) == SHAPE
     g = geom(grid=(0, 16, 32))
     assert L.veda_tiled_tokens(g.ref, V.BF16) == SHAPE
@@ -93,22 +93,22 @@ def test_padded_rejected_where_unsupported(L):
     n_t = g.n_tiles                                           # 3 * 4 * 8 = 96 > 80 (dividing head)
     st = (g.n_tokens * 2 * 128, 2 * 128, 128)
     RAS, big = V.RASTER, 1 << 40
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, 4, 0.088, A, *st, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, V.COLS, A, None, 4, 0.088, A, *st, None,
                                          None) == UNSUP
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, RAS, A, 4, 0.088, A, *st, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, RAS, A, None, 4, 0.088, A, *st, None,
                                          None) == UNSUP                      # a raster V, likewise
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, RAS, *st, 0.088, A, 4, A, None, A, big, None) == UNSUP
     assert L.veda_oracle_tilemap_raster(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, None, n_t, A, None, A, big,
                                         None) == SHAPE
     assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, 0.088, None, n_t, A, None, A, big, None) == SHAPE
     # k may not exceed the smallest per-head tile count (80 here), on every path
-    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.COLS, A, 81, 0.088, A, None, None) == SHAPE
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, V.COLS, A, 81, 0.088, A, *st, None,
-                                         None) == SHAPE
-    assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, 81, A, A,
-                                 big, None) == SHAPE
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.COLS, A, None, 81, 0.088, A, None, None) == SHAPE
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.ROWS, *st, A, V.COLS, A, None, 81, 0.088, A, *st,
+                                         None, None) == SHAPE
+    assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 81,
+                                 A, A, big, None) == SHAPE
     assert L.veda_trippool_score_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None,
-                                        None, 81, A, None, None, None, A, big, None) == SHAPE
+                                        None, None, 81, A, None, None, None, A, big, None) == SHAPE
     assert L.veda_distill_step(g.ref, V.BF16, A, A, A, A, 256, 64, 0.125, A, n_t + 1, A, A, A, A, 0.0, A, big,
                                None) == SHAPE
 
@@ -130,7 +130,7 @@ def test_gather_validation(L):
 
 
 def score(L, g, topk=6, idx=B_, scores=None, ws=A, ws_bytes=1 << 30, hidden=256, out=64):
-    return L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, hidden, out, 0.125, scores, None, None, None,
+    return L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, hidden, out, 0.125, scores, None, None, None, None,
                                  topk, idx, ws, ws_bytes, None)
 
 
@@ -167,12 +167,32 @@ def test_attn_validation(L):
     g = geom()
     f = L.veda_sparse_attn_fwd
     C = V.COLS
-    assert f(g.ref, V.BF16, A, A, None, C, A, 4, 0.088, A, None, None) == NULL
-    assert f(g.ref, V.BF16, A, A, A, C, A, 0, 0.088, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, A, A, C, A, 33, 0.088, A, None, None) == SHAPE
-    assert f(g.ref, V.BF16, A, A, A, C, A, 4, 0.088, MIS, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, A, C, A, 4, 0.088, A, MIS, None) == ALIGN
-    assert f(geom(d=64).ref, V.BF16, A, A, A, C, A, 4, 0.088, A, None, None) == UNSUP
+    assert f(g.ref, V.BF16, A, A, None, C, A, None, 4, 0.088, A, None, None) == NULL
+    assert f(g.ref, V.BF16, A, A, A, C, A, None, 0, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, C, A, None, 33, 0.088, A, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, A, C, A, None, 4, 0.088, MIS, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, A, C, A, None, 4, 0.088, A, MIS, None) == ALIGN
+    assert f(geom(d=64).ref, V.BF16, A, A, A, C, A, None, 4, 0.088, A, None, None) == UNSUP
+    assert f(g.ref, V.BF16, A, A, A, C, A, MIS, 4, 0.088, A, None, None) == ALIGN      # key-tile bounds
+    for bad in (0.0, -0.088, float("inf"), float("nan")):                               # softmax scale
+        assert f(g.ref, V.BF16, A, A, A, C, A, None, 4, bad, A, None, None) == SHAPE
+        assert L.veda_oracle_tilemap(g.ref, V.BF16, A, A, bad, A, 4, A, None, A, 1 << 40, None) == SHAPE
+
+
+def test_key_tile_bound_pointers(L):
+    """The per-key-tile norm bounds (scoring output, attention input) are checked like every
+    other device pointer, in all five calls that take them."""
+    g = geom()
+    st = (4096 * 2 * 128, 2 * 128, 128)
+    RAS, C = V.RASTER, V.COLS
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, RAS, *st, A, C, A, MIS, 4, 0.088, A, *st, None,
+                                         None) == ALIGN
+    assert L.veda_trippool_score(g.ref, V.BF16, A, A, A, A, A, A, 256, 64, 0.125, None, None, None, None, MIS, 6,
+                                 B_, A, 1 << 30, None) == ALIGN
+    assert L.veda_trippool_score_raster(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None,
+                                        None, MIS, 6, B_, None, None, None, A, 1 << 30, None) == ALIGN
+    assert L.veda_trippool_score_raster_noalloc(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None,
+                                                None, None, None, MIS, 6, B_, None, None, None, None) == ALIGN
 
 
 def test_attn_v_layout_validation(L):
@@ -180,10 +200,10 @@ def test_attn_v_layout_validation(L):
     raster V in the tiled call (no strides) and an unknown layout are refused with a status,
     never computed as if V were in another layout."""
     g = geom()
-    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.RASTER, A, 4, 0.088, A, None, None) == UNSUP
-    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, 7, A, 4, 0.088, A, None, None) == SHAPE
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, V.RASTER, A, None, 4, 0.088, A, None, None) == UNSUP
+    assert L.veda_sparse_attn_fwd(g.ref, V.BF16, A, A, A, 7, A, None, 4, 0.088, A, None, None) == SHAPE
     st = (4096 * 2 * 128, 2 * 128, 128)
-    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, 7, A, 4, 0.088, A, *st, None,
+    assert L.veda_sparse_attn_fwd_raster(g.ref, V.BF16, A, A, V.RASTER, *st, A, 7, A, None, 4, 0.088, A, *st, None,
                                          None) == SHAPE
 
 
@@ -244,32 +264,32 @@ def test_raster_validation(L):
     st = (4096 * 2 * 128, 2 * 128, 128)
     RAS = V.RASTER
     C = V.COLS
-    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, C, A, 4, 0.088, A, *st, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, None, RAS, *st, A, C, A, 4, 0.088, A, *st, None, None) == NULL
-    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, C, A, 4, 0.088, A, *st, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, C, A, 4, 0.088, A, *st, None, None) == SHAPE   # K layout
+    assert f(g.ref, V.BF16, A, A, RAS, 4096 * 256, 260, 128, A, C, A, None, 4, 0.088, A, *st, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, None, RAS, *st, A, C, A, None, 4, 0.088, A, *st, None, None) == NULL
+    assert f(g.ref, V.BF16, MIS, A, RAS, *st, A, C, A, None, 4, 0.088, A, *st, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, V.COLS, *st, A, C, A, None, 4, 0.088, A, *st, None, None) == SHAPE   # K layout
     # O has strides of its own, checked like Q's
-    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, 4, 0.088, A, 4096 * 256, 260, 128, None, None) == ALIGN
-    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, 4, 0.088, A, -1, 256, 128, None, None) == SHAPE
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, None, 4, 0.088, A, 4096 * 256, 260, 128, None, None) == ALIGN
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, C, A, None, 4, 0.088, A, -1, 256, 128, None, None) == SHAPE
     # in-tile token offset x token stride beyond 2^31 bytes (Q's or O's)
-    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, C, A, 4,
+    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, 0, 1 << 20, 128, A, C, A, None, 4,
              0.088, A, *st, None, None) == UNSUP
-    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, *st, A, C, A, 4,
+    assert f(geom(grid=(8, 16, 32), shapes=((8, 4, 4),) * 2).ref, V.BF16, A, A, RAS, *st, A, C, A, None, 4,
              0.088, A, 0, 1 << 20, 128, None, None) == UNSUP
     s = L.veda_trippool_score_raster
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None, None,
-             None, A, 1 << 30, None) == NULL
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, None, None,
+             None, None, A, 1 << 30, None) == NULL
     # K's tiled copy comes only from a raster K, and must be aligned
-    assert s(g.ref, V.BF16, A, A, V.ROWS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, B_, None,
+    assert s(g.ref, V.BF16, A, A, V.ROWS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, B_, None,
              None, A, 1 << 30, None) == SHAPE
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, MIS, None,
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, MIS, None,
              None, A, 1 << 30, None) == ALIGN
     # V's tiled copy needs the raster V and the output together, both aligned
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, A,
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, None, A,
              None, A, 1 << 30, None) == NULL
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, None,
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, None, None,
              B_, A, 1 << 30, None) == NULL
-    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None, A,
+    assert s(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, None, A,
              MIS, A, 1 << 30, None) == ALIGN
     t = L.veda_oracle_tilemap_raster
     assert t(g.ref, V.BF16, A, A, V.ROWS, *st, 0.088, A, 0, A, None, A, 1 << 40, None) == SHAPE
@@ -303,6 +323,11 @@ def test_binding_checks_sizes_before_taking_pointers():
         V.veda_trippool_score(g, bf(n), bf(n), w1, w2, topk=6, idx=i32(2 * 32 * 6 - 1))
     with pytest.raises(V.VedaError, match="at least"):
         V.veda_trippool_score(g, bf(n), bf(n), w1, w2, scores=torch.zeros(2 * 32 * 31))
+    with pytest.raises(V.VedaError, match="at least"):     # key-tile bounds: [B, H, n_t]
+        V.veda_trippool_score(g, bf(n), bf(n), w1, w2, topk=6, idx=i32(2 * 32 * 6), k_bound=torch.zeros(2 * 32 - 1))
+    with pytest.raises(V.VedaError, match="dtype"):
+        V.veda_sparse_attn_fwd(g, bf(n), bf(n), bf(n), i32(2 * 32 * 4).view(1, 2, 32, 4), 4, 0.088, bf(n),
+                               k_bound=torch.zeros(2 * 32, dtype=torch.float64))
     with pytest.raises(V.VedaError, match="at least"):
         V.veda_oracle_tilemap(g, bf(n), bf(n), 0.088, i32(2 * 4), 4, torch.zeros(2 * 4 * 32 - 1))
     with pytest.raises(V.VedaError, match="at least"):
@@ -323,18 +348,18 @@ def test_noalloc_scoring_rejects_beyond_its_scratch(L):
     RAS = V.RASTER
     big = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 56)        # 56 heads x 1200 tiles = 67200
     st = (153600 * 56 * 128, 56 * 128, 128)
-    assert f(big.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A, None,
+    assert f(big.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 60, A, None,
              None, None, None) == -8
     assert b"scratch" in L.veda_status_str(-8)
     fits = geom(grid=(40, 48, 80), shapes=((2, 8, 8),) * 54)       # 64800 tiles: passes the size check,
     st = (153600 * 54 * 128, 54 * 128, 128)                         # then a NULL K is refused
-    assert f(fits.ref, V.BF16, A, None, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 60, A, None,
+    assert f(fits.ref, V.BF16, A, None, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 60, A, None,
              None, None, None) == NULL
     g = geom()
     st = (4096 * 2 * 128, 2 * 128, 128)
-    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, None, None,
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, None, None,
              None, None, None) == NULL
-    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 512, 64, 0.125, None, None, None, None, 6, A, None,
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 512, 64, 0.125, None, None, None, None, None, 6, A, None,
              None, None, None) == UNSUP
-    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, 6, A, None,
+    assert f(g.ref, V.BF16, A, A, RAS, *st, A, A, A, A, 256, 64, 0.125, None, None, None, None, None, 6, A, None,
              A, None, None) == NULL                                    # V's copy: both or neither

@@ -169,6 +169,35 @@ def test_padded_descriptors(r):
             assert err.max() <= 1e-6, (cfg.name, h, err.max())
 
 
+def test_padded_key_tile_bounds(r):
+    """Each key tile's row-norm bound, sqrt(sum_c max(max_c^2, min_c^2)) over the oracle's
+    padded max and min descriptors (real rows only), 0 past a head's own tiles; and the
+    attention's running-maximum softmax (no bounds) against the oracle, beside the fixed
+    offset that test_padded_attention checks."""
+    cfg, P, d = r.cfg, r.cfg.tile, r.cfg.head_dim
+    kb = host(r.sa.k_bound)
+    o_run = torch.empty_like(r.sa.o_t)
+    V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, r.idx, r.kk, r.sa.softmax_scale, o_run)
+    torch.cuda.synchronize()
+    worst = mx = 0.0
+    for b, h in r.pairs():
+        qt, kt, vt, slots = r.oracle_head(b, h)
+        ntile = len(slots) // P
+        desc = O.trippool(kt, P, valid=slots >= 0)
+        ref = np.sqrt((np.maximum(np.abs(desc[:, d:2 * d]), np.abs(desc[:, 2 * d:])) ** 2).sum(1))
+        worst = max(worst, float(np.abs(kb[b, h, :ntile] / ref - 1).max()))
+        assert not kb[b, h, ntile:].any(), (cfg.name, h, "bounds past the head's tiles")
+        tiles = r.q_tiles(h)
+        ref_o = O.sparse_attention(qt, kt, vt, host(r.idx[b, h]).astype(np.int64), P, 1 / math.sqrt(d),
+                                   q_tiles=tiles, key_valid=slots >= 0)
+        rows = (tiles[:, None] * P + np.arange(P)[None]).ravel()
+        real = slots[rows] >= 0
+        mx = max(mx, float(np.abs(host(o_run[b, h])[rows][real] - ref_o[real]).max()))
+    measure(f"[gpu-padded] {cfg.name}: key-tile bounds max rel err {worst:.3g}; running-maximum attention "
+            f"max|dO| {mx:.3g}")
+    assert worst <= 1e-5 and mx <= 2e-2
+
+
 def test_padded_scores_topk(r):
     cfg, P = r.cfg, r.cfg.tile
     worst, exempt, rows = 0.0, 0, 0
@@ -263,13 +292,15 @@ def test_padded_raster_path(r):
         idx = torch.full_like(r.idx, -1)
         k_copy = torch.full_like(sa.k_t, float("nan")) if k_layout == V.RASTER else None
         v_copy = torch.full_like(sa.v_t, float("nan"))
+        kb = torch.full_like(sa.k_bound, float("nan"))
         V.veda_trippool_score_raster(g, r.q, r.k if k_layout == V.RASTER else sa.k_t, sa.w1, sa.w2,
                                      score_scale=cfg.score_scale, scores=scores, q_desc=qd, k_desc=kd, topk=r.kk,
                                      idx=idx, workspace=sa.ws, k_layout=k_layout, k_tiled_out=k_copy,
-                                     v=r.v, v_tiled_out=v_copy)
+                                     v=r.v, v_tiled_out=v_copy, k_bound=kb)
         torch.cuda.synchronize()
         assert torch.equal(v_copy.view(torch.int16), sa.v_t.view(torch.int16)), (cfg.name, "V's copy")
         assert torch.equal(qd, r.qd) and torch.equal(kd, r.kd), (cfg.name, k_layout)
+        assert torch.equal(kb, sa.k_bound), (cfg.name, k_layout, "key-tile bounds")
         for h in range(H):   # a head's own rows (the rows past its tiles are not written)
             nth = g.head_tiles(h)
             assert torch.equal(scores[:, h, :nth], r.scores[:, h, :nth]), (cfg.name, k_layout, h)
@@ -285,10 +316,11 @@ def test_padded_raster_path(r):
     v_cols = r.v_cols()
     o_t = torch.empty_like(sa.o_t)
     lse_t2 = torch.empty_like(r.lse)
-    V.veda_sparse_attn_fwd(g, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse_t2, v_layout=V.COLS)
+    V.veda_sparse_attn_fwd(g, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse_t2, v_layout=V.COLS,
+                           k_bound=sa.k_bound)
     out2 = torch.zeros_like(r.q)
     V.veda_sparse_attn_fwd_raster(g, r.q, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, out2, k_layout=V.ROWS,
-                                  v_layout=V.COLS)
+                                  v_layout=V.COLS, k_bound=sa.k_bound)
     torch.cuda.synchronize()
     for h in range(H):   # a head's own rows (rows past its tiles are not written)
         rows = g.head_tiles(h) * P

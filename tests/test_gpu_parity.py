@@ -248,12 +248,14 @@ def test_output_unpermuted(r):
 
 
 def test_dense_path(r):
-    """k = n_t with every tile listed: equals full attention."""
+    """k = n_t with every tile listed: equals full attention (with the key-tile bounds, as
+    the benchmark's dense path runs)."""
     cfg, ci = r.cfg, r.cfg.index
     idx = dense_index(r.geom)
     o_t = torch.empty_like(r.sa.o_t)
     say(f"[gpu-parity] {cfg.name}: dense path k={cfg.n_tiles}")
-    V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, cfg.n_tiles, 1 / math.sqrt(cfg.head_dim), o_t)
+    V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, cfg.n_tiles, 1 / math.sqrt(cfg.head_dim), o_t,
+                           k_bound=r.sa.k_bound)
     torch.cuda.synchronize()
     heads = r.heads({0: None, 1: None, 2: 4, 3: 4, 4: 4}[ci])
     tph = {0: None, 1: None, 2: 8, 3: 8, 4: 4}[ci]
@@ -285,6 +287,7 @@ def test_sparsity_sweep(r):
                 assert O.topk_agrees(s32[h][i], got[i], kk)[0], (cfg.name, kk, h, i)
         o_t = torch.empty_like(r.sa.o_t)
         say(f"[gpu-parity] {cfg.name}: k={kk}")
+        # no key-tile bounds: the sweep checks the running-maximum softmax at every k
         V.veda_sparse_attn_fwd(r.geom, r.sa.q_t, r.sa.k_t, r.sa.v_t, idx, kk, 1 / math.sqrt(cfg.head_dim), o_t)
         torch.cuda.synchronize()
         heads = r.heads(8)
@@ -494,7 +497,8 @@ def test_v_layouts_match(r):
     v_cols = r.v_cols()
     o_t = torch.empty_like(sa.o_t)
     lse = torch.empty_like(r.lse)
-    V.veda_sparse_attn_fwd(r.geom, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse, v_layout=V.COLS)
+    V.veda_sparse_attn_fwd(r.geom, sa.q_t, sa.k_t, v_cols, r.idx, r.kk, sa.softmax_scale, o_t, lse, v_layout=V.COLS,
+                           k_bound=sa.k_bound)
     torch.cuda.synchronize()
     assert same_bits(o_t, sa.o_t) and same_bits(lse, r.lse), cfg.name
     del o_t
@@ -502,7 +506,7 @@ def test_v_layouts_match(r):
         for v_layout, vop in ((V.COLS, v_cols), (V.RASTER, r.v)):
             out = torch.zeros_like(r.out)
             V.veda_sparse_attn_fwd_raster(r.geom, r.q, kop, vop, r.idx, r.kk, sa.softmax_scale, out,
-                                          k_layout=k_layout, v_layout=v_layout)
+                                          k_layout=k_layout, v_layout=v_layout, k_bound=sa.k_bound)
             torch.cuda.synchronize()
             assert same_bits(out, r.out), (cfg.name, k_layout, v_layout)
 
@@ -550,12 +554,13 @@ def test_raster_path_matches_tiled(r, k_raster):
         k_copy = torch.full_like(sa.k_t, float("nan"))
         v_copy = torch.full_like(sa.v_t, float("nan"))
         idx2 = torch.full_like(idx, -1)
+        kb = torch.full_like(sa.k_bound, float("nan"))
         V.veda_trippool_score_raster(r.geom, r.q, r.k, sa.w1, sa.w2, score_scale=cfg.score_scale, topk=r.kk,
                                      idx=idx2, workspace=sa.ws, k_layout=V.RASTER, k_tiled_out=k_copy,
-                                     v=r.v, v_tiled_out=v_copy)
+                                     v=r.v, v_tiled_out=v_copy, k_bound=kb)
         torch.cuda.synchronize()
         assert torch.equal(idx2, r.idx)
-        assert same_bits(k_copy, sa.k_t) and same_bits(v_copy, sa.v_t)
+        assert same_bits(k_copy, sa.k_t) and same_bits(v_copy, sa.v_t) and same_bits(kb, sa.k_bound)
     else:
         # V's copy from the scoring launch with a tiled K as well
         v_copy = torch.full_like(sa.v_t, float("nan"))
@@ -564,3 +569,49 @@ def test_raster_path_matches_tiled(r, k_raster):
                                      idx=idx2, workspace=sa.ws, k_layout=V.ROWS, v=r.v, v_tiled_out=v_copy)
         torch.cuda.synchronize()
         assert torch.equal(idx2, r.idx) and same_bits(v_copy, sa.v_t)
+
+
+# ----------------------------------------------------------------------------- softmax offset
+def test_key_tile_bounds_and_offset_paths(r):
+    """The scoring call's per-key-tile bound (from the oracle's max and min descriptors:
+    sqrt(sum_c max(max_c^2, min_c^2)), which bounds every key-row norm of the tile), and
+    attention with and without it.  Both start each row's exponent offset at its first kept
+    tile's row max; without bounds the kernel takes every later tile's row max and moves the
+    offset when one exceeds it by more than 2^8, with bounds it keeps the offset fixed (the
+    bound proving that no later exponential exceeds 2^64).  The fixed offset is checked
+    against the oracle by test_sparse_attention, the running one here on sampled heads; the
+    two agree bit for bit on every row whose offset the running maximum never moves.  A
+    bound 2^40 too large sends every wave back to the running maximum, which must then give
+    exactly the output and LSE of the call without bounds."""
+    cfg, sa = r.cfg, r.sa
+    d, P = cfg.head_dim, cfg.tile
+    say(f"[gpu-parity] {cfg.name}: key-tile bounds and softmax offsets")
+    kb = host(sa.k_bound)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in r.heads(8):
+            _, kt, _, _ = r.oracle_head(b, h)
+            desc = O.trippool(kt, P)
+            ref = np.sqrt((np.maximum(np.abs(desc[:, d:2 * d]), np.abs(desc[:, 2 * d:])) ** 2).sum(1))
+            worst = max(worst, float(np.abs(kb[b, h] / ref - 1).max()))
+            rown = np.linalg.norm(kt.reshape(-1, P, d), axis=2).max(1)
+            assert np.all(kb[b, h] >= rown * (1 - 1e-6)), (cfg.name, h)
+    measure(f"[gpu-parity] {cfg.name}: key-tile bounds max rel err {worst:.3g}")
+    assert worst <= 1e-5            # fp32 sum of 128 squares of exactly represented values
+    if not r.bf16:
+        return                      # the fp32 kernel keeps a running maximum throughout
+    o_run, l_run = torch.empty_like(sa.o_t), torch.empty_like(r.lse)
+    V.veda_sparse_attn_fwd(r.geom, sa.q_t, sa.k_t, sa.v_t, r.idx, r.kk, sa.softmax_scale, o_run, l_run)
+    o_far, l_far = torch.empty_like(sa.o_t), torch.empty_like(r.lse)
+    V.veda_sparse_attn_fwd(r.geom, sa.q_t, sa.k_t, sa.v_t, r.idx, r.kk, sa.softmax_scale, o_far, l_far,
+                           k_bound=sa.k_bound * 2.0 ** 40)
+    torch.cuda.synchronize()
+    assert same_bits(o_far, o_run) and same_bits(l_far, l_run), cfg.name
+    heads = r.heads(8)
+    mx, rel, lse_err = attention_errors(r, r.idx, r.kk, heads, tiles_per_head=16, o_t=o_run, lse=l_run)
+    same_rows = float((l_run.view(torch.int32) == r.lse.view(torch.int32)).float().mean())
+    measure(f"[gpu-parity] {cfg.name}: running-maximum softmax, {len(heads)} heads x 16 query tiles: "
+            f"max|dO| {mx:.3g} relFro {rel:.3g} max|dLSE| {lse_err:.3g}; rows bit-identical to the fixed offset "
+            f"{same_rows:.4f}")
+    amax, arel = tol(r)
+    assert mx <= amax and rel <= arel and lse_err <= 4e-3

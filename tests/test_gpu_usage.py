@@ -85,15 +85,16 @@ def test_graph_capture_noalloc_step():
     def step():
         V.veda_trippool_score_raster_noalloc(geom, q, k, sa.w1, sa.w2, score_scale=cfg.score_scale, topk=kk,
                                              idx=idx, k_layout=V.RASTER, k_tiled_out=sa.k_t, v=v,
-                                             v_tiled_out=sa.v_t)
-        V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, sa.v_t, idx, kk, sa.softmax_scale, out, k_layout=V.ROWS)
+                                             v_tiled_out=sa.v_t, k_bound=sa.k_bound)
+        V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, sa.v_t, idx, kk, sa.softmax_scale, out, k_layout=V.ROWS,
+                                      k_bound=sa.k_bound)
         V.veda_oracle_tilemap_raster(geom, q, sa.k_t, sa.softmax_scale, qtl, n_sel, tmap, workspace=tm_ws,
                                      k_layout=V.ROWS)
 
     say("[gpu-usage] eager step (also looks up the static scratch before any capture)")
     step()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (idx, out, tmap, sa.k_t, sa.v_t)]
+    want = [t.clone() for t in (idx, out, tmap, sa.k_t, sa.v_t, sa.k_bound)]
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -106,11 +107,11 @@ def test_graph_capture_noalloc_step():
         step()
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in (idx, out, tmap, sa.k_t, sa.v_t):               # eager work between replays
+        for t in (idx, out, tmap, sa.k_t, sa.v_t, sa.k_bound):   # eager work between replays
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for got, ref in zip((idx, out, tmap, sa.k_t, sa.v_t), want):
+        for got, ref in zip((idx, out, tmap, sa.k_t, sa.v_t, sa.k_bound), want):
             assert torch.equal(bits(got), bits(ref)), rep
         say(f"[gpu-usage] replay {rep}: identical to the eager step")

@@ -1,7 +1,7 @@
 """The no-allocation scoring call (veda_trippool_score_raster_noalloc, static scratch) through
 the C ABI against the workspace call it mirrors (veda_trippool_score_raster), which the
-parity tests check against the oracle: scores, probabilities, descriptors and the top-k
-lists must be bit-identical.  Two calls in a row on one GPU, the second with a smaller
+parity tests check against the oracle: scores, probabilities, descriptors, key-tile bounds
+and the top-k lists must be bit-identical.  Two calls in a row on one GPU, the second with a smaller
 problem (so the shared scratch holds the first call's values when the second starts)."""
 import numpy as np
 import pytest
@@ -36,6 +36,7 @@ def run_case(name, topk, k_layout):
                     probs=torch.full((B, H, nt, nt), float("nan"), device="cuda"),
                     q_desc=torch.full((B, H, nt, 3 * d), float("nan"), device="cuda"),
                     k_desc=torch.full((B, H, nt, 3 * d), float("nan"), device="cuda"),
+                    k_bound=torch.full((B, H, nt), float("nan"), device="cuda"),
                     idx=torch.full((B, H, nt, topk), -1, dtype=torch.int32, device="cuda"))
 
     ref, got = outputs(), outputs()

@@ -89,21 +89,21 @@ def lib():
         sig = {
             "veda_tile_gather": (i32, [G, i32, vp, i64, i64, i64, vp, i32, i32, vp]),
             "veda_trippool_workspace_bytes": (sz, [G, i32, i32]),
-            "veda_trippool_score": (i32, [G, i32, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp,
-                                          vp, sz, vp]),
+            "veda_trippool_score": (i32, [G, i32, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, i32,
+                                          vp, vp, sz, vp]),
             "veda_topk_mask": (i32, [i64, i32, vp, i32, vp, vp, vp]),
-            "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, i32, vp, i32, f32, vp, vp, vp]),
+            "veda_sparse_attn_fwd": (i32, [G, i32, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp]),
             "veda_oracle_tilemap_workspace_bytes": (sz, [G, i32]),
             "veda_oracle_tilemap": (i32, [G, i32, vp, vp, f32, vp, i32, vp, vp, vp, sz, vp]),
             "veda_head_sq_error_workspace_bytes": (sz, [i32, i32, i32]),
             "veda_head_sq_error": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "veda_distill_workspace_bytes": (sz, [G, i32]),
             "veda_trippool_score_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
-                                                 vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+                                                 vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "veda_trippool_score_raster_noalloc": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32,
-                                                         i32, f32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
-            "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, i32, f32, vp,
-                                                  i64, i64, i64, vp, vp]),
+                                                         i32, f32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "veda_sparse_attn_fwd_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, vp, i32, vp, vp, i32, f32,
+                                                  vp, i64, i64, i64, vp, vp]),
             "veda_oracle_tilemap_raster": (i32, [G, i32, vp, vp, i32, i64, i64, i64, f32, vp, i32, vp, vp, vp, sz,
                                                  vp]),
             "veda_distill_step": (i32, [G, i32, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp, f32, vp, sz,
@@ -251,29 +251,36 @@ def _weights(geom, w1_q, w2_q, w1_k, w2_k):
     return ws, hidden, mout
 
 
-def _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx):
+def _score_outputs(geom, scores, probs, q_desc, k_desc, k_bound, topk, idx):
     torch = _torch()
     B, H, nt = geom.batch, geom.heads, geom.n_tiles
     rows = B * H * nt
     return (_p(scores, "scores", True, torch.float32, rows * nt), _p(probs, "probs", True, torch.float32, rows * nt),
             _p(q_desc, "q_desc", True, torch.float32, rows * 3 * geom.head_dim),
             _p(k_desc, "k_desc", True, torch.float32, rows * 3 * geom.head_dim),
-            _p(idx, "idx", True, torch.int32, rows * max(int(topk), 0)))
+            _k_bound(geom, k_bound, "k_bound"), _p(idx, "idx", True, torch.int32, rows * max(int(topk), 0)))
+
+
+def _k_bound(geom, t, name):
+    """Checked pointer of a per-key-tile bound array [B, H, n_t] float32, or None."""
+    return _p(t, name, True, _torch().float32, geom.batch * geom.heads * geom.n_tiles)
 
 
 def veda_trippool_score(geom, q_tiled, k_tiled, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
                         scores=None, probs=None, q_desc=None, k_desc=None, topk=0, idx=None, workspace=None,
-                        stream=None):
+                        stream=None, k_bound=None):
+    """k_bound: optional [B, H, n_t] float32 output, each key tile's bound on its key-row
+    norms (from its max and min descriptors), which the attention calls take."""
     w1_k = w1_q if w1_k is None else w1_k
     w2_k = w2_q if w2_k is None else w2_k
     dt = _elem_dtype(q_tiled)
     n = _tiled_numel(geom)
     qp, kp = _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n)
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
-    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, k_bound, topk, idx)
     _call("veda_trippool_score",
-        geom.ref, _dtype_code(q_tiled), qp, kp, a, b, c, e, hidden, mout, float(score_scale), *outs[:4], int(topk),
-        outs[4], _p(workspace, "workspace"), _ws(workspace), _stream(stream))
+        geom.ref, _dtype_code(q_tiled), qp, kp, a, b, c, e, hidden, mout, float(score_scale), *outs[:5], int(topk),
+        outs[5], _p(workspace, "workspace"), _ws(workspace), _stream(stream))
 
 
 def veda_topk_mask(scores, k, idx, mask=None, stream=None):
@@ -297,16 +304,18 @@ def _kv_idx(geom, kv_idx, k):
 
 
 def veda_sparse_attn_fwd(geom, q_tiled, k_tiled, v_tiled, kv_idx, k, softmax_scale, o_tiled, lse=None,
-                         v_layout=ROWS, stream=None):
+                         v_layout=ROWS, stream=None, k_bound=None):
     """v_tiled holds V in v_layout: COLS (channel-major tiles) or ROWS (tile-major, like Q
-    and K)."""
+    and K).  k_bound: the scoring call's [B, H, n_t] key-tile norm bounds of this K, or None
+    (running softmax maximum)."""
     if v_layout not in (COLS, ROWS):
         raise VedaError("v_layout must be COLS or ROWS (a raster V goes to veda_sparse_attn_fwd_raster)")
     dt = _elem_dtype(q_tiled)
     n = _tiled_numel(geom)
     _call("veda_sparse_attn_fwd",
         geom.ref, _dtype_code(q_tiled), _p(q_tiled, "q_tiled", True, dt, n), _p(k_tiled, "k_tiled", True, dt, n),
-        _p(v_tiled, "v_tiled", True, dt, n), int(v_layout), _kv_idx(geom, kv_idx, k), int(k), float(softmax_scale),
+        _p(v_tiled, "v_tiled", True, dt, n), int(v_layout), _kv_idx(geom, kv_idx, k), _k_bound(geom, k_bound, "k_bound"),
+        int(k), float(softmax_scale),
         _p(o_tiled, "o_tiled", True, dt, n),
         _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tiled), _stream(stream))
 
@@ -435,7 +444,8 @@ def _v_copy(geom, q, v, v_tiled_out):
 
 def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125, scores=None,
                                probs=None, q_desc=None, k_desc=None, topk=0, idx=None, workspace=None,
-                               k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None):
+                               k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None,
+                               k_bound=None):
     """veda_trippool_score on raster Q [B, N, H, d] (read through each head's tiling); K
     raster too, or tile-major with k_layout=ROWS.  With a raster K, k_tiled_out (if given)
     receives K's tile-major copy, written while K is pooled; with a raster V (strides of Q),
@@ -445,16 +455,16 @@ def veda_trippool_score_raster(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, sco
     rs, kp = _k_operand(geom, q, k, k_layout, *(() if v is None else (v,)))
     qp = _raster(geom, q, "q", _elem_dtype(q))
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
-    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, k_bound, topk, idx)
     vc = _v_copy(geom, q, v, v_tiled_out)
     _call("veda_trippool_score_raster",
           geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e, hidden, mout, float(score_scale),
-          *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), *vc, _p(workspace, "workspace"),
+          *outs[:5], int(topk), outs[5], _k_tiled_out(geom, q, k_tiled_out), *vc, _p(workspace, "workspace"),
           _ws(workspace), _stream(stream))
 
 
 def veda_sparse_attn_fwd_raster(geom, q, k, v, kv_idx, kk, softmax_scale, o, lse=None, k_layout=RASTER,
-                                v_layout=ROWS, stream=None):
+                                v_layout=ROWS, stream=None, k_bound=None):
     """veda_sparse_attn_fwd with raster Q and output O [B, N, H, d]; K raster or tile-major
     (k_layout=ROWS); V channel-major tiled (COLS), tile-major (ROWS) or raster (RASTER, with
     the strides of Q); O with strides of its own; lse [B, H, N] in raster token order."""
@@ -470,7 +480,7 @@ def veda_sparse_attn_fwd_raster(geom, q, k, v, kv_idx, kk, softmax_scale, o, lse
     op = _raster(geom, o, "o", dt)
     _call("veda_sparse_attn_fwd_raster",
         geom.ref, _dtype_code(q), _raster(geom, q, "q", dt), kp, int(k_layout), *rs,
-        vp, int(v_layout), _kv_idx(geom, kv_idx, kk), int(kk),
+        vp, int(v_layout), _kv_idx(geom, kv_idx, kk), _k_bound(geom, k_bound, "k_bound"), int(kk),
         float(softmax_scale), op, *_raster_strides(o),
         _p(lse, "lse", True, _torch().float32, geom.batch * geom.heads * geom.n_tokens), _stream(stream))
 
@@ -487,7 +497,8 @@ def veda_oracle_tilemap_raster(geom, q, k, softmax_scale, q_tiles, n_sel, tilema
 
 def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=None, score_scale=0.125,
                                        scores=None, probs=None, q_desc=None, k_desc=None, topk=0, idx=None,
-                                       k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None):
+                                       k_layout=RASTER, k_tiled_out=None, v=None, v_tiled_out=None, stream=None,
+                                       k_bound=None):
     """veda_trippool_score_raster with no workspace: the library's static scratch holds the
     MLP outputs (B * H * n_t <= 65536 tiles; calls that overlap on one GPU race)."""
     w1_k = w1_q if w1_k is None else w1_k
@@ -495,8 +506,8 @@ def veda_trippool_score_raster_noalloc(geom, q, k, w1_q, w2_q, w1_k=None, w2_k=N
     rs, kp = _k_operand(geom, q, k, k_layout, *(() if v is None else (v,)))
     qp = _raster(geom, q, "q", _elem_dtype(q))
     (a, b, c, e), hidden, mout = _weights(geom, w1_q, w2_q, w1_k, w2_k)
-    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, topk, idx)
+    outs = _score_outputs(geom, scores, probs, q_desc, k_desc, k_bound, topk, idx)
     vc = _v_copy(geom, q, v, v_tiled_out)
     _call("veda_trippool_score_raster_noalloc", geom.ref, _dtype_code(q), qp, kp, int(k_layout), *rs, a, b, c, e,
-          hidden, mout, float(score_scale), *outs[:4], int(topk), outs[4], _k_tiled_out(geom, q, k_tiled_out), *vc,
+          hidden, mout, float(score_scale), *outs[:5], int(topk), outs[5], _k_tiled_out(geom, q, k_tiled_out), *vc,
           _stream(stream))

@@ -110,13 +110,18 @@ veda_status check_raster(const Geo &geo, const HeadShapes &hs, veda_dtype dt, in
   return VEDA_OK;
 }
 
+// A softmax scale the kernels handle: positive and finite (they take row maxima of the
+// unscaled logits).
+bool scale_ok(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
+
 // Validation shared by the raster scoring calls: everything but the workspace.  Fills the
 // kernels' geometry, shapes and raster byte strides.
 veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster, const void *k_raster,
                                veda_layout k_layout, int64_t rs_b, int64_t rs_n, int64_t rs_h, const float *w1_q,
                                const float *w2_q, const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                int32_t mlp_out, const float *scores, const float *probs, const float *q_desc,
-                               const float *k_desc, int32_t topk, const int32_t *idx, const void *k_tiled_out,
+                               const float *k_desc, const float *k_bound, int32_t topk, const int32_t *idx,
+                               const void *k_tiled_out,
                                const void *v_raster, const void *v_tiled_out, Geo *geo, HeadShapes *hs,
                                RasterView *rv) {
   int nt_min;
@@ -129,8 +134,8 @@ veda_status check_score_raster(const veda_geom *g, veda_dtype dtype, const void 
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo->nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
   if ((v_raster == nullptr) != (v_tiled_out == nullptr)) return VEDA_ERR_NULL;  // V's copy: both or neither
-  const void *ptrs[] = {q_raster, k_raster, w1_q,   w2_q,        w1_k,     w2_k,       scores,
-                        probs,    q_desc,   k_desc, idx, k_tiled_out, v_raster, v_tiled_out};
+  const void *ptrs[] = {q_raster, k_raster, w1_q, w2_q, w1_k,        w2_k,     scores,     probs,
+                        q_desc,   k_desc,   k_bound, idx, k_tiled_out, v_raster, v_tiled_out};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
@@ -207,8 +212,8 @@ size_t veda_trippool_workspace_bytes(const veda_geom *g, int32_t mlp_hidden, int
 veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
                                 const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                 int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores, float *probs,
-                                float *q_desc, float *k_desc, int32_t topk, int32_t *idx, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                float *q_desc, float *k_desc, float *k_bound, int32_t topk, int32_t *idx,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
@@ -220,13 +225,14 @@ veda_status veda_trippool_score(const veda_geom *g, veda_dtype dtype, const void
   if (topk < 0 || topk > nt_min) return VEDA_ERR_SHAPE;
   if (mlp_hidden != 256 || mlp_out != 64) return VEDA_ERR_UNSUPPORTED;
   if (geo.nt > SCORE_MAX_NT) return VEDA_ERR_UNSUPPORTED;
-  const void *ptrs[] = {q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, idx, workspace};
+  const void *ptrs[] = {q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, scores, probs, q_desc, k_desc, k_bound, idx, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (workspace == nullptr || workspace_bytes < score_workspace_bytes(geo, mlp_hidden, mlp_out))
     return VEDA_ERR_WORKSPACE;
   return hip_status(launch_score(geo, dtype, q_tiled, k_tiled, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
-                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs));
+                                 score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs,
+                                 nullptr, false, nullptr, nullptr, nullptr, k_bound));
 }
 
 veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
@@ -234,14 +240,14 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
                                        int64_t rs_h,
                                        const float *w1_q, const float *w2_q, const float *w1_k, const float *w2_k,
                                        int32_t mlp_hidden, int32_t mlp_out, float score_scale, float *scores,
-                                       float *probs, float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                       void *k_tiled_out, const void *v_raster, void *v_tiled_out, void *workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
+                                       float *probs, float *q_desc, float *k_desc, float *k_bound, int32_t topk,
+                                       int32_t *idx, void *k_tiled_out, const void *v_raster, void *v_tiled_out,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
-                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, k_bound, topk, idx,
                                      k_tiled_out, v_raster, v_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (workspace != nullptr && !aligned16(workspace)) return VEDA_ERR_ALIGN;
@@ -249,7 +255,7 @@ veda_status veda_trippool_score_raster(const veda_geom *g, veda_dtype dtype, con
     return VEDA_ERR_WORKSPACE;
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, workspace, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out));
+                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out, k_bound));
 }
 
 veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dtype, const void *q_raster,
@@ -257,14 +263,14 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
                                                int64_t rs_n, int64_t rs_h, const float *w1_q, const float *w2_q,
                                                const float *w1_k, const float *w2_k, int32_t mlp_hidden,
                                                int32_t mlp_out, float score_scale, float *scores, float *probs,
-                                               float *q_desc, float *k_desc, int32_t topk, int32_t *idx,
-                                               void *k_tiled_out, const void *v_raster, void *v_tiled_out,
-                                               hipStream_t stream) {
+                                               float *q_desc, float *k_desc, float *k_bound, int32_t topk,
+                                               int32_t *idx, void *k_tiled_out, const void *v_raster,
+                                               void *v_tiled_out, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   RasterView rv;
   veda_status s = check_score_raster(g, dtype, q_raster, k_raster, k_layout, rs_b, rs_n, rs_h, w1_q, w2_q, w1_k,
-                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, topk, idx,
+                                     w2_k, mlp_hidden, mlp_out, scores, probs, q_desc, k_desc, k_bound, topk, idx,
                                      k_tiled_out, v_raster, v_tiled_out, &geo, &hs, &rv);
   if (s != VEDA_OK) return s;
   if (score_workspace_bytes(geo, mlp_hidden, mlp_out) > SCRATCH_BYTES) return VEDA_ERR_SCRATCH;
@@ -273,7 +279,7 @@ veda_status veda_trippool_score_raster_noalloc(const veda_geom *g, veda_dtype dt
   // The MLP outputs are written whole before they are read: nothing needs clearing.
   return hip_status(launch_score(geo, dtype, q_raster, k_raster, w1_q, w2_q, w1_k, w2_k, mlp_hidden, mlp_out,
                                  score_scale, scores, probs, q_desc, k_desc, topk, idx, ws, stream, &hs, &rv,
-                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out));
+                                 k_layout == VEDA_RASTER, k_tiled_out, v_raster, v_tiled_out, k_bound));
 }
 
 veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, int32_t k, int32_t *idx,
@@ -287,8 +293,9 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
 }
 
 veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const void *q_tiled, const void *k_tiled,
-                                 const void *v_tiled, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
-                                 float softmax_scale, void *o_tiled, float *lse, hipStream_t stream) {
+                                 const void *v_tiled, veda_layout v_layout, const int32_t *kv_idx,
+                                 const float *k_bound, int32_t k, float softmax_scale, void *o_tiled, float *lse,
+                                 hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
@@ -297,28 +304,28 @@ veda_status veda_sparse_attn_fwd(const veda_geom *g, veda_dtype dtype, const voi
   if (!q_tiled || !k_tiled || !v_tiled || !kv_idx || !o_tiled) return VEDA_ERR_NULL;
   if (v_layout == VEDA_RASTER) return VEDA_ERR_UNSUPPORTED;  // no raster strides in the tiled call
   if (v_layout != VEDA_TILE_ROWS && v_layout != VEDA_TILE_COLS) return VEDA_ERR_SHAPE;
-  if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
-  const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, o_tiled, lse};
+  if (k < 1 || k > nt_min || !scale_ok(softmax_scale)) return VEDA_ERR_SHAPE;
+  const void *ptrs[] = {q_tiled, k_tiled, v_tiled, kv_idx, k_bound, o_tiled, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
-  return hip_status(launch_sparse_attn(geo, hs, dtype, q_tiled, k_tiled, v_tiled, v_layout, kv_idx, k, softmax_scale,
-                                       o_tiled, lse, stream));
+  return hip_status(launch_sparse_attn(geo, hs, dtype, q_tiled, k_tiled, v_tiled, v_layout, kv_idx, k_bound, k,
+                                       softmax_scale, o_tiled, lse, stream));
 }
 
 veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, const void *q_raster,
                                         const void *k_raster, veda_layout k_layout, int64_t rs_b, int64_t rs_n,
                                         int64_t rs_h,
-                                        const void *v, veda_layout v_layout, const int32_t *kv_idx, int32_t k,
-                                        float softmax_scale, void *o_raster, int64_t os_b, int64_t os_n,
-                                        int64_t os_h, float *lse, hipStream_t stream) {
+                                        const void *v, veda_layout v_layout, const int32_t *kv_idx,
+                                        const float *k_bound, int32_t k, float softmax_scale, void *o_raster,
+                                        int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t stream) {
   Geo geo;
   HeadShapes hs;
   int nt_min;
   veda_status s = check_geom(g, dtype, &geo, &hs, &nt_min);
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !v || !kv_idx || !o_raster) return VEDA_ERR_NULL;
-  if (k < 1 || k > nt_min) return VEDA_ERR_SHAPE;
-  const void *ptrs[] = {q_raster, k_raster, v, kv_idx, o_raster, lse};
+  if (k < 1 || k > nt_min || !scale_ok(softmax_scale)) return VEDA_ERR_SHAPE;
+  const void *ptrs[] = {q_raster, k_raster, v, kv_idx, k_bound, o_raster, lse};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return VEDA_ERR_ALIGN;
   if (k_layout != VEDA_RASTER && k_layout != VEDA_TILE_ROWS) return VEDA_ERR_SHAPE;
@@ -328,8 +335,8 @@ veda_status veda_sparse_attn_fwd_raster(const veda_geom *g, veda_dtype dtype, co
   // padded tilings: K and V tiled (the copies read whole tiles)
   if (geo.padded && (k_layout != VEDA_TILE_ROWS || v_layout == VEDA_RASTER)) return VEDA_ERR_UNSUPPORTED;
   return hip_status(launch_sparse_attn_raster(geo, hs, dtype, q_raster, k_raster, k_layout == VEDA_RASTER, rs_b, rs_n,
-                                              rs_h, v, v_layout, kv_idx, k, softmax_scale, o_raster, os_b, os_n, os_h,
-                                              lse, stream));
+                                              rs_h, v, v_layout, kv_idx, k_bound, k, softmax_scale, o_raster, os_b,
+                                              os_n, os_h, lse, stream));
 }
 
 size_t veda_oracle_tilemap_workspace_bytes(const veda_geom *g, int32_t n_sel) {
@@ -351,6 +358,7 @@ veda_status veda_oracle_tilemap(const veda_geom *g, veda_dtype dtype, const void
   if (s != VEDA_OK) return s;
   if (!q_tiled || !k_tiled || !tilemap) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && (n_sel != geo.nt || geo.padded))) return VEDA_ERR_SHAPE;
+  if (!scale_ok(softmax_scale)) return VEDA_ERR_SHAPE;
   if (geo.nt > (dtype == VEDA_F32 ? TILEMAP_MAX_NT_F32 : TILEMAP_MAX_NT)) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_tiled, k_tiled, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)
@@ -382,6 +390,7 @@ veda_status veda_oracle_tilemap_raster(const veda_geom *g, veda_dtype dtype, con
   if (s != VEDA_OK) return s;
   if (!q_raster || !k_raster || !tilemap) return VEDA_ERR_NULL;
   if (n_sel < 1 || n_sel > geo.nt || (q_tiles == nullptr && (n_sel != geo.nt || geo.padded))) return VEDA_ERR_SHAPE;
+  if (!scale_ok(softmax_scale)) return VEDA_ERR_SHAPE;
   if (geo.nt > (dtype == VEDA_F32 ? TILEMAP_MAX_NT_F32 : TILEMAP_MAX_NT)) return VEDA_ERR_UNSUPPORTED;
   const void *ptrs[] = {q_raster, k_raster, q_tiles, tilemap, lse, workspace};
   for (const void *p : ptrs)

@@ -20,10 +20,17 @@
 //  - S^T = K Q^T (32 keys x 32 queries per MFMA block) puts one query per lane column, so
 //    the row max needs one exchange between lane halves; O^T = V^T P^T keeps each lane's
 //    accumulators on its own query, so the online-softmax rescale is lane-local;
-//  - softmax in fp32 in the log2 domain (scale * log2 e folded into one FMA); the running
-//    max only moves when a row max exceeds it by more than 2^8 (the rescale of O is then
-//    rare; p <= 256 stays exact in fp32 and bf16 range); P rounded to bf16 (nearest even)
-//    for P V; 1/l applied in fp32 at the end;
+//  - softmax in fp32 in the log2 domain (scale * log2 e folded into one FMA); P rounded to
+//    bf16 (nearest even) for P V; 1/l applied in fp32 at the end.  The exponent offset m
+//    in p = exp2(s c - m) starts at the first kept tile's row max.  Running offset: it
+//    only moves when a later tile's row max exceeds it by more than 2^8 (the rescale of O
+//    is then rare; p <= 256 stays exact in fp32 and bf16 range).  Fixed offset, when
+//    per-key-tile norm bounds are given: b = c |q| max over the kept tiles of the bound is
+//    at or above every logit of the row (Cauchy-Schwarz); if b - m <= 64 for every row of
+//    the wave, no later p can exceed 2^64 (far inside fp32 and bf16 range, and so are l
+//    and O), so m stays where it is and no later tile needs a row max.  That gives the
+//    running offset's result bit for bit unless a later row max exceeds m by more than
+//    2^8 (where the running offset rescales instead);
 //  - workgroups are mapped so that each XCD walks consecutive query tiles of one head,
 //    sharing that head's K/V tiles in its L2.
 //
@@ -37,6 +44,7 @@ namespace veda {
 static constexpr float LOG2E = 1.4426950408889634f;
 static constexpr float LN2 = 0.6931471805599453f;
 static constexpr float RESCALE_SLACK = 8.0f;  // log2 units
+static constexpr float BOUND_SLACK = 64.0f;   // log2 units: fixed offset while every later p <= 2^64
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,11 +72,13 @@ enum { VM_COLS = 0, VM_ROWS = 1, VM_RAST = 2 };
 // strides of Q).  PAD: padded tiling: per-head tile counts and partial key tiles (K and V
 // tiled); with RQ the padding query rows of a partial query tile are neither read (Q taken
 // as zero, as the gather stores it) nor written.
+// kbound: [B, H, nt] upper bounds of the key-row norms of each key tile, or null (running
+// offset throughout).
 template <bool RQ, bool RK, bool PAD, int VM>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ vt,
-                 const int32_t *__restrict__ kv_idx, int kk, float c2, __bf16 *__restrict__ o,
-                 float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv, RasterView ro) {
+                 const int32_t *__restrict__ kv_idx, const float *__restrict__ kbound, int kk, float c2,
+                 __bf16 *__restrict__ o, float *__restrict__ lse, Geo g, HeadShapes hs, RasterView rv, RasterView ro) {
   constexpr bool VROW = VM != VM_COLS;          // V read with transposed reads
   constexpr int SW = VROW ? SWZ_QUAD : SWZ_ROW;  // swizzle of both LDS tiles
   const int L = xcd_tile(blockIdx.x, gridDim.x);
@@ -98,8 +108,25 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
   __shared__ uint4 Ks[128 * 16];
   __shared__ uint4 Vs[128 * 16];
 
-  // Q fragments first, consumed by an empty asm so that they have arrived before the first
-  // copy is issued (otherwise the compiler sinks the loads and waits for them in the loop).
+  // The kept list is read 64 entries at a time into one register (lane l holds entry 64c + l)
+  // and each step takes its entry with a readlane: no scalar load waits inside the loop.
+  int lchunk = list[min(lane, kk - 1)];
+  // The bound on this row's logits for a fixed offset: |c| |q| max over the kept tiles of
+  // kbound (list entries clamped as in the loop).  The first 64 kept tiles' bounds load
+  // beside the Q fragments (one unconditional load, pinned with them by the empty asm below,
+  // so that the wait for Q covers it); longer lists read the rest first.
+  bool lazy = kbound == nullptr;  // uniform: running offset for the whole query tile
+  float km = 0.f;
+  if (!lazy)
+    for (int c0 = 64; c0 < kk; c0 += 64)
+      km = fmaxf(km, kbound[bh * g.nt + min(max(list[min(c0 + lane, kk - 1)], 0), last)]);
+  const uint32_t *km0_src = lazy ? reinterpret_cast<const uint32_t *>(list)  // any valid word when unused
+                                 : reinterpret_cast<const uint32_t *>(kbound + bh * g.nt + min(max(lchunk, 0), last));
+  const uint32_t km0 = *km0_src;
+
+  // Q fragments, consumed by an empty asm so that they have arrived before the first copy
+  // is issued (otherwise the compiler sinks the loads and waits for them in the loop, or
+  // after the copies, which it does not count).
   const int qrow = i * 128 + 32 * w + lr;
   // this lane's query row: tiled row qrow, or its raster token (a real token unless the row
   // is padding of a partial tile of a padded tiling)
@@ -117,7 +144,8 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
       for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)0.0f;
     }
   }
-  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]),
+               "v"(km0));
 
   // copy offsets of a tile-major tile and of a raster one (computed only if K or V is raster)
   uint32_t toff[8], roff[8];
@@ -150,12 +178,22 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
         vrd[p][db] = vs_lds + (uint32_t)((4 * hi + rq) * 256 + 16 * slot + 8 * (i16 & 1));
       }
   }
-  // The kept list is read 64 entries at a time into one register (lane l holds entry 64c + l)
-  // and each step takes its entry with a readlane: no scalar load waits inside the loop.
-  int lchunk = list[min(lane, kk - 1)];
   int jn = min(max(__builtin_amdgcn_readlane(lchunk, 0), 0), last);  // out-of-range entries are clamped
   tile_to_lds(k_tile(jn), ks_lds, w, koff);
   tile_to_lds(v_tile(jn), vs_lds, w, voff);
+  float m_bound = 0.f;
+  if (!lazy) {  // the lane pair of a query row holds 64 of its channels each
+    float qn = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn = fmaf((float)qf[s][e], (float)qf[s][e], qn);
+    qn = half_sum(qn);
+    km = fmaxf(km, __uint_as_float(km0));
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) km = fmaxf(km, __shfl_xor(km, x));
+    m_bound = fabsf(c2) * sqrtf(qn) * km;
+  }
   wait_vmem<8>();
   barrier();  // K(0) is complete
 
@@ -218,22 +256,28 @@ attn_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, con
       tile_to_lds(k_tile(jn), ks_lds, w, koff);
     }
 
-    // ---- online softmax (log2 domain)
-    float mx = -1e30f;
+    // ---- online softmax (log2 domain): the row max of the first tile (it sets the offset),
+    // and of every later tile with the running offset
+    if (tt == 0 || lazy) {  // uniform
+      float mx = -1e30f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-    mx = half_max(mx) * c2;
-    if (__ballot(mx > m_run + RESCALE_SLACK)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
+      mx = half_max(mx) * c2;
+      // tt == 0 with bounds: the offset stays fixed unless a row's bound lies more than 2^64
+      // above its first tile's max (or that max above the bound: the bounds are not this K's)
+      if (!lazy) lazy = __ballot(mx < m_bound - BOUND_SLACK || mx > m_bound + RESCALE_SLACK) != 0;
+      if (__ballot(mx > m_run + RESCALE_SLACK)) {  // always at tt == 0 (m_run starts at -1e30)
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      }
     }
     // P = exp2(s * c - m) rounded to bf16; l sums the rounded values, so that the weights
     // that multiply V are exactly the ones normalised (matters for near one-hot rows).
@@ -381,19 +425,18 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const float *__restrict__ 
 
 template <bool RQ, bool RK, int VM>
 static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const RasterView &ro, veda_dtype dt,
-                          const void *q,
-                          const void *k, const void *v, const int32_t *kv_idx, int kk, float scale, void *o,
-                          float *lse, hipStream_t st) {
+                          const void *q, const void *k, const void *v, const int32_t *kv_idx, const float *kbound,
+                          int kk, float scale, void *o, float *lse, hipStream_t st) {
   if (dt == VEDA_BF16) {
     constexpr bool PADDABLE = !RK && VM != VM_RAST;  // padded tilings read K and V tiled (the C ABI checks)
     if (PADDABLE && g.padded)
       attn_bf16_kernel<RQ, false, PADDABLE, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
-          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
-          rv, ro);
+          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kbound, kk, scale * LOG2E, (__bf16 *)o, lse,
+          g, hs, rv, ro);
     else
       attn_bf16_kernel<RQ, RK, false, VM><<<dim3(g.nt * g.H * g.B), 256, 0, st>>>(
-          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kk, scale * LOG2E, (__bf16 *)o, lse, g, hs,
-          rv, ro);
+          (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, kv_idx, kbound, kk, scale * LOG2E, (__bf16 *)o, lse,
+          g, hs, rv, ro);
   } else
     attn_f32_kernel<RQ, RK, VM><<<dim3(g.nt, g.H, g.B), 64, 0, st>>>((const float *)q, (const float *)k,
                                                                      (const float *)v, kv_idx, kk, scale, (float *)o,
@@ -402,15 +445,14 @@ static void launch_attn_t(const Geo &g, const HeadShapes &hs, const RasterView &
 
 template <bool RQ, bool RK>
 static void launch_attn_v(int vm, const Geo &g, const HeadShapes &hs, const RasterView &rv, const RasterView &ro,
-                          veda_dtype dt,
-                          const void *q, const void *k, const void *v, const int32_t *kv_idx, int kk, float scale,
-                          void *o, float *lse, hipStream_t st) {
+                          veda_dtype dt, const void *q, const void *k, const void *v, const int32_t *kv_idx,
+                          const float *kbound, int kk, float scale, void *o, float *lse, hipStream_t st) {
   if (vm == VM_COLS)
-    launch_attn_t<RQ, RK, VM_COLS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_COLS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kbound, kk, scale, o, lse, st);
   else if (vm == VM_ROWS)
-    launch_attn_t<RQ, RK, VM_ROWS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_ROWS>(g, hs, rv, ro, dt, q, k, v, kv_idx, kbound, kk, scale, o, lse, st);
   else if constexpr (RQ)  // a raster V comes only with raster Q (its strides)
-    launch_attn_t<RQ, RK, VM_RAST>(g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_t<RQ, RK, VM_RAST>(g, hs, rv, ro, dt, q, k, v, kv_idx, kbound, kk, scale, o, lse, st);
 }
 
 static int v_mode(veda_layout v_layout) {
@@ -418,23 +460,24 @@ static int v_mode(veda_layout v_layout) {
 }
 
 hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
-                              const void *v, veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                              float *lse, hipStream_t st) {
+                              const void *v, veda_layout v_layout, const int32_t *kv_idx, const float *kbound, int kk,
+                              float scale, void *o, float *lse, hipStream_t st) {
   launch_attn_v<false, false>(v_mode(v_layout), g, hs, RasterView{0, 0, 0}, RasterView{0, 0, 0}, dt, q, k, v, kv_idx,
-                              kk, scale, o, lse, st);
+                              kbound, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                                      bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
-                                     veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                                     int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t st) {
+                                     veda_layout v_layout, const int32_t *kv_idx, const float *kbound, int kk,
+                                     float scale, void *o, int64_t os_b, int64_t os_n, int64_t os_h, float *lse,
+                                     hipStream_t st) {
   const int64_t eb = dt == VEDA_BF16 ? 2 : 4;
   const RasterView rv{rs_b * eb, rs_n * eb, rs_h * eb}, ro{os_b * eb, os_n * eb, os_h * eb};
   if (k_raster)
-    launch_attn_v<true, true>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, true>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kbound, kk, scale, o, lse, st);
   else
-    launch_attn_v<true, false>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kk, scale, o, lse, st);
+    launch_attn_v<true, false>(v_mode(v_layout), g, hs, rv, ro, dt, q, k, v, kv_idx, kbound, kk, scale, o, lse, st);
   return hipGetLastError();
 }
 

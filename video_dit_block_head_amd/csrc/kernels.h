@@ -12,14 +12,15 @@ hipError_t launch_gather(const Geo &g, const HeadShapes &hs, veda_dtype dt, void
 // (and hs) set, Q is a raster tensor read through each head's tiling, and K too if k_raster;
 // k_tiled_out (raster K only) receives K's tile-major copy, written as K is pooled;
 // v_tiled_out (raster Q only) receives the tile-major copy of the raster V v_raster (strides
-// of Q), streamed in the same launch.
+// of Q), streamed in the same launch; k_bound [B][H][n_t] receives each key tile's row-norm
+// bound (from its max and min descriptors).
 size_t score_workspace_bytes(const Geo &g, int hidden, int mlp_out);
 hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st, const HeadShapes *hs = nullptr, const RasterView *rv = nullptr,
                         bool k_raster = false, void *k_tiled_out = nullptr, const void *v_raster = nullptr,
-                        void *v_tiled_out = nullptr);
+                        void *v_tiled_out = nullptr, float *k_bound = nullptr);
 
 // TripPool + MLP only: y [Q|K][B][H][n_t][64]; descriptors [B][H][n_t][3d] if non-NULL;
 // the pre-activation hidden layer z [Q|K][B][H][n_t][256] if non-NULL.  With qlist
@@ -30,23 +31,25 @@ hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const voi
                            float *k_desc, hipStream_t st, const HeadShapes *hs = nullptr,
                            const RasterView *rv = nullptr, bool k_raster = false, float *z = nullptr,
                            const int32_t *qlist = nullptr, int nlist = 0, void *k_tiled_out = nullptr,
-                           const void *v_raster = nullptr, void *v_tiled_out = nullptr);
+                           const void *v_raster = nullptr, void *v_tiled_out = nullptr, float *k_bound = nullptr);
 
 hipError_t launch_topk(int64_t rows, int n_cols, const float *scores, int k, int32_t *idx, uint8_t *mask,
                        hipStream_t st);
 
-// V in v_layout: VEDA_TILE_COLS or VEDA_TILE_ROWS.
+// V in v_layout: VEDA_TILE_COLS or VEDA_TILE_ROWS.  kbound: [B][H][n_t] key-tile row-norm
+// bounds (the fixed exponent offset), or null (running offset).
 hipError_t launch_sparse_attn(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
-                              const void *v, veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                              float *lse, hipStream_t st);
+                              const void *v, veda_layout v_layout, const int32_t *kv_idx, const float *kbound, int kk,
+                              float scale, void *o, float *lse, hipStream_t st);
 
 // Q (element strides rs_*) and O (element strides os_*) in raster layout [B, N, H, d], K
 // raster (Q's strides) or tile-major, V channel-major tiled, tile-major, or raster with Q's
 // strides.
 hipError_t launch_sparse_attn_raster(const Geo &g, const HeadShapes &hs, veda_dtype dt, const void *q, const void *k,
                                      bool k_raster, int64_t rs_b, int64_t rs_n, int64_t rs_h, const void *v,
-                                     veda_layout v_layout, const int32_t *kv_idx, int kk, float scale, void *o,
-                                     int64_t os_b, int64_t os_n, int64_t os_h, float *lse, hipStream_t st);
+                                     veda_layout v_layout, const int32_t *kv_idx, const float *kbound, int kk,
+                                     float scale, void *o, int64_t os_b, int64_t os_n, int64_t os_h, float *lse,
+                                     hipStream_t st);
 
 size_t tilemap_workspace_bytes(const Geo &g, int n_sel);
 hipError_t launch_tilemap(const Geo &g, veda_dtype dt, const void *q, const void *k, float scale,

@@ -58,13 +58,17 @@ static constexpr int PM_HST = 260;    // hidden block row stride (floats)
 // vout (RQ only, else null): the items are (b, h, Q|K|V, group), and a V item copies its 32
 // tiles of the raster V vsrc (strides of Q) to their tile-major place in vout, as the K
 // items write kout (zero rows where the tiling has no token), and does nothing else.
+// kbound (nullable): [B, H, nt], for each key tile sqrt(sum over channels of
+// max(max^2, min^2)) from its max and min descriptors, an upper bound of the norm of each
+// of its key rows (0 for tiles past a padded head's own count).
 template <int EB, bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
 pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const float *__restrict__ w1q,
                 const float *__restrict__ w2q, const float *__restrict__ w1k, const float *__restrict__ w2k,
                 float *__restrict__ y, float *__restrict__ qdesc, float *__restrict__ kdesc, float *__restrict__ zout,
                 const int32_t *__restrict__ qlist, int nlist, Geo g, HeadShapes hs, RasterView rv,
-                uint8_t *__restrict__ kout, const uint8_t *__restrict__ vsrc, uint8_t *__restrict__ vout) {
+                uint8_t *__restrict__ kout, const uint8_t *__restrict__ vsrc, uint8_t *__restrict__ vout,
+                float *__restrict__ kbound) {
   constexpr int EPC = 16 / EB;            // channels per 16-byte chunk
   constexpr int P = EB == 2 ? 128 : 64;   // tokens per tile
   constexpr int D = EB == 2 ? 128 : 64;   // head dim
@@ -211,6 +215,19 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
       const int row = e / D3, col = e % D3;
       if (r0 + row < g.nt) dout[(((int64_t)b * g.H + h) * g.nt + r0 + row) * D3 + col] = Ds[row * PM_DS + col];
     }
+  }
+  if (which == 1 && kbound != nullptr) {  // uniform: each key tile's row-norm bound, 8 lanes per row
+    const int row = t >> 3, part = t & 7, j = r0 + row;
+    float nb = 0.f;
+#pragma unroll
+    for (int c = part * (D / 8); c < (part + 1) * (D / 8); ++c) {
+      const float a = fmaxf(fabsf(Ds[row * PM_DS + D + c]), fabsf(Ds[row * PM_DS + 2 * D + c]));
+      nb = fmaf(a, a, nb);
+    }
+    nb += __shfl_xor(nb, 4);
+    nb += __shfl_xor(nb, 2);
+    nb += __shfl_xor(nb, 1);
+    if (part == 0 && j < g.nt) kbound[((int64_t)b * g.H + h) * g.nt + j] = j < nth ? sqrtf(nb) : 0.f;
   }
 
   // ---- layer 1: hidden units 64 w .. 64 w + 63; column m of the two accumulator blocks is
@@ -449,25 +466,25 @@ template <int EB, bool RQ, bool RK>
 static void launch_pool_mlp_t(const Geo &g, const HeadShapes &hs, const RasterView &rv, const void *q, const void *k,
                               const float *w1q, const float *w2q, const float *w1k, const float *w2k, float *y,
                               float *q_desc, float *k_desc, float *z, const int32_t *qlist, int nlist,
-                              uint8_t *kout, const uint8_t *vsrc, uint8_t *vout, hipStream_t st) {
+                              uint8_t *kout, const uint8_t *vsrc, uint8_t *vout, float *kbound, hipStream_t st) {
   if (!RQ) vout = nullptr;  // a V copy comes only with raster Q (its strides)
   const int nwh = vout != nullptr ? 3 : 2;
   const dim3 pg(((g.nt + PM_ROWS - 1) / PM_ROWS) * g.H * nwh * g.B);
   if (g.padded)
     pool_mlp_kernel<EB, RQ, RK, true><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
                                                           y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout, vsrc,
-                                                          vout);
+                                                          vout, kbound);
   else
     pool_mlp_kernel<EB, RQ, RK, false><<<pg, 256, 0, st>>>((const uint8_t *)q, (const uint8_t *)k, w1q, w2q, w1k, w2k,
                                                            y, q_desc, k_desc, z, qlist, nlist, g, hs, rv, kout, vsrc,
-                                                           vout);
+                                                           vout, kbound);
 }
 
 hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const void *k, const float *w1q,
                            const float *w2q, const float *w1k, const float *w2k, float *y, float *q_desc,
                            float *k_desc, hipStream_t st, const HeadShapes *hs, const RasterView *rv,
                            bool k_raster, float *z, const int32_t *qlist, int nlist, void *k_tiled_out,
-                           const void *v_raster, void *v_tiled_out) {
+                           const void *v_raster, void *v_tiled_out, float *k_bound) {
   uint8_t *kout = static_cast<uint8_t *>(k_tiled_out);
   const uint8_t *vsrc = static_cast<const uint8_t *>(v_raster);
   uint8_t *vout = static_cast<uint8_t *>(v_tiled_out);
@@ -476,19 +493,19 @@ hipError_t launch_pool_mlp(const Geo &g, veda_dtype dt, const void *q, const voi
   const bool bf = dt == VEDA_BF16;
   if (rv == nullptr) {
     if (bf)
-      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<2, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
     else
-      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<4, false, false>(g, hs0, rv0, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
   } else if (k_raster) {
     if (bf)
-      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<2, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
     else
-      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<4, true, true>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
   } else {
     if (bf)
-      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<2, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
     else
-      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, st);
+      launch_pool_mlp_t<4, true, false>(g, *hs, *rv, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, z, qlist, nlist, kout, vsrc, vout, k_bound, st);
   }
   return hipGetLastError();
 }
@@ -497,13 +514,13 @@ hipError_t launch_score(const Geo &g, veda_dtype dt, const void *q, const void *
                         const float *w2q, const float *w1k, const float *w2k, int hidden, int mlp_out, float scale,
                         float *scores, float *probs, float *q_desc, float *k_desc, int topk, int32_t *idx,
                         void *ws, hipStream_t st, const HeadShapes *hs, const RasterView *rv, bool k_raster,
-                        void *k_tiled_out, const void *v_raster, void *v_tiled_out) {
+                        void *k_tiled_out, const void *v_raster, void *v_tiled_out, float *k_bound) {
   (void)hidden;
   (void)mlp_out;
   float *y = (float *)ws;
   const HeadShapes hsv = hs != nullptr ? *hs : HeadShapes{};
   const hipError_t pe = launch_pool_mlp(g, dt, q, k, w1q, w2q, w1k, w2k, y, q_desc, k_desc, st, hs, rv, k_raster,
-                                        nullptr, nullptr, 0, k_tiled_out, v_raster, v_tiled_out);
+                                        nullptr, nullptr, 0, k_tiled_out, v_raster, v_tiled_out, k_bound);
   if (pe != hipSuccess) return pe;
   if (g.nt <= 64)
     launch_score_t<1>(g, y, scale, scores, probs, topk, idx, hsv, st);

@@ -33,6 +33,10 @@ class SparseAttention:
         self.k_t = torch.empty(shape, dtype=dtype, device=device)
         self.v_t = torch.empty(shape, dtype=dtype, device=device)   # tile-major (ROWS), like q_t and k_t
         self.o_t = torch.empty(shape, dtype=dtype, device=device)
+        # each key tile's row-norm bound, written by the scoring calls and passed to attention
+        # while it describes the K that attention reads (_kb_src: k_t, a raster K, or None)
+        self.k_bound = torch.empty((g.batch, g.heads, g.n_tiles), dtype=torch.float32, device=device)
+        self._kb_src = None
         nbytes = veda_trippool_workspace_bytes(g, self.w1.shape[-1], self.w2.shape[-1])
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self._idx = {}
@@ -49,17 +53,23 @@ class SparseAttention:
         veda_tile_gather(self.geom, q, self.q_t, ROWS)
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
+        self._kb_src = None
+
+    def _bound_for(self, k):
+        """The key-tile bounds if they were computed from k (the tensor attention reads)."""
+        return self.k_bound if self._kb_src is not None and self._kb_src is k else None
 
     def score(self, topk, scores=None, probs=None, q_desc=None, k_desc=None):
         idx = self.idx_buffer(topk) if topk > 0 else None
         veda_trippool_score(self.geom, self.q_t, self.k_t, self.w1, self.w2, self.w1_k, self.w2_k,
                             self.score_scale, scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc,
-                            topk=topk, idx=idx, workspace=self.ws)
+                            topk=topk, idx=idx, workspace=self.ws, k_bound=self.k_bound)
+        self._kb_src = self.k_t
         return idx
 
     def attend(self, idx, lse=None):
         veda_sparse_attn_fwd(self.geom, self.q_t, self.k_t, self.v_t, idx, int(idx.shape[-1]),
-                             self.softmax_scale, self.o_t, lse, v_layout=ROWS)
+                             self.softmax_scale, self.o_t, lse, v_layout=ROWS, k_bound=self._bound_for(self.k_t))
         return self.o_t
 
     def scatter(self, out):
@@ -99,6 +109,7 @@ class SparseAttention:
     def gather_kv(self, k, v):
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
+        self._kb_src = None
 
     def gather_v(self, v):
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
@@ -116,13 +127,15 @@ class SparseAttention:
         veda_trippool_score_raster(self.geom, q, kt, self.w1, self.w2, self.w1_k, self.w2_k, self.score_scale,
                                    scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc, topk=topk, idx=idx,
                                    workspace=self.ws, k_layout=lay, k_tiled_out=self.k_t if tile_k else None,
-                                   v=v, v_tiled_out=None if v is None else self.v_t)
+                                   v=v, v_tiled_out=None if v is None else self.v_t, k_bound=self.k_bound)
+        # the bounds describe the raster K, and its tiled copy when this call wrote it
+        self._kb_src = self.k_t if (k is None or tile_k) else k
         return idx
 
     def attend_raster(self, q, idx, out, lse=None, k=None):
         kt, lay = self._k(k)
         veda_sparse_attn_fwd_raster(self.geom, q, kt, self.v_t, idx, int(idx.shape[-1]), self.softmax_scale, out,
-                                    lse, k_layout=lay, v_layout=ROWS)
+                                    lse, k_layout=lay, v_layout=ROWS, k_bound=self._bound_for(kt))
         return out
 
     def tilemap_raster(self, q, q_tiles, n_sel, out, lse=None, k=None):
