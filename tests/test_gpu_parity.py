@@ -615,3 +615,60 @@ def test_key_tile_bounds_and_offset_paths(r):
             f"{same_rows:.4f}")
     amax, arel = tol(r)
     assert mx <= amax and rel <= arel and lse_err <= 4e-3
+
+
+@pytest.mark.parametrize("case", ["fixed", "fallback"])
+def test_offset_with_growing_logits(case):
+    """Queries near one direction u and keys of time slice t along u with weight a_t growing
+    along the kept list, so that later tiles' row maxima exceed the first tile's by more than
+    2^8 (the running offset rescales) while the key-tile bounds stay close to the true key
+    norms.  "fixed": the largest bound lies within 2^64 of every row's first-tile max, the
+    fixed offset is kept and exponentials reach about 2^18 (the outputs differ from the
+    running offset's in rounding); "fallback": the last slice's weight puts the bound beyond
+    2^64 and every wave takes the running offset, bit for bit.  Both against the oracle, on
+    a 4x8x16 grid with two tile shapes (the second puts two time slices in each tile)."""
+    shapes = [(1, 8, 16), (2, 8, 8)]
+    grid = (4, 8, 16)
+    a = {"fixed": (2.0, 8.0, 14.0, 20.0), "fallback": (2.0, 8.0, 14.0, 200.0)}[case]
+    rng = np.random.default_rng(11)
+    H, N, d, P = 2, 512, 128, 128
+    geom = V.Geom(1, H, d, grid, P, shapes)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    t_of = np.repeat(np.arange(grid[0]), grid[1] * grid[2])            # raster token -> t
+    qn = 8.0 * u + 0.3 * rng.standard_normal((1, N, H, d))
+    kn = np.asarray(a)[t_of][None, :, None, None] * u + 0.3 * rng.standard_normal((1, N, H, d))
+    vn = rng.standard_normal((1, N, H, d))
+    up = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+    q, k, v = up(qn), up(kn), up(vn)
+    w1 = torch.from_numpy((rng.standard_normal((H, 3 * d, 256)) / math.sqrt(3 * d)).astype(np.float32))
+    w2 = torch.from_numpy((rng.standard_normal((H, 256, 64)) / 16).astype(np.float32))
+    sa = SparseAttention(geom, torch.bfloat16, w1, w2)
+    say(f"[gpu-parity] growing logits, {case}")
+    sa.gather(q, k, v)
+    sa.score(2)                                   # writes the key-tile bounds of this K
+    nt = geom.n_tiles
+    idx = dense_index(geom)                       # every tile, ascending: logits grow along the list
+    o_fix, o_run = torch.empty_like(sa.o_t), torch.empty_like(sa.o_t)
+    l_fix = torch.empty((1, H, N), dtype=torch.float32, device="cuda")
+    l_run = torch.empty_like(l_fix)
+    V.veda_sparse_attn_fwd(geom, sa.q_t, sa.k_t, sa.v_t, idx, nt, sa.softmax_scale, o_fix, l_fix, k_bound=sa.k_bound)
+    V.veda_sparse_attn_fwd(geom, sa.q_t, sa.k_t, sa.v_t, idx, nt, sa.softmax_scale, o_run, l_run)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_fix.float()).all() and torch.isfinite(l_fix).all()
+    same = same_bits(o_fix, o_run) and same_bits(l_fix, l_run)
+    assert same == (case == "fallback"), case
+    worst = lse_worst = 0.0
+    for h in range(H):
+        perm = O.tile_permutation(grid, shapes[h])
+        qt, kt, vt = (O.to_tiles(host(x[0, :, h]), perm) for x in (q, k, v))
+        ref, ref_lse = O.sparse_attention(qt, kt, vt, host(idx[0, h]).astype(np.int64), P, 1 / math.sqrt(d),
+                                          return_lse=True)
+        for o, l in ((o_fix, l_fix), (o_run, l_run)):
+            got = host(o[0, h])
+            worst = max(worst, float(np.abs(got - ref).max()))
+            assert math.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) <= 1e-2, (case, h)
+            lse_worst = max(lse_worst, float(np.abs(host(l[0, h]) - ref_lse).max()))
+    measure(f"[gpu-parity] growing logits ({case}): max|dO| {worst:.3g}, max|dLSE| {lse_worst:.3g}, "
+            f"fixed offset bit-identical to running: {same}")
+    assert worst <= 2e-2 and lse_worst <= 4e-3
