@@ -34,9 +34,10 @@ class SparseAttention:
         self.v_t = torch.empty(shape, dtype=dtype, device=device)   # tile-major (ROWS), like q_t and k_t
         self.o_t = torch.empty(shape, dtype=dtype, device=device)
         # each key tile's row-norm bound, written by the scoring calls and passed to attention
-        # while it describes the K that attention reads (_kb_src: k_t, a raster K, or None)
+        # while it describes the K that attention reads (_kb_src: the tensors it was computed
+        # from, k_t and/or a raster K)
         self.k_bound = torch.empty((g.batch, g.heads, g.n_tiles), dtype=torch.float32, device=device)
-        self._kb_src = None
+        self._kb_src = ()
         nbytes = veda_trippool_workspace_bytes(g, self.w1.shape[-1], self.w2.shape[-1])
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self._idx = {}
@@ -53,18 +54,18 @@ class SparseAttention:
         veda_tile_gather(self.geom, q, self.q_t, ROWS)
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
-        self._kb_src = None
+        self._kb_src = ()
 
     def _bound_for(self, k):
         """The key-tile bounds if they were computed from k (the tensor attention reads)."""
-        return self.k_bound if self._kb_src is not None and self._kb_src is k else None
+        return self.k_bound if any(x is k for x in self._kb_src) else None
 
     def score(self, topk, scores=None, probs=None, q_desc=None, k_desc=None):
         idx = self.idx_buffer(topk) if topk > 0 else None
         veda_trippool_score(self.geom, self.q_t, self.k_t, self.w1, self.w2, self.w1_k, self.w2_k,
                             self.score_scale, scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc,
                             topk=topk, idx=idx, workspace=self.ws, k_bound=self.k_bound)
-        self._kb_src = self.k_t
+        self._kb_src = (self.k_t,)
         return idx
 
     def attend(self, idx, lse=None):
@@ -109,7 +110,7 @@ class SparseAttention:
     def gather_kv(self, k, v):
         veda_tile_gather(self.geom, k, self.k_t, ROWS)
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
-        self._kb_src = None
+        self._kb_src = ()
 
     def gather_v(self, v):
         veda_tile_gather(self.geom, v, self.v_t, ROWS)
@@ -128,8 +129,8 @@ class SparseAttention:
                                    scores=scores, probs=probs, q_desc=q_desc, k_desc=k_desc, topk=topk, idx=idx,
                                    workspace=self.ws, k_layout=lay, k_tiled_out=self.k_t if tile_k else None,
                                    v=v, v_tiled_out=None if v is None else self.v_t, k_bound=self.k_bound)
-        # the bounds describe the raster K, and its tiled copy when this call wrote it
-        self._kb_src = self.k_t if (k is None or tile_k) else k
+        # the bounds describe the K read, and its tiled copy when this call wrote it
+        self._kb_src = (self.k_t,) if k is None else ((k, self.k_t) if tile_k else (k,))
         return idx
 
     def attend_raster(self, q, idx, out, lse=None, k=None):
