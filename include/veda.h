@@ -175,13 +175,13 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  *           not meaningful).
  *   k_bound: [B, H, n_t] f32 upper bounds of the key-row norms of each key tile of this
  *           K (the k_bound output of the scoring call that read it), nullable.  The bf16
- *           kernel offsets each row's exponentials by its first kept tile's row maximum m;
- *           without k_bound it takes every later tile's row maximum too and moves m when
- *           one exceeds it by more than 8 (log2 units).  With k_bound, the 32 rows of a
- *           wave keep m fixed and take no further row maximum when every row's
- *           b = softmax_scale * |q| * max over its kept tiles of k_bound (at or above each
- *           of its logits) lies at most 64 (log2) above its m, so that no exponential
- *           exceeds 2^64; the result is then the same bit for bit unless a later tile's
+ *           kernel offsets each row's exponentials by its first kept tile's row maximum m
+ *           (log2 units: logits times softmax_scale * log2 e); without k_bound it takes
+ *           every later tile's row maximum too and moves m when one exceeds it by more
+ *           than 8.  With k_bound, the 32 rows of a wave keep m fixed and take no further
+ *           row maximum when every row's b = log2 e * softmax_scale * |q| * max over its
+ *           kept tiles of k_bound (at or above each of its scaled logits) lies at most 64
+ *           above its m, so that no exponential exceeds 2^64; the result is then the same bit for bit unless a later tile's
  *           row maximum exceeds m by more than 8, and the same softmax up to rounding
  *           otherwise.  Rows whose first tile's maximum lies above b by more than 8 (a
  *           k_bound of another K) take the running maximum.  A k_bound below the true
