@@ -140,20 +140,30 @@ pool_mlp_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, co
                         ? cdst + ((int64_t)b * g.H + h) * (int64_t)g.N * 256 + (int64_t)j * P * 256 + c * 16
                         : nullptr;
     if (j < nth && PAD && box_rows(bx) < P) {
-      // a partial tile of a padded tiling: its real rows, one at a time (raster rows at
-      // origin + intra, which names a real token only inside the tile's box)
+      // a partial tile of a padded tiling: its real rows only (raster rows at origin +
+      // intra, which names a real token only inside the tile's box), eight loads in flight
+      // per lane; each lane still takes its rows in increasing order
       const uint8_t *src = rast ? src0 + tile_origin(j, pt, ph, pw, g.Hs, g.Ws) * rv.sn + c * 16
                                 : src0 + (int64_t)j * P * 256 + c * 16;
       const int64_t rstride = rast ? rv.sn : 256;
 #pragma unroll 1
-      for (int o = rg; o < P; o += 4) {
-        if (in_box(o, ph, pw, bx)) {
-          const int64_t ro = rast ? (int64_t)tile_intra(o, ph, pw, g.Hs, g.Ws) * rstride : (int64_t)o * 256;
-          const uint4 v = load_stream16(src + ro);
-          if (!vcopy) accum(v);
-          if (kdst != nullptr) store_stream16(kdst + o * 256, v);
-        } else if (kdst != nullptr) {
-          store_stream16(kdst + o * 256, make_uint4(0u, 0u, 0u, 0u));
+      for (int o0 = rg; o0 < P; o0 += 32) {
+        uint4 v[8];
+        bool real[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int o = o0 + 4 * i;
+          real[i] = in_box(o, ph, pw, bx);
+          v[i] = make_uint4(0u, 0u, 0u, 0u);
+          if (real[i]) {
+            const int64_t ro = rast ? (int64_t)tile_intra(o, ph, pw, g.Hs, g.Ws) * rstride : (int64_t)o * 256;
+            v[i] = load_stream16(src + ro);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (real[i] && !vcopy) accum(v[i]);
+          if (kdst != nullptr) store_stream16(kdst + (o0 + 4 * i) * 256, v[i]);  // zero rows for padding
         }
       }
     } else if (PAD && j >= nth && j < g.nt) {
