@@ -186,7 +186,11 @@ veda_status veda_topk_mask(int64_t rows, int32_t n_cols, const float *scores, in
  *           otherwise.  Rows whose first tile's maximum lies above b by more than 8 (a
  *           k_bound of another K) take the running maximum.  A k_bound below the true
  *           norms can still overflow the exponentials of later tiles: the output is then
- *           not meaningful, with no out-of-bounds access.  The fp32 kernel ignores it.
+ *           not meaningful, with no out-of-bounds access.  With the offset fixed, the
+ *           fp32 sums of P V reach up to 2^64 * k * P * max |v| (k * P kept keys), which
+ *           stays finite while max |v| < 3.4e38 / (2^64 * k * P), about 2.4e15 at
+ *           k * P = 7680 and 1.2e14 at 153600; V with larger values needs k_bound = NULL
+ *           (then p <= 2^8).  The fp32 kernel ignores it.
  *   softmax_scale: > 0 and finite (else VEDA_ERR_SHAPE)
  *   o_tiled: out VEDA_TILE_ROWS, same dtype
  *   lse:     out [B, H, N] f32 natural-log log-sum-exp of each query row, nullable */
