@@ -63,3 +63,36 @@ def test_attention_homogeneous_in_v(name):
         assert torch.equal(out_s.view(torch.int16), want.view(torch.int16)), (name, e)
         assert torch.equal(lse_s, lse), (name, e)
         say(f"[gpu-vscale] {name}: e={e} output scaled bit for bit, LSE unchanged")
+
+
+@pytest.mark.parametrize("name", ["small", "large"])
+def test_attention_weights_sum_to_one(name):
+    """Every key of a head carrying the same V row c: each output row is a convex combination
+    of copies of c, so it must be c, and in bf16 exactly (the normaliser and the P V sums of
+    the same rounded weights differ by a few fp32 ulps, far below half a bf16 ulp of c).  A
+    normaliser that missed or double-counted terms, or weights not rounded alike on both
+    sides, moves it.  Both softmax offsets; every row of every head at full size."""
+    cfg = get(name)
+    say(f"[gpu-vscale] {name}: generating")
+    wl = make(cfg)
+    geom = V.Geom(cfg.batch, cfg.heads, cfg.head_dim, cfg.grid, cfg.tile, wl.shapes)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    sa = SparseAttention(geom, torch.bfloat16, torch.from_numpy(wl.w1), torch.from_numpy(wl.w2),
+                         score_scale=cfg.score_scale)
+    kk = cfg.topk[0]
+    idx = sa.score_raster(q, kk, k=k, tile_k=True, v=v)
+    B, N, H, d = cfg.batch, cfg.n_tokens, cfg.heads, cfg.head_dim
+    # c[h]: head h's first V row (bf16 values), the same for every key of the head
+    c = v[:, 0, :, :].clone()                                   # [B, H, d]
+    vt = c[:, :, None, :].expand(B, H, geom.n_tiled, d).contiguous()
+    want = c[:, None, :, :].expand(B, N, H, d)
+    for bound in (True, False):
+        out = torch.empty_like(q)
+        V.veda_sparse_attn_fwd_raster(geom, q, sa.k_t, vt, idx, kk, sa.softmax_scale, out, k_layout=V.ROWS,
+                                      v_layout=V.ROWS, k_bound=sa.k_bound if bound else None)
+        torch.cuda.synchronize()
+        same = out.view(torch.int16) == want.reshape(B, N, H, d).contiguous().view(torch.int16)
+        say(f"[gpu-vscale] {name}: constant V per head, bounds {'given' if bound else 'absent'}: "
+            f"{int(same.sum())} of {same.numel()} output values equal to c")
+        assert bool(same.all()), (name, bound)
