@@ -42,6 +42,13 @@ static constexpr int TM_QT = 2;
 // head's tiling (token of row r of tile j = origin(j) + intra(r)); otherwise tile-major.
 // PAD: padded tiling: per-head tile counts, partial tiles (K tiled); with RQ the padding
 // query rows of a partial tile are not read (Q taken as zero, as the gather stores it).
+// Maximum of v over lanes l and l ^ 32, the two halves of a query row's lane pair, with
+// v_permlane32_swap (a VALU op; a shuffle would go through the LDS and its latency).
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <bool RQ, bool RK, bool PAD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, float c2,
@@ -166,7 +173,7 @@ tilemap_bf16_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, 
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[qb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      mx = pair_max(mx) * c2;
       if (hi == 0 && owner) rm[(int64_t)j * 128 + 64 * (w & 1) + 32 * qb + lr] = mx;
       if (__ballot(mx > m_run[qb] + TM_SLACK)) {
         const float m_new = fmaxf(m_run[qb], mx);
