@@ -257,8 +257,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}); the path is "
-              "per-head independent and a multi-GPU run is not part of this build", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}): the path is "
+              "independent per head, so more GPUs would each run this same work on their share of the heads",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
