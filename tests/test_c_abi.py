@@ -53,3 +53,18 @@ def test_validation(c_out):
     assert int(c_out["topk_k0"]) == -2        # VEDA_ERR_SHAPE
     assert int(c_out["topk_empty"]) == 0      # zero rows: nothing to do
     assert int(c_out["tiled_tokens_bad"]) == -2
+
+
+def test_readme_c_example_compiles(tmp_path):
+    """The C example of README.md (the default step through include/veda.h) compiles against
+    the header as it stands, warnings as errors."""
+    if shutil.which("gcc") is None or not os.path.isdir(ROCM_INC):
+        pytest.skip("gcc or the ROCm headers are not available")
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = text.split("```c\n")[1:]
+    assert blocks, "README.md has no C example"
+    src = tmp_path / "readme_step.c"
+    src.write_text(blocks[0].split("```")[0])
+    subprocess.run(["gcc", "-c", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", ROCM_INC, str(src), "-o", str(tmp_path / "s.o")],
+                   check=True, capture_output=True, text=True)
